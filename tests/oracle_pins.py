@@ -1,0 +1,448 @@
+"""Pins of the fp64 oracle against facts the pages and mathematics fix.
+
+Each ``pin_*`` function takes the oracle module (so that the mutation tests can
+hand in a copy with a planted mistake) and raises AssertionError when the
+module disagrees with a closed form, an invariant, an equivalence of two
+different algorithms, or brute-force summation.  None of them re-types the
+oracle's own formula: expected values come from special inputs whose result
+the pages' definitions give in closed form, or from sums written out here.
+
+Pages (title, section):
+  RetNet reading notes (mzeromiko): §2.2 recurrent, §2.3 parallel, §2.4
+  chunkwise, §三.2 MSR, §三.3 normalisation.
+  e993 news page (RetNet paper translation): the three forms are rewritings of
+  one mapping; GroupNorm's scale invariance makes the normalisation tricks
+  leave the final result unchanged.
+"""
+
+import numpy as np
+
+XPOS, SCALE_QK, NORM_DROW, NORM_SCORE = 1, 2, 4, 8
+NORM_ALL = SCALE_QK | NORM_DROW | NORM_SCORE
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    ref = max(np.max(np.abs(b)), 1e-300)
+    err = np.max(np.abs(a - b)) / ref
+    assert err <= rtol, f"{what}: rel err {err:.3e} > {rtol:.1e}"
+
+
+def _thetas(dk):
+    return 10000.0 ** (-2.0 * np.arange(dk // 2) / dk)
+
+
+# ---------------------------------------------------------------- parameters
+
+def pin_gamma_theta(m):
+    # MSR module: gamma = 1 - 2^(-5 - arange(0, h)); exact binary fractions
+    g = m.gammas(4)
+    assert np.array_equal(g, [0.96875, 0.984375, 0.9921875, 0.99609375]), g
+    # theta_j = 10000^(-2j/d_k) with d_k = 8 gives 10^-j
+    _close(m.thetas(8), [1.0, 0.1, 0.01, 0.001], 1e-15, "theta ladder")
+
+
+# -------------------------------------------------------- form equivalence
+
+def pin_forms_agree(m, L=128, flags_list=range(16), chunks=(1, 2, 3, 5, 8, 16, 32, 64, 100, 128),
+                    b=1, h=2, dk=8, dv=6, seed=0):
+    """Recurrent == parallel == chunkwise (every chunk size) in fp64.
+
+    B = 1 reduces the chunkwise form to the recurrent one and B >= L to the
+    parallel one; the normalisers of the parallel form are explicit row sums.
+    """
+    q = _rand((b, h, L, dk), seed)
+    k = _rand((b, h, L, dk), seed + 1)
+    v = _rand((b, h, L, dv), seed + 2)
+    g = np.array([0.75, 0.96875])[:h] if h <= 2 else m.gammas(h)
+    th = _thetas(dk)
+    for flags in flags_list:
+        o_par = m.retention_parallel(q, k, v, g, th, flags, pos0=3)
+        o_rec, S_rec, z_rec = m.retention_recurrent(q, k, v, g, th, flags, pos0=3)
+        _close(o_rec, o_par, 1e-12, f"recurrent vs parallel flags={flags}")
+        for B in chunks:
+            o_ch, S_ch, z_ch = m.retention_chunkwise(q, k, v, g, th, flags, B, pos0=3)
+            _close(o_ch, o_par, 1e-12, f"chunkwise B={B} vs parallel flags={flags}")
+            _close(S_ch, S_rec, 1e-12, f"chunkwise B={B} final state flags={flags}")
+            _close(z_ch, z_rec, 1e-12, f"chunkwise B={B} final key-sum flags={flags}")
+
+
+def _all_forms(m, q, k, v, g, th, flags, chunks=(1, 3, 4, 7, 64), pos0=0):
+    yield "parallel", m.retention_parallel(q, k, v, g, th, flags, pos0=pos0)
+    yield "recurrent", m.retention_recurrent(q, k, v, g, th, flags, pos0=pos0)[0]
+    for B in chunks:
+        yield f"chunkwise B={B}", m.retention_chunkwise(q, k, v, g, th, flags, B, pos0=pos0)[0]
+
+
+# ------------------------------------------------------------ closed forms
+
+def pin_onehot_decay(m):
+    """q_n = e_a, a single key e_a with value e_c at m0: O_n[c] = gamma^(n-m0), n >= m0.
+
+    D is causal including the diagonal (§2.3); no normalisation flags.
+    """
+    L, dk, dv, a, c, m0 = 20, 4, 3, 1, 2, 6
+    g = np.array([0.8, 0.5])
+    q = np.zeros((1, 2, L, dk)); q[..., a] = 1.0
+    k = np.zeros((1, 2, L, dk)); k[:, :, m0, a] = 1.0
+    v = np.zeros((1, 2, L, dv)); v[:, :, m0, c] = 1.0
+    n = np.arange(L)
+    want = np.zeros((1, 2, L, dv))
+    for hh in range(2):
+        want[0, hh, :, c] = np.where(n >= m0, g[hh] ** np.maximum(n - m0, 0), 0.0)
+    for name, o in _all_forms(m, q, k, v, g, _thetas(dk), 0):
+        _close(o, want, 1e-14, f"one-hot decay ({name})")
+
+
+def _xpos_setup(q_axis, k_axis, L=24, dk=8, dv=3, m0=5, scale=1.0):
+    q = np.zeros((1, 1, L, dk)); q[..., q_axis] = scale
+    k = np.zeros((1, 1, L, dk)); k[:, :, m0, k_axis] = 1.0
+    v = np.zeros((1, 1, L, dv)); v[:, :, m0, 1] = 1.0
+    return q, k, v
+
+
+def pin_xpos_closed_form(m):
+    """Real form of e^{i n theta}: pair (2j, 2j+1) rotated by +p theta_j.
+
+    q = e_{2j}, key e_{2j+1} at m0 -> O_n = gamma^(n-m0) sin((n-m0) theta_j);
+    key e_{2j} -> cos; q = e_{2j+1}, key e_{2j} -> -sin.  Independent of pos0.
+    """
+    L, dk, m0, j = 24, 8, 5, 1
+    th = _thetas(dk) * 3.0
+    g = np.array([0.9])
+    n = np.arange(L)
+    d = n - m0
+    base = np.where(d >= 0, 0.9 ** np.maximum(d, 0), 0.0)
+    cases = [(2 * j, 2 * j + 1, np.sin(d * th[j])),
+             (2 * j, 2 * j, np.cos(d * th[j])),
+             (2 * j + 1, 2 * j, -np.sin(d * th[j])),
+             (2 * j + 1, 2 * j + 1, np.cos(d * th[j]))]
+    for qa, ka, trig in cases:
+        q, k, v = _xpos_setup(qa, ka, L, dk, m0=m0)
+        want = np.zeros((1, 1, L, 3))
+        want[0, 0, :, 1] = base * trig
+        for pos0 in (0, 1000):
+            for name, o in _all_forms(m, q, k, v, g, th, XPOS, pos0=pos0):
+                _close(o, want, 1e-12, f"xpos q=e{qa} k=e{ka} pos0={pos0} ({name})")
+
+
+def pin_drow_scale_closed_form(m):
+    """QK^T/sqrt(d_k) and D~ = D / sqrt(sum_{i<=n} D_ni) on the one-hot input.
+
+    The D row sum is summed term by term here (the page's definition), not
+    taken from the geometric-series closed form.
+    """
+    L, dk, m0, j = 30, 8, 4, 2
+    th = _thetas(dk)
+    g = np.array([0.97])
+    q, k, v = _xpos_setup(2 * j, 2 * j, L, dk, m0=m0)
+    n = np.arange(L)
+    rowsum = np.array([sum(0.97 ** (nn - i) for i in range(nn + 1)) for nn in n])
+    d = n - m0
+    want = np.zeros((1, 1, L, 3))
+    want[0, 0, :, 1] = np.where(d >= 0, 0.97 ** np.maximum(d, 0), 0.0) * np.cos(d * th[j])
+    w_scale = want / np.sqrt(dk)
+    w_drow = want / np.sqrt(rowsum)[None, None, :, None]
+    for flags, w in ((XPOS | SCALE_QK, w_scale), (XPOS | NORM_DROW, w_drow),
+                     (XPOS | SCALE_QK | NORM_DROW, w_drow / np.sqrt(dk))):
+        for name, o in _all_forms(m, q, k, v, g, th, flags):
+            _close(o, w, 1e-12, f"flags={flags} ({name})")
+
+
+def pin_score_clamp(m):
+    """R~ = R / max(|sum_i R_ni|, 1): with one live key the row sum is the score.
+
+    With q scaled by 1e4 the clamp is active and the output is sign(score),
+    i.e. exactly +-1; rows whose |score| < 1 stay unnormalised.
+    """
+    L, dk, m0, j = 40, 8, 3, 0
+    th = _thetas(dk) * 0.37
+    g = np.array([0.95])
+    q, k, v = _xpos_setup(2 * j, 2 * j, L, dk, m0=m0, scale=1e4)
+    n = np.arange(L)
+    d = n - m0
+    score = np.where(d >= 0, 1e4 * 0.95 ** np.maximum(d, 0) * np.cos(d * th[j]), 0.0)
+    active = np.abs(score) >= 1.0
+    assert active.sum() > 20 and (~active & (d >= 0)).sum() >= 0
+    for name, o in _all_forms(m, q, k, v, g, th, XPOS | NORM_SCORE):
+        o1 = o[0, 0, :, 1]
+        assert np.allclose(o1[active], np.sign(score[active]), rtol=0, atol=1e-12), f"clamp ({name})"
+        assert np.allclose(o1[~active], score[~active], rtol=0, atol=1e-12), f"unclamped rows ({name})"
+        assert np.all(o[0, 0, :, [0, 2]] == 0.0)
+    # a row sum that is negative uses |.|: the sign of the output follows the score
+    assert np.any(score[active] < 0)
+
+
+# ------------------------------------------------------------- invariants
+
+def pin_groupnorm_invariance(m):
+    """GroupNorm(alpha * head) = GroupNorm(head): the three normalisation
+    factors are positive per-row scalars, so GN of the retention output is the
+    same for every combination of them (e993 news page, normalisation)."""
+    b, h, L, dk, dv = 2, 3, 33, 8, 6
+    q = _rand((b, h, L, dk), 10)
+    k = _rand((b, h, L, dk), 11)
+    v = _rand((b, h, L, dv), 12)
+    g = m.gammas(h)
+    th = _thetas(dk)
+    ref = None
+    for f in range(8):
+        flags = XPOS | (f << 1)
+        o = m.retention_chunkwise(q, k, v, g, th, flags, 7)[0]
+        gn = m.group_norm_heads(o, eps=0.0)
+        if ref is None:
+            ref = gn
+        else:
+            _close(gn, ref, 1e-10, f"GN invariance flags={flags}")
+    # per (token, head) group: mean 0, biased variance 1
+    gg = ref.reshape(b, L, h, dv)
+    assert np.max(np.abs(gg.mean(-1))) < 1e-12
+    assert np.max(np.abs((gg ** 2).mean(-1) - 1.0)) < 1e-10
+    # per-token positive rescaling of a head is invisible
+    o = m.retention_chunkwise(q, k, v, g, th, XPOS, 7)[0]
+    alpha = np.exp(_rand((b, h, L, 1), 13))
+    _close(m.group_norm_heads(o * alpha, 0.0), m.group_norm_heads(o, 0.0), 1e-10, "GN per-token alpha")
+
+
+def pin_groupnorm_values(m):
+    """Hand-computed GroupNorm of one group: [1,2,3,4] has mean 2.5 and biased
+    variance 1.25, so it maps to [-3,-1,1,3]/sqrt(5); the group of the second
+    head is independent of the first; the affine is per channel."""
+    y = np.zeros((1, 2, 1, 4))
+    y[0, 0, 0] = [1, 2, 3, 4]
+    y[0, 1, 0] = [10, 10, 10, 14]          # mean 11, var 3
+    out = m.group_norm_heads(y, eps=0.0)
+    want = np.array([[-3, -1, 1, 3]]) / np.sqrt(5.0)
+    _close(out[0, 0, :4], want[0], 1e-15, "GN head 0")
+    _close(out[0, 0, 4:], np.array([-1, -1, -1, 3]) / np.sqrt(3.0), 1e-15, "GN head 1")
+    w = np.arange(1, 9, dtype=np.float64)
+    bb = -np.arange(8, dtype=np.float64)
+    out2 = m.group_norm_heads(y, eps=0.0, weight=w, bias=bb)
+    _close(out2, out * w + bb, 1e-15, "GN affine")
+    # eps enters under the square root: [1, -1] with eps=3 -> [1,-1]/2
+    y2 = np.array([1.0, -1.0]).reshape(1, 1, 1, 2)
+    _close(m.group_norm_heads(y2, eps=3.0)[0, 0], [0.5, -0.5], 1e-15, "GN eps")
+
+
+def pin_swish(m):
+    """swish(x) = x sigmoid(x): 0 at 0, ~x for large x, ~0 for very negative x,
+    swish(1) = 1/(1 + 1/e) = 0.7310585786300049."""
+    x = np.array([0.0, 1.0, 40.0, -40.0, -1.0])
+    s = m.swish(x)
+    assert s[0] == 0.0
+    assert abs(s[1] - 0.7310585786300049) < 1e-15
+    assert abs(s[2] - 40.0) < 1e-12 and abs(s[3]) < 1e-15
+    assert abs(s[4] + 0.2689414213699951) < 1e-15
+    # gate applies swish(g) elementwise to the normalised heads
+    y = np.array([1.0, 2.0, 3.0, 4.0]).reshape(1, 1, 1, 4)
+    gate = np.array([[[0.0, 1.0, 40.0, -1.0]]])
+    out = m.gate_norm(y, gate, 0.0)
+    yn = np.array([-3, -1, 1, 3]) / np.sqrt(5.0)
+    _close(out[0, 0], yn * np.array([0.0, 0.7310585786300049, 40.0, -0.2689414213699951]),
+           1e-12, "gate")
+
+
+def pin_relative_position(m):
+    """Scores depend on n - m only (§2.1): shifting pos0 leaves O unchanged."""
+    b, h, L, dk, dv = 1, 2, 29, 8, 5
+    q = _rand((b, h, L, dk), 20)
+    k = _rand((b, h, L, dk), 21)
+    v = _rand((b, h, L, dv), 22)
+    g = m.gammas(h)
+    th = _thetas(dk)
+    for flags in (XPOS, XPOS | NORM_ALL):
+        a = m.retention_chunkwise(q, k, v, g, th, flags, 8, pos0=0)[0]
+        bb = m.retention_chunkwise(q, k, v, g, th, flags, 8, pos0=1000)[0]
+        _close(bb, a, 1e-10, f"pos0 shift flags={flags}")
+        c = m.retention_recurrent(q, k, v, g, th, flags, pos0=777)[0]
+        _close(c, a, 1e-10, f"pos0 shift recurrent flags={flags}")
+
+
+def pin_split_resume(m):
+    """The state (R, z) is the whole sequence checkpoint: running L1 tokens,
+    handing (R, z) over and running the rest (positions and token counts
+    continuing) equals one pass, at any split point and chunk size."""
+    b, h, L, dk, dv = 2, 2, 45, 8, 6
+    q = _rand((b, h, L, dk), 30)
+    k = _rand((b, h, L, dk), 31)
+    v = _rand((b, h, L, dv), 32)
+    g = m.gammas(h)
+    th = _thetas(dk)
+    flags = XPOS | NORM_ALL
+    full, S_full, z_full = m.retention_chunkwise(q, k, v, g, th, flags, 8)
+    for L1, B1, B2 in ((1, 4, 8), (13, 5, 3), (32, 16, 7), (44, 44, 1)):
+        o1, S1, z1 = m.retention_chunkwise(q[:, :, :L1], k[:, :, :L1], v[:, :, :L1], g, th, flags, B1)
+        o2, S2, z2 = m.retention_chunkwise(q[:, :, L1:], k[:, :, L1:], v[:, :, L1:], g, th, flags, B2,
+                                           pos0=L1, n_prev=L1, state_in=S1, z_in=z1)
+        _close(np.concatenate([o1, o2], axis=2), full, 1e-12, f"split at {L1}")
+        _close(S2, S_full, 1e-12, f"state after split {L1}")
+        _close(z2, z_full, 1e-12, f"key-sum after split {L1}")
+        o3, S3, _ = m.retention_recurrent(q[:, :, L1:], k[:, :, L1:], v[:, :, L1:], g, th, flags,
+                                          pos0=L1, n_prev=L1, state_in=S1, z_in=z1)
+        _close(o3, o2, 1e-12, f"recurrent resume at {L1}")
+
+
+def pin_causality_linearity(m):
+    """D is zero above the diagonal: tokens after p never change o_<=p.
+    Without the score clamp the map is linear in V."""
+    b, h, L, dk, dv = 1, 2, 31, 8, 4
+    q = _rand((b, h, L, dk), 40)
+    k = _rand((b, h, L, dk), 41)
+    v = _rand((b, h, L, dv), 42)
+    g = m.gammas(h)
+    th = _thetas(dk)
+    p = 17
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[:, :, p + 1:] += 5.0
+    k2[:, :, p + 1:] -= 3.0
+    v2[:, :, p + 1:] *= -2.0
+    for flags in (XPOS, XPOS | NORM_ALL):
+        for B in (1, 6, 64):
+            a = m.retention_chunkwise(q, k, v, g, th, flags, B)[0]
+            c = m.retention_chunkwise(q2, k2, v2, g, th, flags, B)[0]
+            assert np.array_equal(a[:, :, :p + 1], c[:, :, :p + 1]) or \
+                np.max(np.abs(a[:, :, :p + 1] - c[:, :, :p + 1])) < 1e-13
+            assert np.max(np.abs(a[:, :, p + 1:] - c[:, :, p + 1:])) > 1e-3
+    w = _rand((b, h, L, dv), 43)
+    flags = XPOS | SCALE_QK | NORM_DROW
+    lhs = m.retention_chunkwise(q, k, 2.0 * v - 3.0 * w, g, th, flags, 6)[0]
+    rhs = 2.0 * m.retention_chunkwise(q, k, v, g, th, flags, 6)[0] - 3.0 * m.retention_chunkwise(q, k, w, g, th, flags, 6)[0]
+    _close(lhs, rhs, 1e-12, "linear in V")
+
+
+# ----------------------------------------------------------------- decode
+
+def pin_decode_zero_kv(m):
+    """With k = v = 0 the step only decays: S_t = gamma^t S_0 and
+    o_t = gamma^(t+1) q'_t S_0 (state read after the update)."""
+    b, h, dk, dv = 2, 3, 8, 5
+    g = m.gammas(h)
+    th = _thetas(dk)
+    S0 = _rand((b, h, dk, dv), 50)
+    S = S0.copy()
+    zero_k = np.zeros((b, h, dk))
+    zero_v = np.zeros((b, h, dv))
+    for t in range(6):
+        # q = e_0 picks row 0 of the state after rotation by phi = pos*theta_0:
+        # q' = (cos phi, sin phi, 0, ...) -> o = cos phi S[0] + sin phi S[1]
+        qv = np.zeros((b, h, dk)); qv[..., 0] = 1.0
+        pos = 100 + t
+        o, S, _ = m.recurrent_step(qv, zero_k, zero_v, S, g, th, XPOS, pos, pos + 1)
+        decay = (g ** (t + 1))[None, :, None]
+        _close(S, S0 * decay[..., None], 1e-14, f"S_t decay t={t}")
+        phi = pos * th[0]
+        want = decay * (np.cos(phi) * S0[:, :, 0, :] + np.sin(phi) * S0[:, :, 1, :])
+        _close(o, want, 1e-13, f"o_t t={t}")
+
+
+def pin_decode_vs_chunkwise(m):
+    """Prefill with the chunkwise form, then decode token by token: equals
+    one chunkwise pass over the whole sequence (all normalisations on, the
+    key-sum z carried for the score normaliser)."""
+    b, h, L, dk, dv = 1, 2, 20, 8, 6
+    q = _rand((b, h, L, dk), 60)
+    k = _rand((b, h, L, dk), 61)
+    v = _rand((b, h, L, dv), 62)
+    g = m.gammas(h)
+    th = _thetas(dk)
+    flags = XPOS | NORM_ALL
+    full = m.retention_chunkwise(q, k, v, g, th, flags, 4)[0]
+    L1 = 12
+    _, S, z = m.retention_chunkwise(q[:, :, :L1], k[:, :, :L1], v[:, :, :L1], g, th, flags, 5)
+    for t in range(L1, L):
+        o, S, z = m.recurrent_step(q[:, :, t], k[:, :, t], v[:, :, t], S, g, th, flags, t, t + 1, z=z)
+        _close(o, full[:, :, t], 1e-12, f"decode step {t}")
+
+
+# ------------------------------------------------------------------ block
+
+def pin_block(m):
+    """MSR block (§三.2): X W_G = 0 gives 0 (swish(0) = 0); scaling W_O scales
+    the output; scaling W_V by alpha > 0 changes nothing (GroupNorm after the
+    retention, eps = 0); heads take contiguous column blocks; the chunk size
+    does not change the result."""
+    b, L, dm, h, dk, dv = 1, 19, 8, 2, 4, 6
+    r = np.random.default_rng(70)
+    X = r.standard_normal((b, L, dm))
+    WQ, WK = r.standard_normal((dm, h * dk)), r.standard_normal((dm, h * dk))
+    WV, WG = r.standard_normal((dm, h * dv)), r.standard_normal((dm, h * dv))
+    WO = r.standard_normal((h * dv, dm))
+    th = _thetas(dk)
+    flags = XPOS | NORM_ALL
+    out = m.msr_forward(X, WQ, WK, WV, WG, WO, h, th, flags, 5, 0.0)
+    assert out.shape == (b, L, dm)
+    assert np.max(np.abs(m.msr_forward(X, WQ, WK, WV, 0 * WG, WO, h, th, flags, 5, 0.0))) == 0.0
+    _close(m.msr_forward(X, WQ, WK, WV, WG, 3.0 * WO, h, th, flags, 5, 0.0), 3.0 * out, 1e-13, "W_O scale")
+    _close(m.msr_forward(X, WQ, WK, WV, WG, WO, h, th, flags, 64, 0.0), out, 1e-11, "chunk size")
+    flags2 = XPOS | SCALE_QK | NORM_DROW
+    o2 = m.msr_forward(X, WQ, WK, WV, WG, WO, h, th, flags2, 5, 0.0)
+    _close(m.msr_forward(X, WQ, WK, 2.5 * WV, WG, WO, h, th, flags2, 5, 0.0), o2, 1e-11, "W_V scale")
+    # the gate multiplies the normalised heads before W_O: with W_O a
+    # permutation and a positive per-column gate, undoing both leaves groups
+    # of mean 0 and variance 1
+    dm2 = h * dv
+    X2 = r.standard_normal((b, L, dm2)); X2[..., 0] = 1.0
+    WQ2, WK2 = r.standard_normal((dm2, h * dk)), r.standard_normal((dm2, h * dk))
+    WV2 = r.standard_normal((dm2, h * dv))
+    WG2 = np.zeros((dm2, h * dv)); WG2[0] = 2.0 + r.random(h * dv)
+    perm = np.arange(dm2)[::-1].copy()
+    WO2 = np.eye(dm2)[:, perm]
+    out2 = m.msr_forward(X2, WQ2, WK2, WV2, WG2, WO2, h, th, flags, 5, 0.0)
+    gate = WG2[0] / (1.0 + np.exp(-WG2[0]))
+    ynorm = (out2 @ WO2.T / gate).reshape(b, L, h, dv)
+    assert np.max(np.abs(ynorm.mean(-1))) < 1e-12
+    assert np.max(np.abs((ynorm ** 2).mean(-1) - 1.0)) < 1e-10
+    # split_heads: column c of head i is input column i*d + c
+    x = np.arange(2 * 3 * 8, dtype=np.float64).reshape(2, 3, 8)
+    s = m.split_heads(x, 2)
+    assert s.shape == (2, 2, 3, 4)
+    for bb in range(2):
+        for i in range(2):
+            for t in range(3):
+                for c in range(4):
+                    assert s[bb, i, t, c] == x[bb, t, i * 4 + c]
+    # fp64 matmul of the block against a triple loop on a small case
+    A = r.standard_normal((3, 4)); Bm = r.standard_normal((4, 5))
+    C = np.zeros((3, 5))
+    for i in range(3):
+        for j in range(5):
+            for kk in range(4):
+                C[i, j] += A[i, kk] * Bm[kk, j]
+    _close(A @ Bm, C, 1e-14, "matmul vs loops")
+
+
+def pin_pages_shape_example(m):
+    """The zyxy lecture's examples print torch.Size([2, 5, 8]) for batch 2,
+    seq 5, d_model 8 (single head and N = 2 heads); see tests/golden."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "pages_shapes.json")) as f:
+        gold = json.load(f)
+    ex = gold["zyxy_examples"]
+    b, L, dm = ex["batch_size"], ex["seq_len"], ex["d_model"]
+    r = np.random.default_rng(80)
+    Q, K, V = (r.standard_normal((b, 1, L, dm)) for _ in range(3))
+    o = m.retention_parallel(Q, K, V, np.array([ex["gamma"]]), None, 0)
+    assert list(o.shape[:1]) + list(o.shape[2:]) == ex["printed_shape"]
+    Qh = m.split_heads(r.standard_normal((b, L, dm)), ex["N"])
+    o2 = m.retention_recurrent(Qh, Qh, Qh, np.array([0.9, 0.8]), None, 0)[0]
+    assert list(np.transpose(o2, (0, 2, 1, 3)).reshape(b, L, dm).shape) == ex["printed_shape"]
+
+
+ALL_PINS = [pin_gamma_theta, pin_forms_agree, pin_onehot_decay, pin_xpos_closed_form,
+            pin_drow_scale_closed_form, pin_score_clamp, pin_groupnorm_invariance,
+            pin_groupnorm_values, pin_swish, pin_relative_position, pin_split_resume,
+            pin_causality_linearity, pin_decode_zero_kv, pin_decode_vs_chunkwise, pin_block,
+            pin_pages_shape_example]
+
+
+def quick_forms(m):
+    """A cheaper form-equivalence pass for the mutation tests."""
+    pin_forms_agree(m, L=37, flags_list=(0, XPOS, XPOS | NORM_ALL, NORM_SCORE, NORM_DROW | SCALE_QK),
+                    chunks=(1, 5, 16, 40), b=1, h=2)
