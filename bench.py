@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the retention hot path on one MI355X.
+
+A step is one retention_chunkwise_fwd over the medium workload (batch 4, 8
+heads, L = 2048, d_k = 256, d_v = 512, bf16 inputs, chunk B = 512, xPos and all
+three normalisations, bf16 output): value = tokens/s = b*L / step time.  The
+inputs are resident in HBM before timing; three input/output buffer sets are
+rotated so the 256 MB MALL cannot serve a repeated set.  Secondary lines in
+the same JSON record: the same workload at B = 64, the long workload (L =
+32768, 16 heads), the decode step (batch 128, 16 heads, 64 steps from
+position 8192) and the GroupNorm + gate epilogue at the block shape.
+
+Prints ONE JSON line.  Only N = 1 GPU is supported.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def chunk_flops(b, h, L, dk, dv, B, with_state_out=False):
+    """Algorithmic flops of the chunkwise form: causal half of the intra-chunk
+    scores and P.V, the cross term for chunks >= 1 and the state update for
+    chunks that feed a later chunk (plus the last one when the state is
+    written out)."""
+    nc = (L + B - 1) // B
+    intra = sum(min(B, L - c * B) * (min(B, L - c * B) + 1) * (dk + dv) for c in range(nc))
+    cross = (nc - 1) * 2 * B * dk * dv
+    state = (nc - 1 + (1 if with_state_out else 0)) * 2 * B * dk * dv
+    return b * h * (intra + cross + state)
+
+
+def chunk_bytes(b, h, L, dk, dv, in_bytes=2, out_bytes=2):
+    return b * h * L * (2 * dk * in_bytes + dv * in_bytes + dv * out_bytes)
+
+
+def time_calls(fn, n, warmup, torch):
+    """Average ms per call of fn() over n calls, HIP events on the stream the
+    library launches on (torch's current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(n):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def make_chunk_sets(cfg, nsets, torch, W, dev):
+    q, k, v = W.chunkwise_inputs(**cfg)
+    sets = []
+    for s in range(nsets):
+        sets.append((dev(q), dev(k), dev(v),
+                     torch.empty((cfg["b"], cfg["h"], cfg["L"], cfg["dv"]), dtype=torch.bfloat16, device="cuda")))
+    return sets, (q, k, v)
+
+
+def cpu_baseline(cfg, B, W):
+    """The fp64 oracle (chunkwise form, numpy + BLAS) on a bounded sample of
+    the medium workload: one of its batch sequences (all heads, full L)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    q, k, v = W.chunkwise_inputs(**cfg)
+    sl = slice(0, 1)
+    qs, ks, vs = (W.as_f32(a[sl], cfg["dtype"]).astype(np.float64) for a in (q, k, v))
+    g, th = W.gamma_vector(cfg["h"]), W.theta_vector(cfg["dk"])
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.retention_chunkwise(qs, ks, vs, g, th, cfg["flags"], B)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 8:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    toks = cfg["L"]   # one sequence of L tokens (all heads)
+    return {"value": toks / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle.retention_chunkwise (fp64 numpy/BLAS), 1 of {cfg['b']} sequences "
+                      f"(all {cfg['h']} heads, L={cfg['L']}, B={B}), {reps} run(s) of {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-primary", action="store_true", help="time the primary workload only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the path is single-GPU "
+              "and its multi-GPU sharding is a design note, not a measured mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_sequence_retention_amd import binding as R
+    from linear_attention_sequence_retention_amd import workloads as W
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    cfg = W.CHUNKWISE["medium"]
+    b, h, L, dk, dv = cfg["b"], cfg["h"], cfg["L"], cfg["dk"], cfg["dv"]
+    g, th = W.gamma_vector(h), W.theta_vector(dk)
+    flags = cfg["flags"]
+    B = 512
+    sets, host = make_chunk_sets(cfg, 3, torch, W, dev)
+    it = [0]
+
+    def step(Bc=B):
+        qd, kd, vd, od = sets[it[0] % 3]
+        it[0] += 1
+        R.chunkwise_fwd(qd, kd, vd, g, th, Bc, flags, out=od)
+
+    # ---- primary: K timed steps bracketed by synchronisation
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_kernel = time_calls(step, args.steps, 0, torch)
+    wall = time.perf_counter() - t0
+    ms = ms_kernel
+    tokens = b * L
+    value = tokens / (ms * 1e-3)
+    flops = chunk_flops(b, h, L, dk, dv, B)
+    nbytes = chunk_bytes(b, h, L, dk, dv)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    intensity = flops / nbytes
+    ridge = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    bound = "hbm" if intensity < ridge else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "traffic": None}
+
+    extra = {"primary": {"kernel": "chunkwise_kernel", "ms": round(ms, 4), "tflops": round(tflops, 1),
+                         "mfma_frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "gbs": round(gbs, 1),
+                         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "alg_gflop": round(flops / 1e9, 2),
+                         "alg_mb": round(nbytes / 1e6, 1), "wall_s": round(wall, 3)}}
+
+    if not args.only_primary:
+        # same workload at B = 64
+        ms64 = time_calls(lambda: step(64), max(5, args.steps // 2), 2, torch)
+        f64_ = chunk_flops(b, h, L, dk, dv, 64)
+        extra["medium_B64"] = {"ms": round(ms64, 4), "tokens_per_s": tokens / (ms64 * 1e-3),
+                               "tflops": round(f64_ / (ms64 * 1e-3) / 1e12, 1),
+                               "mfma_frac": round(f64_ / (ms64 * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                               "gbs": round(nbytes / (ms64 * 1e-3) / 1e9, 1)}
+        del sets[:]
+        torch.cuda.empty_cache()
+        # long workload
+        lc = W.CHUNKWISE["long"]
+        lq, lk, lv = W.chunkwise_inputs(**lc)
+        lqd, lkd, lvd = dev(lq), dev(lk), dev(lv)
+        del lq, lk, lv
+        lo = torch.empty((lc["b"], lc["h"], lc["L"], lc["dv"]), dtype=torch.bfloat16, device="cuda")
+        lg, lth = W.gamma_vector(lc["h"]), W.theta_vector(lc["dk"])
+        msl = time_calls(lambda: R.chunkwise_fwd(lqd, lkd, lvd, lg, lth, 512, lc["flags"], out=lo), 3, 1, torch)
+        fl = chunk_flops(lc["b"], lc["h"], lc["L"], lc["dk"], lc["dv"], 512)
+        bl = chunk_bytes(lc["b"], lc["h"], lc["L"], lc["dk"], lc["dv"])
+        extra["long_B512"] = {"ms": round(msl, 3), "tokens_per_s": lc["b"] * lc["L"] / (msl * 1e-3),
+                              "tflops": round(fl / (msl * 1e-3) / 1e12, 1),
+                              "mfma_frac": round(fl / (msl * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                              "gbs": round(bl / (msl * 1e-3) / 1e9, 1)}
+        del lqd, lkd, lvd, lo
+        torch.cuda.empty_cache()
+        # decode: 64 sequential steps at batch 128
+        dc = W.DECODE
+        db, dh, ddk, ddv = dc["b"], dc["h"], dc["dk"], dc["dv"]
+        S0, qs, ks, vs = W.decode_inputs(**dc)
+        S = torch.from_numpy(S0).cuda()
+        del S0
+        qd = [dev(x) for x in qs]
+        kd = [dev(x) for x in ks]
+        vd = [dev(x) for x in vs]
+        od = torch.empty((db, dh, ddv), dtype=torch.float32, device="cuda")
+        dg, dth = W.gamma_vector(dh), W.theta_vector(ddk)
+        pos0 = dc["pos0"]
+
+        def decode64():
+            for t in range(dc["steps"]):
+                R.recurrent_step(qd[t], kd[t], vd[t], S, dg, dth, pos0 + t, pos0 + t + 1, dc["flags"], out=od)
+        msd = time_calls(decode64, 3, 1, torch) / dc["steps"]
+        dbytes = 2 * db * dh * ddk * ddv * 4 + db * dh * (2 * ddk * 2 + ddv * 2 + ddv * 4)
+        extra["decode"] = {"ms_per_step": round(msd, 4), "gbs": round(dbytes / (msd * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(dbytes / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           "tokens_per_s": db / (msd * 1e-3), "alg_mb_per_step": round(dbytes / 1e6, 1)}
+        del S, qd, kd, vd
+        torch.cuda.empty_cache()
+        # GroupNorm + gate at the block shape (2 x 8192 tokens, 16 heads x 512)
+        gb, gL, gh, gdv = 2, 8192, 16, 512
+        y = torch.randn((gb, gh, gL, gdv), device="cuda").to(torch.bfloat16)
+        gg = torch.randn((gb, gL, gh * gdv), device="cuda").to(torch.bfloat16)
+        zo = torch.empty_like(gg)
+        msg = time_calls(lambda: R.gate_norm(y, gg, 1e-5, out=zo), 20, 3, torch)
+        gbytes = 3 * gb * gL * gh * gdv * 2
+        extra["gate_norm"] = {"ms": round(msg, 4), "gbs": round(gbytes / (msg * 1e-3) / 1e9, 1),
+                              "hbm_frac": round(gbytes / (msg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    line = {
+        "metric": "chunkwise retention fwd tokens/s & % bf16 MFMA peak; decode step GB/s % HBM",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in/out, fp16 MFMA operands, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "chunkwise_fwd " + W.workload_name(cfg, B) + " xpos+all_norms",
+                   "global_batch": b, "seq_len": L, "heads": h, "d_k": dk, "d_v": dv, "chunk": B,
+                   "parallelism": "single_gpu"},
+        "roofline": roof,
+        "mfma": {"achieved": round(tflops, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(tflops / PEAK_MFMA_TFLOPS, 4)},
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, B, W)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

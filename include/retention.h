@@ -1,0 +1,163 @@
+/*
+ * retention.h -- C ABI of libretention.so, the MI355X (gfx950) hot path of
+ * RetNet multi-scale retention.
+ *
+ * Sources (page title, section):
+ *   [notes]  RetNet reading notes, mzeromiko.github.io ("阅读笔记：RetNet"):
+ *            §2.2 recurrent mode, §2.3 parallel mode (xPos Theta, decay mask D),
+ *            §2.4 chunkwise recurrent mode (R_i, zeta, xi), §三.2 MSR module
+ *            (per-head gamma, GroupNorm_h, swish gate), §三.3 normalisation.
+ *   [zyxy]   zyxy.net lecture on RetNet, §5 multi-scale grouping (the
+ *            (batch, heads, seq, d_head) head layout).
+ *
+ * Conventions shared by every entry point
+ *   - All device buffers belong to the caller.  The library never allocates,
+ *     frees or synchronises; work is enqueued on `stream` (NULL = the null
+ *     stream) and completes asynchronously.
+ *   - gamma and theta are HOST float64 arrays, read during the call only.
+ *   - Every call validates its arguments before any HIP call and returns a
+ *     ret_status; it never aborts or prints.  retention_last_error() returns a
+ *     thread-local message describing the last non-OK return.  Device faults
+ *     surface at the caller's next synchronisation, as usual in HIP.
+ *   - Tensors are row-major; the innermost (feature) axis is contiguous.
+ *     ret_strides gives the element strides of the batch, head and sequence
+ *     axes of a [b, h, L, d] view.
+ *   - bf16 values are stored as raw 16-bit patterns; every conversion to
+ *     bf16 inside the library rounds to nearest even.
+ *   - Calls on different streams are independent when their output buffers
+ *     (and workspaces) are distinct.
+ */
+#ifndef RETENTION_H
+#define RETENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RETENTION_ABI_VERSION 1
+
+typedef enum {
+  RET_OK = 0,
+  RET_E_INVAL = 1,        /* null pointer, non-positive size, gamma outside (0,1), ... */
+  RET_E_UNSUPPORTED = 2,  /* a shape or dtype combination without a compiled kernel */
+  RET_E_ALIGN = 3,        /* a pointer or stride breaks the required alignment */
+  RET_E_WORKSPACE = 4,    /* workspace missing or too small */
+  RET_E_HIP = 5           /* a HIP launch failed; the message names the HIP error */
+} ret_status;
+
+typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype;
+
+/* Flag bits selecting the steps of [notes] §2.3 and §三.3. */
+enum {
+  RET_XPOS = 1u,        /* rotate q and k: pair (2j, 2j+1) times e^{i p theta_j} ([notes] §2.3) */
+  RET_SCALE_QK = 2u,    /* QK^T -> QK^T / sqrt(d_k)                                ([notes] §三.3) */
+  RET_NORM_DROW = 4u,   /* D_nm -> D_nm / sqrt(sum_{i<=n} D_ni)                       ([notes] §三.3) */
+  RET_NORM_SCORE = 8u   /* R_nm -> R_nm / max(|sum_i R_ni|, 1), R = QK^T (.) D        ([notes] §三.3) */
+};
+#define RET_NORM_ALL (RET_SCALE_QK | RET_NORM_DROW | RET_NORM_SCORE)
+
+typedef struct { int64_t b, h, l; } ret_strides;   /* element strides of a [b,h,L,d] view */
+
+/*
+ * retention_chunkwise_fwd -- chunkwise recurrent retention forward ([notes]
+ * §2.4), with the xPos rotation of §2.3 and the normalisations of §三.3.
+ *
+ * For each (batch, head) and chunk i of B consecutive tokens (the last chunk
+ * may be shorter, B_i = min(B, L - iB)):
+ *   O_[i] = (Q_[i] K_[i]^T (.) D) V_[i] + (Q_[i] R_{i-1}) (.) xi,  xi_j = gamma^(j+1)
+ *   R_i   = K_[i]^T (V_[i] (.) zeta) + gamma^(B_i) R_{i-1},        zeta_j = gamma^(B_i-j-1)
+ * Q and K are rotated by their absolute position pos0 + t when RET_XPOS is set.
+ * The normalisations are those of the parallel form over the whole sequence
+ * (including the n_prev tokens summarised by state_in/z_in): row t has seen
+ * n = n_prev + t + 1 tokens, its score row sum is carried across chunks by
+ * the key-sum z_i = K_[i]^T zeta + gamma^(B_i) z_{i-1}, and
+ *   o_t = s_t num_t / max(|s_t den_t|, 1)   (the division only with RET_NORM_SCORE)
+ * with s_t = d_k^{-1/2} (RET_SCALE_QK) * sqrt((1-gamma)/(1-gamma^n)) (RET_NORM_DROW).
+ *
+ *   q, k   [b,h,L,d_k] of in_dt, strides sq / sk (d axis contiguous)
+ *   v      [b,h,L,d_v] of in_dt, strides sv
+ *   o      [b,h,L,d_v] of out_dt, strides so; must not overlap q, k, v
+ *   gamma  host float64 [h], each in (0, 1) ([notes] §三.2 uses 1 - 2^(-5-i))
+ *   theta  host float64 [d_k/2]; required with RET_XPOS, ignored otherwise
+ *   chunk_B  the chunk size B >= 1 (the interval at which R is carried)
+ *   pos0   absolute position of token 0 (xPos phase); n_prev tokens already
+ *          summarised by state_in / z_in (0 for a fresh sequence)
+ *   state_in / state_out  device float32 [b,h,d_k,d_v] or NULL (= zero / not
+ *          written); state_out may equal state_in
+ *   z_in / z_out  device float32 [b,h,d_k] key-sums or NULL (same rules);
+ *          a continued sequence with RET_NORM_SCORE needs z_in
+ *   workspace  device scratch of retention_chunkwise_workspace_bytes() bytes
+ *          (may be NULL when that size is 0)
+ * Supported: in_dt bf16 with (d_k, d_v) in {(32,32), (64,64), (128,128),
+ * (128,256), (256,256), (256,512)}; in_dt f32 with (d_k, d_v) in {(32,32),
+ * (64,64)}; out_dt f32 or bf16; q/k/v/o 16-byte aligned with strides that
+ * keep every row 16-byte aligned; L >= 1, b*h >= 1, h <= 64.
+ */
+int retention_chunkwise_fwd(const void* q, ret_strides sq, const void* k, ret_strides sk,
+                            const void* v, ret_strides sv, void* o, ret_strides so,
+                            int b, int h, int L, int d_k, int d_v, int chunk_B,
+                            const double* gamma, const double* theta,
+                            int64_t pos0, int64_t n_prev, unsigned flags,
+                            ret_dtype in_dt, ret_dtype out_dt,
+                            const float* state_in, float* state_out,
+                            const float* z_in, float* z_out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace retention_chunkwise_fwd needs for this problem. */
+size_t retention_chunkwise_workspace_bytes(int b, int h, int L, int d_k, int d_v, int chunk_B,
+                                           unsigned flags);
+
+/*
+ * retention_recurrent_step -- one decode step of the recurrent form
+ * ([notes] §2.2): S <- gamma S + k'^T v, o = q' S, the current token included.
+ *
+ *   q, k   [b,h,d_k] of in_dt (contiguous); v [b,h,d_v] of in_dt
+ *   S      device float32 [b,h,d_k,d_v], updated in place
+ *   z      device float32 [b,h,d_k] key-sum, updated in place (z <- gamma z + k'),
+ *          or NULL; required with RET_NORM_SCORE
+ *   o      [b,h,d_v] of out_dt (contiguous); must not overlap the inputs
+ *   pos    absolute position of this token (xPos phase)
+ *   n_tokens  tokens seen including this one (the D-row count n >= 1)
+ * The row scalings of §三.3 apply as in retention_chunkwise_fwd, so a
+ * chunkwise prefill handing (state_out, z_out) to this call continues the
+ * same sequence.  Supported: d_k even, 2 <= d_k <= 512; d_v a multiple of 4,
+ * 4 <= d_v <= 1024; S 16-byte aligned.
+ */
+int retention_recurrent_step(const void* q, const void* k, const void* v, float* S, float* z,
+                             void* o, int b, int h, int d_k, int d_v,
+                             const double* gamma, const double* theta,
+                             int64_t pos, int64_t n_tokens, unsigned flags,
+                             ret_dtype in_dt, ret_dtype out_dt, hipStream_t stream);
+
+/*
+ * msr_gate_norm -- the MSR epilogue before W_O ([notes] §三.2):
+ *   Z = swish(G) (.) GroupNorm_h(Concat(head_1 .. head_h))
+ * GroupNorm_h normalises each head's d_v outputs of one token by their mean
+ * and biased variance (eps added to the variance), then applies the optional
+ * per-channel affine; swish(x) = x / (1 + e^{-x}).
+ *
+ *   y    [b,h,L,d_v] head outputs of y_dt, strides sy
+ *   g    [b,L,h*d_v] gate pre-activation X W_G of g_dt (contiguous)
+ *   out  [b,L,h*d_v] of out_dt (contiguous)
+ *   gn_weight, gn_bias  device float32 [h*d_v] or NULL (= 1 and 0)
+ * Supported: d_v a multiple of 8, 8 <= d_v <= 4096; 16-byte aligned rows.
+ */
+int msr_gate_norm(const void* y, ret_strides sy, const void* g, void* out,
+                  int b, int L, int h, int d_v,
+                  const float* gn_weight, const float* gn_bias, float eps,
+                  ret_dtype y_dt, ret_dtype g_dt, ret_dtype out_dt, hipStream_t stream);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char* retention_last_error(void);
+
+/* RETENTION_ABI_VERSION of the loaded library. */
+int retention_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RETENTION_H */

@@ -1,0 +1,189 @@
+// C ABI of libretention.so: argument validation (before any HIP call),
+// launch configuration and error reporting.  The operations are specified in
+// include/retention.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return RET_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool valid_dt(ret_dtype d) { return d == RET_F32 || d == RET_BF16; }
+size_t dt_size(ret_dtype d) { return d == RET_BF16 ? 2 : 4; }
+
+int check_gamma(const double* gamma, int h) {
+  if (!gamma) return fail(RET_E_INVAL, "gamma is NULL");
+  for (int i = 0; i < h; ++i)
+    if (!(gamma[i] > 0.0 && gamma[i] < 1.0)) return fail(RET_E_INVAL, "gamma[%d] = %g is not in (0, 1)", i, gamma[i]);
+  return RET_OK;
+}
+
+int check_theta(const double* theta, int dk, unsigned flags) {
+  if (!(flags & RET_XPOS)) return RET_OK;
+  if (!theta) return fail(RET_E_INVAL, "RET_XPOS needs theta");
+  if (dk % 2) return fail(RET_E_INVAL, "RET_XPOS needs an even d_k (got %d)", dk);
+  for (int j = 0; j < dk / 2; ++j)
+    if (!isfinite(theta[j])) return fail(RET_E_INVAL, "theta[%d] is not finite", j);
+  return RET_OK;
+}
+
+// a [b,h,L,d] view whose rows are 16-byte aligned
+int check_view(const char* name, const void* p, ret_strides s, size_t esz) {
+  if (!p) return fail(RET_E_INVAL, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(RET_E_ALIGN, "%s is not 16-byte aligned", name);
+  const int64_t a = 16 / (int64_t)esz;
+  if (s.b % a || s.h % a || s.l % a)
+    return fail(RET_E_ALIGN, "%s strides (%lld, %lld, %lld) break 16-byte row alignment", name, (long long)s.b,
+                (long long)s.h, (long long)s.l);
+  if (s.b < 0 || s.h < 0 || s.l < 0) return fail(RET_E_INVAL, "%s has a negative stride", name);
+  return RET_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(RET_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+void fill_params(ret::HeadParams& hp, const double* gamma, int h, const double* theta, int dk, unsigned flags) {
+  memset(&hp, 0, sizeof(hp));
+  for (int i = 0; i < h; ++i) hp.gamma[i] = gamma[i];
+  if ((flags & RET_XPOS) && theta)
+    for (int j = 0; j < dk / 2; ++j) hp.theta[j] = theta[j];
+}
+
+}  // namespace
+
+extern "C" {
+
+int retention_abi_version(void) { return RETENTION_ABI_VERSION; }
+
+const char* retention_last_error(void) { return g_err; }
+
+size_t retention_chunkwise_workspace_bytes(int b, int h, int L, int d_k, int d_v, int chunk_B, unsigned flags) {
+  if (b <= 0 || h <= 0 || L <= 0 || d_k <= 0 || d_v <= 0 || chunk_B <= 0) return 0;
+  return ret::chunkwise_workspace(b, h, L, d_k, d_v, chunk_B, flags);
+}
+
+int retention_chunkwise_fwd(const void* q, ret_strides sq, const void* k, ret_strides sk,
+                            const void* v, ret_strides sv, void* o, ret_strides so,
+                            int b, int h, int L, int d_k, int d_v, int chunk_B,
+                            const double* gamma, const double* theta,
+                            int64_t pos0, int64_t n_prev, unsigned flags,
+                            ret_dtype in_dt, ret_dtype out_dt,
+                            const float* state_in, float* state_out,
+                            const float* z_in, float* z_out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (b <= 0 || h <= 0 || L <= 0 || d_k <= 0 || d_v <= 0)
+    return fail(RET_E_INVAL, "sizes must be positive (b=%d h=%d L=%d d_k=%d d_v=%d)", b, h, L, d_k, d_v);
+  if (h > ret::kMaxHeads) return fail(RET_E_UNSUPPORTED, "h = %d exceeds %d heads", h, ret::kMaxHeads);
+  if (d_k > 2 * ret::kMaxPairs) return fail(RET_E_UNSUPPORTED, "d_k = %d exceeds %d", d_k, 2 * ret::kMaxPairs);
+  if (chunk_B <= 0) return fail(RET_E_INVAL, "chunk_B must be >= 1 (got %d)", chunk_B);
+  if (pos0 < 0 || n_prev < 0) return fail(RET_E_INVAL, "pos0 and n_prev must be >= 0");
+  if (flags & ~15u) return fail(RET_E_INVAL, "unknown flag bits 0x%x", flags & ~15u);
+  if (!valid_dt(in_dt) || !valid_dt(out_dt)) return fail(RET_E_INVAL, "unknown dtype");
+  int r;
+  if ((r = check_gamma(gamma, h))) return r;
+  if ((r = check_theta(theta, d_k, flags))) return r;
+  const size_t ie = dt_size(in_dt), oe = dt_size(out_dt);
+  if ((r = check_view("q", q, sq, ie))) return r;
+  if ((r = check_view("k", k, sk, ie))) return r;
+  if ((r = check_view("v", v, sv, ie))) return r;
+  if ((r = check_view("o", o, so, oe))) return r;
+  if (o == q || o == k || o == v) return fail(RET_E_INVAL, "o must not alias q, k or v");
+  if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16)))
+    return fail(RET_E_ALIGN, "state buffers must be 16-byte aligned");
+  if ((flags & RET_NORM_SCORE) && n_prev > 0 && state_in && !z_in)
+    return fail(RET_E_INVAL, "a continued sequence with RET_NORM_SCORE needs z_in");
+  if (!ret::chunkwise_supported(in_dt, d_k, d_v))
+    return fail(RET_E_UNSUPPORTED, "no chunkwise kernel for in_dt=%s d_k=%d d_v=%d",
+                in_dt == RET_BF16 ? "bf16" : "f32", d_k, d_v);
+  const size_t need = ret::chunkwise_workspace(b, h, L, d_k, d_v, chunk_B, flags);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(RET_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : 0);
+
+  ret::HeadParams hp;
+  fill_params(hp, gamma, h, theta, d_k, flags);
+  ret::ChunkArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.sq = sq; a.sk = sk; a.sv = sv; a.so = so;
+  a.b = b; a.h = h; a.L = L; a.dk = d_k; a.dv = d_v; a.B = chunk_B;
+  a.pos0 = pos0; a.n_prev = n_prev; a.flags = flags; a.in_dt = in_dt; a.out_dt = out_dt;
+  a.state_in = state_in; a.z_in = z_in; a.state_out = state_out; a.z_out = z_out;
+  a.ws = workspace; a.ws_bytes = workspace_bytes; a.hp = &hp;
+  bool sup = true;
+  hipError_t e = ret::launch_chunkwise(a, stream, &sup);
+  if (!sup) return fail(RET_E_UNSUPPORTED, "no chunkwise kernel for this shape");
+  return hip_status(e, "retention_chunkwise_fwd launch");
+}
+
+int retention_recurrent_step(const void* q, const void* k, const void* v, float* S, float* z,
+                             void* o, int b, int h, int d_k, int d_v,
+                             const double* gamma, const double* theta,
+                             int64_t pos, int64_t n_tokens, unsigned flags,
+                             ret_dtype in_dt, ret_dtype out_dt, hipStream_t stream) {
+  if (b <= 0 || h <= 0 || d_k <= 0 || d_v <= 0)
+    return fail(RET_E_INVAL, "sizes must be positive (b=%d h=%d d_k=%d d_v=%d)", b, h, d_k, d_v);
+  if (h > ret::kMaxHeads) return fail(RET_E_UNSUPPORTED, "h = %d exceeds %d heads", h, ret::kMaxHeads);
+  if (d_k % 2 || d_k > 2 * ret::kMaxPairs) return fail(RET_E_UNSUPPORTED, "d_k must be even and <= 512 (got %d)", d_k);
+  if (d_v % 4 || d_v > 1024) return fail(RET_E_UNSUPPORTED, "d_v must be a multiple of 4 and <= 1024 (got %d)", d_v);
+  if (pos < 0 || n_tokens < 1) return fail(RET_E_INVAL, "pos must be >= 0 and n_tokens >= 1");
+  if (flags & ~15u) return fail(RET_E_INVAL, "unknown flag bits 0x%x", flags & ~15u);
+  if (!valid_dt(in_dt) || !valid_dt(out_dt)) return fail(RET_E_INVAL, "unknown dtype");
+  if (!q || !k || !v || !S || !o) return fail(RET_E_INVAL, "q, k, v, S and o must be non-NULL");
+  if (!aligned(S, 16)) return fail(RET_E_ALIGN, "S must be 16-byte aligned");
+  if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(o, 4) || (z && !aligned(z, 4)))
+    return fail(RET_E_ALIGN, "q, k, v, z and o must be 4-byte aligned");
+  if ((flags & RET_NORM_SCORE) && !z) return fail(RET_E_INVAL, "RET_NORM_SCORE needs the key-sum z");
+  if (o == (void*)S || o == q || o == k || o == v) return fail(RET_E_INVAL, "o must not alias the inputs");
+  int r;
+  if ((r = check_gamma(gamma, h))) return r;
+  if ((r = check_theta(theta, d_k, flags))) return r;
+
+  ret::HeadParams hp;
+  fill_params(hp, gamma, h, theta, d_k, flags);
+  ret::StepArgs a;
+  a.q = q; a.k = k; a.v = v; a.S = S; a.z = z; a.o = o;
+  a.b = b; a.h = h; a.dk = d_k; a.dv = d_v; a.pos = pos; a.n_tokens = n_tokens; a.flags = flags;
+  a.in_dt = in_dt; a.out_dt = out_dt; a.hp = &hp;
+  return hip_status(ret::launch_recurrent_step(a, stream), "retention_recurrent_step launch");
+}
+
+int msr_gate_norm(const void* y, ret_strides sy, const void* g, void* out,
+                  int b, int L, int h, int d_v,
+                  const float* gn_weight, const float* gn_bias, float eps,
+                  ret_dtype y_dt, ret_dtype g_dt, ret_dtype out_dt, hipStream_t stream) {
+  if (b <= 0 || L <= 0 || h <= 0 || d_v <= 0)
+    return fail(RET_E_INVAL, "sizes must be positive (b=%d L=%d h=%d d_v=%d)", b, L, h, d_v);
+  if (d_v % 8 || d_v > 4096) return fail(RET_E_UNSUPPORTED, "d_v must be a multiple of 8 and <= 4096 (got %d)", d_v);
+  if (!valid_dt(y_dt) || !valid_dt(g_dt) || !valid_dt(out_dt)) return fail(RET_E_INVAL, "unknown dtype");
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(RET_E_INVAL, "eps must be finite and >= 0");
+  int r;
+  if ((r = check_view("y", y, sy, dt_size(y_dt)))) return r;
+  if (!g || !out) return fail(RET_E_INVAL, "g and out must be non-NULL");
+  if (!aligned(g, 16) || !aligned(out, 16)) return fail(RET_E_ALIGN, "g and out must be 16-byte aligned");
+  if (out == y || out == g) return fail(RET_E_INVAL, "out must not alias y or g");
+  ret::GateArgs a;
+  a.y = y; a.sy = sy; a.g = g; a.out = out; a.b = b; a.L = L; a.h = h; a.dv = d_v;
+  a.w = gn_weight; a.bias = gn_bias; a.eps = eps; a.y_dt = y_dt; a.g_dt = g_dt; a.out_dt = out_dt;
+  return hip_status(ret::launch_gate_norm(a, stream), "msr_gate_norm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// MSR epilogue before W_O (RetNet reading notes, §三.2):
+//   Z = swish(G) (.) GroupNorm_h(Concat(head_1 .. head_h))
+// One wave per (batch, token, head) group of d_v channels: the group is held
+// in registers (8 channels per lane per 512-wide slab), its mean and biased
+// variance come from two wave reductions (centred second pass), and the
+// normalised, gated result is written once.  HBM-bound: Y and G are read
+// once and Z written once.
+#include "internal.h"
+
+namespace ret {
+
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+  __device__ __forceinline__ static void ld(const bf16* p, float* x) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    x[0] = lo_bf(u.x); x[1] = hi_bf(u.x); x[2] = lo_bf(u.y); x[3] = hi_bf(u.y);
+    x[4] = lo_bf(u.z); x[5] = hi_bf(u.z); x[6] = lo_bf(u.w); x[7] = hi_bf(u.w);
+  }
+  __device__ __forceinline__ static void st(bf16* p, const float* x) {
+    uint4 u;
+    u.x = pack_bf2(x[0], x[1]); u.y = pack_bf2(x[2], x[3]);
+    u.z = pack_bf2(x[4], x[5]); u.w = pack_bf2(x[6], x[7]);
+    *reinterpret_cast<uint4*>(p) = u;
+  }
+};
+template <> struct Vec8<float> {
+  __device__ __forceinline__ static void ld(const float* p, float* x) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  __device__ __forceinline__ static void st(float* p, const float* x) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
+};
+
+template <typename TY, typename TG, typename TO, int NI>
+__global__ void __launch_bounds__(256)
+gate_norm_kernel(const TY* __restrict__ y, ret_strides sy, const TG* __restrict__ g, TO* __restrict__ out,
+                 int L, int h, int dv, int64_t ngroups, const float* __restrict__ w,
+                 const float* __restrict__ bias, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gi = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gi >= ngroups) return;
+  const int hh = (int)(gi % h);
+  const int64_t bt = gi / h;
+  const int t = (int)(bt % L);
+  const int bb = (int)(bt / L);
+  const TY* yp = y + bb * sy.b + hh * sy.h + (int64_t)t * sy.l;
+  const int64_t row = gi * dv;   // offset of this group in G and Z
+  float x[NI][8];
+  float sum = 0.f;
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int e = 8 * lane + 512 * it;
+    if (e < dv) {
+      Vec8<TY>::ld(yp + e, x[it]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum += x[it][j];
+    }
+  }
+  const float inv_n = 1.f / (float)dv;
+  const float mean = wave_sum(sum) * inv_n;
+  float sq = 0.f;
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int e = 8 * lane + 512 * it;
+    if (e < dv) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float d = x[it][j] - mean;
+        sq += d * d;
+      }
+    }
+  }
+  const float rstd = rsqrtf(wave_sum(sq) * inv_n + eps);
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int e = 8 * lane + 512 * it;
+    if (e < dv) {
+      float gg[8], r[8];
+      Vec8<TG>::ld(g + row + e, gg);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float yn = (x[it][j] - mean) * rstd;
+        const int c = hh * dv + e + j;
+        if (w) yn *= w[c];
+        if (bias) yn += bias[c];
+        const float sw = gg[j] / (1.f + __expf(-gg[j]));
+        r[j] = sw * yn;
+      }
+      Vec8<TO>::st(out + row + e, r);
+    }
+  }
+}
+
+template <typename TY, typename TG, typename TO>
+static hipError_t launch_gn_t(const GateArgs& a, hipStream_t st) {
+  const int64_t ng = (int64_t)a.b * a.L * a.h;
+  dim3 grid((unsigned)((ng + 3) / 4));
+  const int ni = (a.dv + 511) / 512;
+#define RET_GN(NI)                                                                               \
+  hipLaunchKernelGGL((gate_norm_kernel<TY, TG, TO, NI>), grid, dim3(256), 0, st, (const TY*)a.y, \
+                     a.sy, (const TG*)a.g, (TO*)a.out, a.L, a.h, a.dv, ng, a.w, a.bias, a.eps)
+  if (ni <= 1) RET_GN(1);
+  else if (ni <= 2) RET_GN(2);
+  else if (ni <= 4) RET_GN(4);
+  else RET_GN(8);
+#undef RET_GN
+  return hipGetLastError();
+}
+
+template <typename TY, typename TG>
+static hipError_t launch_gn_o(const GateArgs& a, hipStream_t st) {
+  return a.out_dt == RET_BF16 ? launch_gn_t<TY, TG, bf16>(a, st) : launch_gn_t<TY, TG, float>(a, st);
+}
+template <typename TY>
+static hipError_t launch_gn_g(const GateArgs& a, hipStream_t st) {
+  return a.g_dt == RET_BF16 ? launch_gn_o<TY, bf16>(a, st) : launch_gn_o<TY, float>(a, st);
+}
+hipError_t launch_gate_norm(const GateArgs& a, hipStream_t st) {
+  return a.y_dt == RET_BF16 ? launch_gn_g<bf16>(a, st) : launch_gn_g<float>(a, st);
+}
+
+}  // namespace ret

@@ -1,0 +1,58 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+#pragma once
+#include "common.h"
+
+namespace ret {
+
+template <typename TO> struct Store;
+template <> struct Store<float> {
+  __device__ __forceinline__ static float cvt(float x) { return x; }
+};
+template <> struct Store<bf16> {
+  __device__ __forceinline__ static bf16 cvt(float x) { return bf16{f2bf(x)}; }
+};
+
+struct StepArgs {
+  const void *q, *k, *v;
+  float *S, *z;
+  void* o;
+  int b, h, dk, dv;
+  int64_t pos, n_tokens;
+  unsigned flags;
+  ret_dtype in_dt, out_dt;
+  const HeadParams* hp;
+};
+hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t st);
+
+struct GateArgs {
+  const void* y;
+  ret_strides sy;
+  const void* g;
+  void* out;
+  int b, L, h, dv;
+  const float *w, *bias;
+  float eps;
+  ret_dtype y_dt, g_dt, out_dt;
+};
+hipError_t launch_gate_norm(const GateArgs& a, hipStream_t st);
+
+struct ChunkArgs {
+  const void *q, *k, *v;
+  void* o;
+  ret_strides sq, sk, sv, so;
+  int b, h, L, dk, dv, B;
+  int64_t pos0, n_prev;
+  unsigned flags;
+  ret_dtype in_dt, out_dt;
+  const float *state_in, *z_in;
+  float *state_out, *z_out;
+  void* ws;
+  size_t ws_bytes;
+  const HeadParams* hp;
+};
+// returns false in *supported when no kernel is compiled for the shape
+hipError_t launch_chunkwise(const ChunkArgs& a, hipStream_t st, bool* supported);
+bool chunkwise_supported(ret_dtype in_dt, int dk, int dv);
+size_t chunkwise_workspace(int b, int h, int L, int dk, int dv, int B, unsigned flags);
+
+}  // namespace ret
