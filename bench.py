@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true", help="time the primary workload only")
+    ap.add_argument("--secondary", default="medium_B64,long,decode,gate_norm",
+                    help="comma list of secondary measurements to run (empty for none)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the path is single-GPU "
@@ -158,7 +160,8 @@ def main():
                          "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "alg_gflop": round(flops / 1e9, 2),
                          "alg_mb": round(nbytes / 1e6, 1), "wall_s": round(wall, 3)}}
 
-    if not args.only_primary:
+    todo = set() if args.only_primary else set(x for x in args.secondary.split(",") if x)
+    if "medium_B64" in todo:
         # same workload at B = 64
         ms64 = time_calls(lambda: step(64), max(5, args.steps // 2), 2, torch)
         f64_ = chunk_flops(b, h, L, dk, dv, 64)
@@ -166,8 +169,9 @@ def main():
                                "tflops": round(f64_ / (ms64 * 1e-3) / 1e12, 1),
                                "mfma_frac": round(f64_ / (ms64 * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
                                "gbs": round(nbytes / (ms64 * 1e-3) / 1e9, 1)}
-        del sets[:]
-        torch.cuda.empty_cache()
+    del sets[:]
+    torch.cuda.empty_cache()
+    if "long" in todo:
         # long workload
         lc = W.CHUNKWISE["long"]
         lq, lk, lv = W.chunkwise_inputs(**lc)
@@ -184,6 +188,7 @@ def main():
                               "gbs": round(bl / (msl * 1e-3) / 1e9, 1)}
         del lqd, lkd, lvd, lo
         torch.cuda.empty_cache()
+    if "decode" in todo:
         # decode: 64 sequential steps at batch 128
         dc = W.DECODE
         db, dh, ddk, ddv = dc["b"], dc["h"], dc["dk"], dc["dv"]
@@ -207,6 +212,7 @@ def main():
                            "tokens_per_s": db / (msd * 1e-3), "alg_mb_per_step": round(dbytes / 1e6, 1)}
         del S, qd, kd, vd
         torch.cuda.empty_cache()
+    if "gate_norm" in todo:
         # GroupNorm + gate at the block shape (2 x 8192 tokens, 16 heads x 512)
         gb, gL, gh, gdv = 2, 8192, 16, 512
         y = torch.randn((gb, gh, gL, gdv), device="cuda").to(torch.bfloat16)

@@ -108,6 +108,8 @@ int retention_chunkwise_fwd(const void* q, ret_strides sq, const void* k, ret_st
   if ((r = check_view("v", v, sv, ie))) return r;
   if ((r = check_view("o", o, so, oe))) return r;
   if (o == q || o == k || o == v) return fail(RET_E_INVAL, "o must not alias q, k or v");
+  if (sq.l >= (1 << 25) || sk.l >= (1 << 25) || sv.l >= (1 << 25))
+    return fail(RET_E_UNSUPPORTED, "sequence strides must be below 2^25 elements");
   if ((state_in && !aligned(state_in, 16)) || (state_out && !aligned(state_out, 16)))
     return fail(RET_E_ALIGN, "state buffers must be 16-byte aligned");
   if ((flags & RET_NORM_SCORE) && n_prev > 0 && state_in && !z_in)

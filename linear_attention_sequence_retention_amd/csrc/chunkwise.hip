@@ -30,7 +30,7 @@
 
 namespace ret {
 
-constexpr int NT = 256;   // threads per workgroup (4 waves)
+constexpr int NT = 512;   // threads per workgroup: 4 score waves + 4 state waves
 constexpr int TR = 64;    // query rows per tile
 constexpr int TK = 64;    // keys per tile
 
@@ -41,16 +41,20 @@ struct Smem {
   static constexpr int P = Pad<OP>::v;
   static constexpr int QP = DK + P;      // pitch of Qs / Ks / Rt rows
   static constexpr int KP = TK + P;      // pitch of Vt / Vz / Ps rows
-  OP Qs[TR * QP];
-  OP Ks[TK * QP];
+  static constexpr int CP = SV + 4;      // pitch of the fp32 cross-term tile
+  OP Qs[TR * QP];      // rotated query tile [row][d]
+  OP Ks[TK * QP];      // rotated key tile [key][d]
   OP Rt[SV * QP];      // scaled R_{c-1}^T for this slice: [col][d]
   OP Vt[SV * KP];      // V^T tile: [col][key]
   OP Vz[SV * KP];      // zeta-scaled V^T tile (diagonal tiles only)
-  OP Ps[TR * KP];      // P tile: [query][key]
+  OP Ps[TR * KP];      // P tile: [query][key]; reused to stage the output
+  float Oc[TR * CP];   // scaled cross term of the query tile
   float zs[DK];        // z_{c-1}
-  float dens[TR];      // scaled score row sums of the current query tile
-  float rscale[TR];    // s_i of the current query tile
-  float wmax[NT / 64]; // per-wave max |R| for the operand copy scale
+  float zeta[TK];      // zeta of the keys of the diagonal tile
+  float dens[TR];      // scaled score row sums of the query tile
+  float rs[TR];        // s_i of the query tile
+  float xs[TR];        // s_i xi_i (cross-term row factor)
+  float wmax[NT / 64];
 };
 
 struct KParams {
@@ -64,114 +68,96 @@ struct KParams {
   float *state_out, *z_out;
 };
 
-// Load TR rows x DK columns of Q or K (rows >= nvalid are zero), rotating each
-// pair (2j, 2j+1) of row i by the phase of absolute position pos_first + i.
-// Thread -> pair j, rows i0, i0 + RPP, ...; the phase of row i0 comes from a
-// float64-reduced fp32 sincos and advances by e^{i RPP theta_j} per step.
-template <typename T, typename OP, int DK>
-__device__ __forceinline__ void load_rot_tile(OP* __restrict__ dst, const T* __restrict__ src, int64_t rs,
-                                              int nvalid, int64_t pos_first, bool xpos,
-                                              const double* __restrict__ theta) {
-  constexpr int PAIRS = DK / 2;
-  constexpr int RPP = NT / PAIRS;
-  constexpr int NPASS = TR / RPP;
-  constexpr int QP = DK + Pad<OP>::v;
-  const int tid = threadIdx.x;
-  const int j = tid % PAIRS;
-  const int i0 = tid / PAIRS;
-  float2 x[NPASS];
-#pragma unroll
-  for (int p = 0; p < NPASS; ++p) {
-    const int i = i0 + p * RPP;
-    x[p] = (i < nvalid) ? Elem<T>::ld2(src + (int64_t)i * rs + 2 * j) : make_float2(0.f, 0.f);
-  }
-  float c = 1.f, s = 0.f, c1 = 1.f, s1 = 0.f;
-  if (xpos) {
-    phase(pos_first + i0, theta[j], c, s);
-    phase(RPP, theta[j], c1, s1);
-  }
-#pragma unroll
-  for (int p = 0; p < NPASS; ++p) {
-    const int i = i0 + p * RPP;
-    float a = x[p].x, b = x[p].y;
-    if (xpos) {
-      rot(a, b, c, s);
-      advance(c, s, c1, s1);
-    }
-    st2(dst + i * QP + 2 * j, a, b);
-  }
-}
+// Raw pair loads (two consecutive input elements) kept in one register
+// between the global load and the LDS store.
+template <typename T> struct Raw;
+template <> struct Raw<bf16> {
+  typedef uint32_t type;
+  __device__ __forceinline__ static type ld(const bf16* p) { return *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ static float2 f(type u) { return make_float2(lo_bf(u), hi_bf(u)); }
+  __device__ __forceinline__ static type zero() { return 0u; }
+};
+template <> struct Raw<float> {
+  typedef float2 type;
+  __device__ __forceinline__ static type ld(const float* p) { return *reinterpret_cast<const float2*>(p); }
+  __device__ __forceinline__ static float2 f(type u) { return u; }
+  __device__ __forceinline__ static type zero() { return make_float2(0.f, 0.f); }
+};
 
-// Load TK keys x SV columns of V transposed into vt[col][key] (keys >= nvalid
-// are zero); when vz is given also store zeta_key * v with
-// zeta_key = gamma^(zeta_top - key) (the chunk-level zeta of the state update).
-template <typename T, typename OP, int SV>
-__device__ __forceinline__ void load_v_tile(OP* __restrict__ vt, OP* __restrict__ vz, const T* __restrict__ src,
-                                            int64_t rs, int nvalid, const Decay& dec, int zeta_top) {
-  constexpr int CP = SV / 2;           // column pairs
-  constexpr int KG = NT / CP;          // key groups of 8 per pass
-  constexpr int KP = TK + Pad<OP>::v;
-  const int tid = threadIdx.x;
-  const int cp = tid % CP;
-  const int kg = tid / CP;
-  for (int kk = 8 * kg; kk < TK; kk += 8 * KG) {
-    float a[8], b[8];
+// Staged global data of one job (a key tile, plus the query tile on the
+// diagonal), loaded into registers one job ahead of its use.
+template <typename T, int DK, int SV>
+struct Stage {
+  static constexpr int PAIRS = DK / 2;
+  static constexpr int RPP = NT / PAIRS;          // rows per pass of the Q/K loader
+  static constexpr int NPASS = TR / RPP;
+  static constexpr int VCP = SV / 2;              // V column pairs
+  static constexpr int VKG = NT / VCP;            // V key groups of 4
+  static constexpr int VPASS = (TK + 4 * VKG - 1) / (4 * VKG);
+  typename Raw<T>::type k[NPASS];
+  typename Raw<T>::type q[NPASS];
+  typename Raw<T>::type v[VPASS][4];
+
+  // issue the loads (rows >= nvalid read as zero).  Bases are uniform
+  // (scalar registers); per-lane offsets are 32-bit and clamped to the last
+  // valid row, so the loads are branch-free and in bounds.
+  __device__ __forceinline__ void load(const T* __restrict__ Qrow, int qs, const T* __restrict__ Krow, int ks,
+                                       const T* __restrict__ Vrow, int vs, int nvalid, bool with_q) {
+    const int tid = threadIdx.x;
+    const int j = tid % PAIRS, i0 = tid / PAIRS;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = kk + e;
-      float2 x = (key < nvalid) ? Elem<T>::ld2(src + (int64_t)key * rs + 2 * cp) : make_float2(0.f, 0.f);
-      a[e] = x.x;
-      b[e] = x.y;
-    }
-    st8(vt + (2 * cp) * KP + kk, a);
-    st8(vt + (2 * cp + 1) * KP + kk, b);
-    if (vz != nullptr) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float zt = dec.pow((float)(zeta_top - (kk + e)));
-        a[e] *= zt;
-        b[e] *= zt;
+    for (int p = 0; p < NPASS; ++p) {
+      const int i = i0 + p * RPP;
+      const int ic = min(i, nvalid - 1);
+      const uint32_t ko = (uint32_t)(ic * ks + 2 * j);
+      typename Raw<T>::type kv = Raw<T>::ld(Krow + ko);
+      k[p] = (i < nvalid) ? kv : Raw<T>::zero();
+      if (with_q) {
+        const uint32_t qo = (uint32_t)(ic * qs + 2 * j);
+        typename Raw<T>::type qv = Raw<T>::ld(Qrow + qo);
+        q[p] = (i < nvalid) ? qv : Raw<T>::zero();
       }
-      st8(vz + (2 * cp) * KP + kk, a);
-      st8(vz + (2 * cp + 1) * KP + kk, b);
+    }
+    const int cp = tid % VCP, kg = tid / VCP;
+#pragma unroll
+    for (int p = 0; p < VPASS; ++p) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 4 * (kg + p * VKG) + e;
+        const int kc = min(key, nvalid - 1);
+        typename Raw<T>::type vv = Raw<T>::ld(Vrow + (uint32_t)(kc * vs + 2 * cp));
+        v[p][e] = (key < nvalid) ? vv : Raw<T>::zero();
+      }
     }
   }
-}
-
-// A fragment of K'^T (rows = d, k = keys) gathered from the row-major key tile.
-template <typename OP, int DK>
-__device__ __forceinline__ typename Mfma<OP>::frag load_kT_frag(const OP* __restrict__ Ks, int key0, int d) {
-  constexpr int QP = DK + Pad<OP>::v;
-  const int h = (threadIdx.x & 32) ? 1 : 0;
-  typename Mfma<OP>::frag f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = Ks[(key0 + 8 * h + e) * QP + d];
-  return f;
-}
+};
 
 template <typename T, typename TO, int DK, int DV, int SV>
 __global__ void __launch_bounds__(NT, 1) chunkwise_kernel(KParams p, HeadParams hp) {
   typedef typename OpOf<T>::type OP;
   typedef Smem<OP, DK, SV> SM;
+  typedef Stage<T, DK, SV> ST;
   typedef Mfma<OP> M;
   constexpr int QP = SM::QP;
   constexpr int KP = SM::KP;
+  constexpr int CPITCH = SM::CP;
   constexpr int NDT = DK / 32;               // d tiles of the state
   constexpr int NCT = SV / 32;               // column tiles of the slice
   constexpr int NST = NDT * NCT;             // state tiles
-  constexpr int SPW = (NST + 3) / 4;         // state tiles per wave
-  constexpr int NOT = (TR / 32) * NCT;       // output tiles per query tile
+  constexpr int SPW = (NST + 7) / 8;         // state tiles per wave
+  constexpr int NOT = (TR / 32) * NCT;       // output tiles per query tile (<= 4)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int lh = lane >> 5;      // lane half
+  const bool score_wave = wave < 4;
+  const int w4 = wave & 3;
+  const int lh = lane >> 5;
   const int l32 = lane & 31;
 
   // workgroup -> (bh, slice); the slices of one head are kept on one XCD
-  // (consecutive workgroup ids are dealt round-robin over the 8 XCDs)
   const int nwg = gridDim.x;
   int wg = blockIdx.x;
   if ((nwg & 7) == 0) wg = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
@@ -184,6 +170,7 @@ __global__ void __launch_bounds__(NT, 1) chunkwise_kernel(KParams p, HeadParams 
   Decay dec;
   dec.init(hp.gamma[head]);
   const bool xpos = (p.flags & RET_XPOS) != 0;
+  const bool drow = (p.flags & RET_NORM_DROW) != 0;
   const float qk_scale = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
 
   const T* Qg = reinterpret_cast<const T*>(p.q) + bb * p.sq.b + head * p.sq.h;
@@ -191,11 +178,12 @@ __global__ void __launch_bounds__(NT, 1) chunkwise_kernel(KParams p, HeadParams 
   const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + s0;
   TO* Og = reinterpret_cast<TO*>(p.o) + bb * p.so.b + head * p.so.h + s0;
 
-  // ---- state slice R[d][s0 + col] in accumulators, key-sum z[d] per thread
+  // ---- state slice R[d][s0 + col] spread over all 8 waves (tile
+  //      wave + 8t), key-sum z[d] on thread tid - 256 of the state waves
   f32x16 R[SPW];
 #pragma unroll
   for (int t = 0; t < SPW; ++t) {
-    const int st = wave + 4 * t;
+    const int st = wave + 8 * t;
     const int dt = st / NCT, ct = st % NCT;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -207,205 +195,314 @@ __global__ void __launch_bounds__(NT, 1) chunkwise_kernel(KParams p, HeadParams 
       R[t][r] = val;
     }
   }
-  float zreg = 0.f;   // z[tid] for tid < DK
-  if (tid < DK && p.z_in) zreg = p.z_in[(int64_t)bh * DK + tid];
+  const int zd = tid - 256;             // d owned by this state-wave thread
+  float zreg = 0.f;
+  if (!score_wave && zd < DK && p.z_in) zreg = p.z_in[(int64_t)bh * DK + zd];
 
-  const int my_ot = wave;                          // output tile of this wave
-  const int ot_q = my_ot / NCT, ot_c = my_ot % NCT;
-  const int sq_k = wave >> 1, sq_q = wave & 1;     // S^T tile: key half, query half
-
+  // ---- flattened job list: per chunk, per query tile: the diagonal key
+  //      tile first (loaded together with the query tile), then the earlier
+  //      key tiles
   const int nchunks = (p.L + p.B - 1) / p.B;
-  for (int c = 0; c < nchunks; ++c) {
-    const int c0 = c * p.B;
-    const int Bc = min(p.B, p.L - c0);
-    const float gB = dec.pow((float)Bc);
+  auto rows_in = [&](int c) { return min(p.B, p.L - c * p.B); };
+  struct Job { int c, rt, kt; };
+  auto next_job = [&](Job j) -> Job {
+    const int nrt = (rows_in(j.c) + TR - 1) / TR;
+    // order within a row tile: kt = rt, 0, 1, ..., rt-1
+    int nk;
+    if (j.kt == j.rt) nk = (j.rt > 0) ? 0 : -1;
+    else nk = (j.kt + 1 < j.rt) ? j.kt + 1 : -1;
+    if (nk >= 0) return Job{j.c, j.rt, nk};
+    if (j.rt + 1 < nrt) return Job{j.c, j.rt + 1, j.rt + 1};
+    return Job{j.c + 1, 0, 0};
+  };
 
-    // ---- operand copy of R_{c-1} (transposed, scaled by 2^-e so that its
-    //      largest element lies in [2^14, 2^15)), z_{c-1}; then scale the
-    //      carried state by gamma^(B_c)
-    float amax = 0.f;
+  ST stg;
+  auto issue = [&](Job j) {
+    if (j.c >= nchunks) return;
+    const int c0 = j.c * p.B, Bc = rows_in(j.c);
+    const int k0 = j.kt * TK;
+    const int nvalid = min(TK, Bc - k0);
+    const bool diag = (j.kt == j.rt);
+    stg.load(Qg + (int64_t)(c0 + k0) * p.sq.l, (int)p.sq.l, Kg + (int64_t)(c0 + k0) * p.sk.l, (int)p.sk.l,
+             Vg + (int64_t)(c0 + k0) * p.sv.l, (int)p.sv.l, nvalid, diag);
+  };
+
+  const int ot_q = w4 / NCT, ot_c = w4 % NCT;      // output / cross tile of wave w4
+  const int sq_k = w4 >> 1, sq_q = w4 & 1;         // S^T tile of score wave w4
+
+  Job job{0, 0, 0};
+  issue(job);
+  f32x16 O = {};
+  float den = 0.f;
+  int cur_chunk = -1;
+  float rup = 1.f;
+
+  while (job.c < nchunks) {
+    const int c0 = job.c * p.B;
+    const int Bc = rows_in(job.c);
+    const int r0 = job.rt * TR;
+    const int k0 = job.kt * TK;
+    const int qvalid = min(TR, Bc - r0);
+    const int kvalid = min(TK, Bc - k0);
+    const bool diag = (job.kt == job.rt);
+
+    __syncthreads();   // previous job done with the LDS tiles
+    if (job.c != cur_chunk) {
+      // ---- chunk start: operand copy of R_{c-1} (transposed, scaled by
+      //      2^-e so its largest element lies in [2^14, 2^15)) and z_{c-1};
+      //      then scale the carried state by gamma^(B_c)
+      cur_chunk = job.c;
+      float amax = 0.f;
 #pragma unroll
-    for (int t = 0; t < SPW; ++t)
-      if (wave + 4 * t < NST)
+      for (int t = 0; t < SPW; ++t)
+        if (wave + 8 * t < NST)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(R[t][r]));
+          for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(R[t][r]));
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    __syncthreads();
-    if (lane == 0) sm.wmax[wave] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(sm.wmax[0], sm.wmax[1]), fmaxf(sm.wmax[2], sm.wmax[3]));
-    int rexp = 0;
-    if (amax > 0.f && amax < 3.0e38f) {
-      int ex;
-      frexpf(amax, &ex);          // amax in [2^(ex-1), 2^ex)
-      rexp = ex - 15;
-    }
-    const float rdown = ldexpf(1.f, -rexp), rup = ldexpf(1.f, rexp);
+      for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      if (lane == 0) sm.wmax[wave] = amax;
+      __syncthreads();
+      amax = 0.f;
 #pragma unroll
-    for (int t = 0; t < SPW; ++t) {
-      const int st = wave + 4 * t;
-      if (st < NST) {
-        const int dt = st / NCT, ct = st % NCT;
+      for (int w = 0; w < NT / 64; ++w) amax = fmaxf(amax, sm.wmax[w]);
+      int rexp = 0;
+      if (amax > 0.f && amax < 3.0e38f) {
+        int ex;
+        frexpf(amax, &ex);
+        rexp = min(max(ex - 15, -100), 100);
+      }
+      const float rdown = ldexpf(1.f, -rexp);
+      rup = ldexpf(1.f, rexp);
+      const float gB = dec.pow((float)Bc);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int d = dt * 32 + acc_row(r, lane);
-          sm.Rt[(ct * 32 + l32) * QP + d] = to_op<OP>(R[t][r] * rdown);
-          R[t][r] *= gB;
+      for (int t = 0; t < SPW; ++t) {
+        const int st = wave + 8 * t;
+        if (st < NST) {
+          const int dt = st / NCT, ct = st % NCT;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int d = dt * 32 + acc_row(r, lane);
+            sm.Rt[(ct * 32 + l32) * QP + d] = to_op<OP>(R[t][r] * rdown);
+            R[t][r] *= gB;
+          }
         }
       }
-    }
-    if (tid < DK) {
-      sm.zs[tid] = zreg;
-      zreg *= gB;
-    }
-
-    const int nrt = (Bc + TR - 1) / TR;
-    for (int rt = 0; rt < nrt; ++rt) {
-      const int r0 = rt * TR;
-      const int qvalid = min(TR, Bc - r0);
-      __syncthreads();
-      load_rot_tile<T, OP, DK>(sm.Qs, Qg + (int64_t)(c0 + r0) * p.sq.l, p.sq.l, qvalid, p.pos0 + c0 + r0, xpos,
-                               hp.theta);
-      if (tid < TR) {
-        sm.dens[tid] = 0.f;
-        float s = qk_scale;
-        if (p.flags & RET_NORM_DROW) s *= dec.drow((float)(p.n_prev + c0 + r0 + tid + 1));
-        sm.rscale[tid] = s;
+      if (!score_wave && zd < DK) {
+        sm.zs[zd] = zreg;
+        zreg *= gB;
       }
-      // row scale of this lane's S^T query column
-      float s_q = qk_scale;
-      if (p.flags & RET_NORM_DROW) s_q *= dec.drow((float)(p.n_prev + c0 + r0 + sq_q * 32 + l32 + 1));
+    }
 
-      f32x16 O = {};
-      float den = 0.f;
+    // ---- staged registers -> LDS (rotation of Q/K, transposition of V)
+    {
+      constexpr int PAIRS = ST::PAIRS, RPP = ST::RPP, NPASS = ST::NPASS;
+      const int j = tid % PAIRS, i0 = tid / PAIRS;
+      float c = 1.f, s = 0.f, c1 = 1.f, s1 = 0.f;
+      if (xpos) {
+        phase(p.pos0 + c0 + k0 + i0, hp.theta[j], c, s);
+        phase(RPP, hp.theta[j], c1, s1);
+      }
+#pragma unroll
+      for (int pp = 0; pp < NPASS; ++pp) {
+        const int i = i0 + pp * RPP;
+        float2 kk = Raw<T>::f(stg.k[pp]);
+        float2 qq = Raw<T>::f(stg.q[pp]);
+        if (xpos) {
+          rot(kk.x, kk.y, c, s);
+          if (diag) rot(qq.x, qq.y, c, s);
+          advance(c, s, c1, s1);
+        }
+        st2(sm.Ks + i * QP + 2 * j, kk.x, kk.y);
+        if (diag) st2(sm.Qs + i * QP + 2 * j, qq.x, qq.y);
+      }
+      constexpr int VCP = ST::VCP, VKG = ST::VKG, VPASS = ST::VPASS;
+      const int cp = tid % VCP, kg = tid / VCP;
+#pragma unroll
+      for (int pp = 0; pp < VPASS; ++pp) {
+        const int key0 = 4 * (kg + pp * VKG);
+        if (key0 < TK) {
+          float a[4], b[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float2 x = Raw<T>::f(stg.v[pp][e]);
+            a[e] = x.x;
+            b[e] = x.y;
+          }
+          st4(sm.Vt + (2 * cp) * KP + key0, a);
+          st4(sm.Vt + (2 * cp + 1) * KP + key0, b);
+          if (diag) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float zt = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key0 - e) * dec.lg2);
+              a[e] *= zt;
+              b[e] *= zt;
+            }
+            st4(sm.Vz + (2 * cp) * KP + key0, a);
+            st4(sm.Vz + (2 * cp + 1) * KP + key0, b);
+          }
+        }
+      }
+      if (diag && tid < TK) sm.zeta[tid] = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - tid) * dec.lg2);
+      if (diag && tid < TR) {
+        // row tables of the query tile: s_i, s_i xi_i 2^e, and den = 0
+        float sc = qk_scale;
+        if (drow) sc *= dec.drow((float)(p.n_prev + c0 + r0 + tid + 1));
+        sm.rs[tid] = sc;
+        sm.xs[tid] = sc * dec.pow((float)(r0 + tid + 1));
+        sm.dens[tid] = 0.f;
+      }
+    }
+    __syncthreads();
+    // ---- prefetch the next job while this one computes
+    const Job nj = next_job(job);
+    issue(nj);
 
-      for (int kt = 0; kt <= rt; ++kt) {
-        const int k0 = kt * TK;
-        const int kvalid = min(TK, Bc - k0);
-        const bool diag = (kt == rt);
-        if (kt > 0) __syncthreads();
-        load_rot_tile<T, OP, DK>(sm.Ks, Kg + (int64_t)(c0 + k0) * p.sk.l, p.sk.l, kvalid, p.pos0 + c0 + k0, xpos,
-                                 hp.theta);
-        load_v_tile<T, OP, SV>(sm.Vt, diag ? sm.Vz : nullptr, Vg + (int64_t)(c0 + k0) * p.sv.l, p.sv.l, kvalid,
-                               dec, Bc - 1 - k0);
-        __syncthreads();
-
-        // S^T tile (32 keys x 32 queries) of this wave
+    if (score_wave) {
+      if (diag) {
+        O = f32x16{};
+        den = 0.f;
+      }
+      // S^T tile (32 keys x 32 queries); on the diagonal tile the block of
+      // keys 32..63 against queries 0..31 is entirely masked
+      const bool skip = diag && sq_k > sq_q;
+      const int qi = r0 + sq_q * 32 + l32;          // chunk-local query of this lane
+      if (!skip) {
         f32x16 S = {};
-#pragma unroll 4
+#pragma unroll 2
         for (int kb = 0; kb < DK; kb += 16) {
           auto a = M::load(sm.Ks + (sq_k * 32 + l32) * QP + kb + 8 * lh);
           auto b = M::load(sm.Qs + (sq_q * 32 + l32) * QP + kb + 8 * lh);
           M::mma(S, a, b);
         }
-        // decay mask and row scale, fp32 row sums, P -> LDS
-        {
-          const int qi = r0 + sq_q * 32 + l32;   // chunk-local query
+        const float s_q = sm.rs[sq_q * 32 + l32];
+        const float base = (float)(qi - k0 - sq_k * 32 - 4 * lh);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float pv[4];
+        for (int i = 0; i < 4; ++i) {
+          float pv[4];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int r = 4 * i + jj;
-              const int ki = k0 + sq_k * 32 + acc_row(r, lane);
-              float val = 0.f;
-              if (ki <= qi) val = S[r] * (s_q * dec.pow((float)(qi - ki)));
-              den += val;
-              pv[jj] = val;
-            }
-            st4(sm.Ps + (sq_q * 32 + l32) * KP + sq_k * 32 + 8 * i + 4 * lh, pv);
+          for (int jj = 0; jj < 4; ++jj) {
+            const int r = 4 * i + jj;
+            const float dist = base - (float)(8 * i + jj);     // qi - ki
+            float val = 0.f;
+            if (dist >= 0.f) val = S[r] * s_q * __builtin_amdgcn_exp2f(dist * dec.lg2);
+            den += val;
+            pv[jj] = val;
+          }
+          st4(sm.Ps + (sq_q * 32 + l32) * KP + sq_k * 32 + 8 * i + 4 * lh, pv);
+        }
+      } else {
+        float zero4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st4(sm.Ps + (sq_q * 32 + l32) * KP + sq_k * 32 + 8 * i + 4 * lh, zero4);
+      }
+    } else {
+      if (diag) {
+        if (zd < DK) {
+          float zacc = 0.f;
+          for (int key = 0; key < kvalid; ++key) zacc += sm.zeta[key] * from_op<OP>(sm.Ks[key * QP + zd]);
+          zreg += zacc;
+        }
+        // cross-chunk term of this query tile: Oc = Q' (2^-e R_{c-1}), and
+        // Q' . z_{c-1}; the row factors s xi (and 2^e for Oc) are applied here
+        if (w4 < NOT) {
+          f32x16 Oc = {};
+#pragma unroll 2
+          for (int kb = 0; kb < DK; kb += 16) {
+            auto a = M::load(sm.Qs + (ot_q * 32 + l32) * QP + kb + 8 * lh);
+            auto b = M::load(sm.Rt + (ot_c * 32 + l32) * QP + kb + 8 * lh);
+            M::mma(Oc, a, b);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qrow = ot_q * 32 + acc_row(r, lane);
+            sm.Oc[qrow * CPITCH + ot_c * 32 + l32] = Oc[r] * (sm.xs[qrow] * rup);
           }
         }
-        __syncthreads();
-        // O += P V[:, slice]
-        if (my_ot < NOT) {
+        {
+          // 4 threads per query row for Q' . z_{c-1}
+          const int i = (tid - 256) >> 2, part = tid & 3;
+          float acc = 0.f;
+          for (int d = part; d < DK; d += 4) acc += from_op<OP>(sm.Qs[i * QP + d]) * sm.zs[d];
+          acc += __shfl_xor(acc, 1, 64);
+          acc += __shfl_xor(acc, 2, 64);
+          if (part == 0) atomicAdd(&sm.dens[i], acc * sm.xs[i]);
+        }
+      }
+    }
+    if (diag) {
+      // state update from the diagonal key tile: R += K'^T (zeta V), all waves
+#pragma unroll
+      for (int t = 0; t < SPW; ++t) {
+        const int st = wave + 8 * t;
+        if (st < NST) {
+          const int dt = st / NCT, ct = st % NCT;
 #pragma unroll
           for (int kb = 0; kb < TK; kb += 16) {
-            auto a = M::load(sm.Ps + (ot_q * 32 + l32) * KP + kb + 8 * lh);
-            auto b = M::load(sm.Vt + (ot_c * 32 + l32) * KP + kb + 8 * lh);
-            M::mma(O, a, b);
-          }
-        }
-        // state update from the diagonal key tile: R += K'^T (zeta V)
-        if (diag) {
+            typename M::frag a;
 #pragma unroll
-          for (int t = 0; t < SPW; ++t) {
-            const int st = wave + 4 * t;
-            if (st < NST) {
-              const int dt = st / NCT, ct = st % NCT;
-#pragma unroll
-              for (int kb = 0; kb < TK; kb += 16) {
-                auto a = load_kT_frag<OP, DK>(sm.Ks, kb, dt * 32 + l32);
-                auto b = M::load(sm.Vz + (ct * 32 + l32) * KP + kb + 8 * lh);
-                M::mma(R[t], a, b);
-              }
-            }
-          }
-          if (tid < DK) {
-            float zacc = 0.f;
-            for (int key = 0; key < kvalid; ++key)
-              zacc += dec.pow((float)(Bc - 1 - k0 - key)) * from_op<OP>(sm.Ks[key * QP + tid]);
-            zreg += zacc;
-          }
-        }
-      }
-
-      // score row sums of this query tile: lanes l and l^32 share a query,
-      // waves (0,q) and (1,q) cover the two key halves
-      den += __shfl_xor(den, 32, 64);
-      if (lh == 0) atomicAdd(&sm.dens[sq_q * 32 + l32], den);
-
-      // cross-chunk term: scale query rows by s xi (xi = gamma^(i+1)), then
-      // Oc = (s xi Q') (2^-e R_{c-1}),  den += s xi (Q' . z_{c-1})
-      __syncthreads();
-      for (int e = tid; e < TR * DK; e += NT) {
-        const int i = e / DK, d = e % DK;
-        const float f = sm.rscale[i] * dec.pow((float)(r0 + i + 1));
-        sm.Qs[i * QP + d] = to_op<OP>(from_op<OP>(sm.Qs[i * QP + d]) * f);
-      }
-      __syncthreads();
-      {
-        // 4 threads per query row for Q' . z
-        const int i = tid >> 2, part = tid & 3;
-        float acc = 0.f;
-        for (int d = part; d < DK; d += 4) acc += from_op<OP>(sm.Qs[i * QP + d]) * sm.zs[d];
-        acc += __shfl_xor(acc, 1, 64);
-        acc += __shfl_xor(acc, 2, 64);
-        if (part == 0) atomicAdd(&sm.dens[i], acc);
-      }
-      f32x16 Oc = {};
-      if (my_ot < NOT) {
-#pragma unroll 4
-        for (int kb = 0; kb < DK; kb += 16) {
-          auto a = M::load(sm.Qs + (ot_q * 32 + l32) * QP + kb + 8 * lh);
-          auto b = M::load(sm.Rt + (ot_c * 32 + l32) * QP + kb + 8 * lh);
-          M::mma(Oc, a, b);
-        }
-      }
-      __syncthreads();
-      // normalise and store
-      if (my_ot < NOT) {
-        const int col = ot_c * 32 + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = ot_q * 32 + acc_row(r, lane);
-          if (qi < qvalid) {
-            const int64_t t_abs = c0 + r0 + qi;
-            float val = O[r] + Oc[r] * rup;
-            if (p.flags & RET_NORM_SCORE) val = val / fmaxf(fabsf(sm.dens[qi]), 1.f);
-            Og[t_abs * p.so.l + col] = Store<TO>::cvt(val);
+            for (int e = 0; e < 8; ++e) a[e] = sm.Ks[(kb + 8 * lh + e) * QP + dt * 32 + l32];
+            auto b = M::load(sm.Vz + (ct * 32 + l32) * KP + kb + 8 * lh);
+            M::mma(R[t], a, b);
           }
         }
       }
     }
+    __syncthreads();
+    // O += P V[:, slice] (on the diagonal tile, queries 0..31 only see keys 0..31)
+    if (score_wave && w4 < NOT) {
+      const int kend = (diag && ot_q == 0) ? 32 : TK;
+      for (int kb = 0; kb < kend; kb += 16) {
+        auto a = M::load(sm.Ps + (ot_q * 32 + l32) * KP + kb + 8 * lh);
+        auto b = M::load(sm.Vt + (ot_c * 32 + l32) * KP + kb + 8 * lh);
+        M::mma(O, a, b);
+      }
+    }
+
+    // ---- end of a query tile: combine, normalise, store
+    const bool last_of_rt = !(nj.c == job.c && nj.rt == job.rt);
+    if (last_of_rt) {
+      if (score_wave) {
+        den += __shfl_xor(den, 32, 64);
+        if (lh == 0) atomicAdd(&sm.dens[sq_q * 32 + l32], den);
+      }
+      __syncthreads();
+      if (score_wave && w4 < NOT) {
+        const int col = ot_c * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = ot_q * 32 + acc_row(r, lane);
+          float val = O[r] + sm.Oc[qrow * CPITCH + col];
+          if (p.flags & RET_NORM_SCORE) val = val / fmaxf(fabsf(sm.dens[qrow]), 1.f);
+          sm.Oc[qrow * CPITCH + col] = val;
+        }
+      }
+      __syncthreads();
+      // coalesced store: each thread writes 4 consecutive columns of a row
+      constexpr int C4 = SV / 4;
+      for (int e = tid; e < TR * C4; e += NT) {
+        const int row = e / C4, c4 = e % C4;
+        if (row < qvalid) {
+          const float* src = sm.Oc + row * CPITCH + 4 * c4;
+          TO* dst = Og + (int64_t)(c0 + r0 + row) * p.so.l + 4 * c4;
+          if constexpr (sizeof(TO) == 2) {
+            uint2 u;
+            u.x = pack_bf2(src[0], src[1]);
+            u.y = pack_bf2(src[2], src[3]);
+            *reinterpret_cast<uint2*>(dst) = u;
+          } else {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{src[0], src[1], src[2], src[3]};
+          }
+        }
+      }
+    }
+    job = nj;
   }
 
   // ---- final state
   if (p.state_out) {
 #pragma unroll
     for (int t = 0; t < SPW; ++t) {
-      const int st = wave + 4 * t;
+      const int st = wave + 8 * t;
       if (st < NST) {
         const int dt = st / NCT, ct = st % NCT;
 #pragma unroll
@@ -416,9 +513,8 @@ __global__ void __launch_bounds__(NT, 1) chunkwise_kernel(KParams p, HeadParams 
       }
     }
   }
-  if (p.z_out && slice == 0 && tid < DK) p.z_out[(int64_t)bh * DK + tid] = zreg;
+  if (p.z_out && slice == 0 && !score_wave && zd < DK) p.z_out[(int64_t)bh * DK + zd] = zreg;
 }
-
 template <typename T, typename TO, int DK, int DV, int SV>
 static hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
   static_assert(DK / 2 <= NT, "pairs per row exceed the workgroup");
