@@ -49,7 +49,7 @@ typedef enum {
   RET_E_HIP = 5           /* a HIP launch failed; the message names the HIP error */
 } ret_status;
 
-typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype;
+typedef enum { RET_F32 = 0, RET_BF16 = 1, RET_F16 = 2 } ret_dtype;
 
 /* Flag bits selecting the steps of [notes] §2.3 and §三.3. */
 enum {
@@ -93,9 +93,15 @@ typedef struct { int64_t b, h, l; } ret_strides;   /* element strides of a [b,h,
  *   workspace  device scratch of retention_chunkwise_workspace_bytes() bytes
  *          (may be NULL when that size is 0)
  * Supported: in_dt bf16 with (d_k, d_v) in {(32,32), (64,64), (128,128),
- * (128,256), (256,256), (256,512)}; in_dt f32 with (d_k, d_v) in {(32,32),
- * (64,64)}; out_dt f32 or bf16; q/k/v/o 16-byte aligned with strides that
- * keep every row 16-byte aligned; L >= 1, b*h >= 1, h <= 64.
+ * (128,256), (256,256), (256,512)}; in_dt f16 with (d_k, d_v) in
+ * {(128,256), (256,512)}; in_dt f32 with (d_k, d_v) in {(32,32), (64,64)};
+ * out_dt f32, bf16 or f16; q/k/v/o 16-byte aligned with strides that keep
+ * every row 16-byte aligned; L >= 1, b*h >= 1, h <= 64.
+ * Numerics: f32 inputs are contracted in fp32 MFMA.  bf16 and f16 inputs are
+ * contracted with fp16 MFMA operands and fp32 accumulation; the operands
+ * require |q|, |k| < 2^15, |v| < 2^16 and normalised scores
+ * s_t |q'_t . k'_m| < 2^16 (the state copy used as an operand is rescaled by
+ * a power of two per chunk, so the state itself has no such limit).
  */
 int retention_chunkwise_fwd(const void* q, ret_strides sq, const void* k, ret_strides sk,
                             const void* v, ret_strides sv, void* o, ret_strides so,
@@ -140,7 +146,7 @@ int retention_recurrent_step(const void* q, const void* k, const void* v, float*
  * and biased variance (eps added to the variance), then applies the optional
  * per-channel affine; swish(x) = x / (1 + e^{-x}).
  *
- *   y    [b,h,L,d_v] head outputs of y_dt, strides sy
+ *   y    [b,h,L,d_v] head outputs of y_dt (f32, bf16 or f16), strides sy
  *   g    [b,L,h*d_v] gate pre-activation X W_G of g_dt (contiguous)
  *   out  [b,L,h*d_v] of out_dt (contiguous)
  *   gn_weight, gn_bias  device float32 [h*d_v] or NULL (= 1 and 0)
@@ -150,6 +156,21 @@ int msr_gate_norm(const void* y, ret_strides sy, const void* g, void* out,
                   int b, int L, int h, int d_v,
                   const float* gn_weight, const float* gn_bias, float eps,
                   ret_dtype y_dt, ret_dtype g_dt, ret_dtype out_dt, hipStream_t stream);
+
+/*
+ * msr_gemm -- the projections of the gated MSR block ([notes] §三.2 and
+ * §2.1: Q = X W_Q, K = X W_K, V = X W_V, G = X W_G, Out = Z W_O):
+ *   C[M][N] = A[M][K] . B[N][K]^T, fp32 accumulation
+ *   A  device [M][K] row-major activations of a_dt (bf16 or f16)
+ *   B  device bf16 [N][K] row-major: the weight as [out_features][in_features],
+ *      i.e. the transpose of the X W layout
+ *   C  device [M][N] row-major of c_dt (f32, bf16 or f16); must not overlap A, B
+ * bf16 A is contracted with B on bf16 MFMA as given; f16 A is contracted on
+ * fp16 MFMA with B converted to fp16 (exact for |w| < 2^16).
+ * Supported: K a multiple of 32; 16-byte aligned pointers.
+ */
+int msr_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+             hipStream_t stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* retention_last_error(void);

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libretention.so")
 
 XPOS, SCALE_QK, NORM_DROW, NORM_SCORE = 1, 2, 4, 8
 NORM_ALL = SCALE_QK | NORM_DROW | NORM_SCORE
-RET_F32, RET_BF16 = 0, 1
+RET_F32, RET_BF16, RET_F16 = 0, 1, 2
 STATUS = {0: "RET_OK", 1: "RET_E_INVAL", 2: "RET_E_UNSUPPORTED", 3: "RET_E_ALIGN",
           4: "RET_E_WORKSPACE", 5: "RET_E_HIP"}
 
@@ -47,6 +47,8 @@ def load_library(path=LIB_PATH):
     lib.msr_gate_norm.argtypes = [vp, Strides, vp, vp, i32, i32, i32, i32, vp, vp, f32,
                                   i32, i32, i32, vp]
     lib.msr_gate_norm.restype = i32
+    lib.msr_gemm.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp]
+    lib.msr_gemm.restype = i32
     lib.retention_last_error.argtypes = []
     lib.retention_last_error.restype = ctypes.c_char_p
     lib.retention_abi_version.argtypes = []
@@ -68,11 +70,13 @@ def _dt(t):
         return RET_BF16
     if t.dtype == torch.float32:
         return RET_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float16:
+        return RET_F16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)")
 
 
 def _torch_dt(code):
-    return torch.bfloat16 if code == RET_BF16 else torch.float32
+    return {RET_BF16: torch.bfloat16, RET_F16: torch.float16}.get(code, torch.float32)
 
 
 def _ptr(t):
@@ -165,3 +169,53 @@ def gate_norm(y, g, eps, weight=None, bias=None, out=None, out_dtype=None, strea
                            _ptr(weight), _ptr(bias), float(eps), _dt(y), _dt(g), _dt(out), _stream(stream))
     _check(st, "msr_gate_norm")
     return out
+
+
+def gemm(a, b_nk, out=None, out_dtype=torch.bfloat16, stream=None):
+    """C = a . b_nk^T for a [M, K] (bf16 or fp16) and a bf16 weight b_nk [N, K]."""
+    if a.dtype not in (torch.bfloat16, torch.float16) or b_nk.dtype != torch.bfloat16:
+        raise TypeError("gemm takes a bf16 or fp16 A and a bf16 weight")
+    if not a.is_contiguous() or not b_nk.is_contiguous():
+        raise ValueError("gemm needs contiguous operands")
+    M, K = a.shape
+    N = b_nk.shape[0]
+    if b_nk.shape[1] != K:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    st = LIB.msr_gemm(_ptr(a), _dt(a), _ptr(b_nk), _ptr(out), _dt(out), M, N, K, _stream(stream))
+    _check(st, "msr_gemm")
+    return out
+
+
+def msr_block_fwd(x, wq_t, wk_t, wv_t, wg_t, wo_t, gamma, theta, chunk, flags, eps, out_dtype=torch.bfloat16,
+                  stream=None):
+    """Gated multi-scale retention block forward (RetNet reading notes, §三.2):
+    MSR(X) = (swish(X W_G) (.) GroupNorm_h(Retention heads)) W_O.
+
+    x: [b, L, d_model] bf16; w*_t: weights as [out_features, in_features] bf16;
+    gamma: the h per-head decays (host float64).
+    Every step runs in the library's kernels: four projections, the
+    chunkwise retention over [b, h, L, d] views of the projections, the
+    GroupNorm + swish gate, and the output projection.  Intermediates (the
+    projections, the head outputs and the gated heads) are stored as fp16.
+    """
+    b, L, dm = x.shape
+    h = len(gamma)
+    x2 = x.reshape(b * L, dm)
+    dk = wq_t.shape[0] // h
+    dv = wv_t.shape[0] // h
+    f16 = torch.float16
+    Q = gemm(x2, wq_t, out_dtype=f16, stream=stream)
+    K = gemm(x2, wk_t, out_dtype=f16, stream=stream)
+    V = gemm(x2, wv_t, out_dtype=f16, stream=stream)
+    G = gemm(x2, wg_t, out_dtype=f16, stream=stream)
+    qv = Q.view(b, L, h, dk).transpose(1, 2)
+    kv = K.view(b, L, h, dk).transpose(1, 2)
+    vv = V.view(b, L, h, dv).transpose(1, 2)
+    Y = torch.empty((b, L, h * dv), dtype=f16, device=x.device)
+    yv = Y.view(b, L, h, dv).transpose(1, 2)
+    chunkwise_fwd(qv, kv, vv, gamma, theta, chunk, flags, out=yv, stream=stream)
+    Z = gate_norm(yv, G.view(b, L, h * dv), eps, stream=stream)
+    out = gemm(Z.view(b * L, h * dv), wo_t, out_dtype=out_dtype, stream=stream)
+    return out.view(b, L, -1)

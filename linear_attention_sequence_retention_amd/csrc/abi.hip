@@ -26,8 +26,8 @@ int ok() {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
-bool valid_dt(ret_dtype d) { return d == RET_F32 || d == RET_BF16; }
-size_t dt_size(ret_dtype d) { return d == RET_BF16 ? 2 : 4; }
+bool valid_dt(ret_dtype d) { return d == RET_F32 || d == RET_BF16 || d == RET_F16; }
+size_t dt_size(ret_dtype d) { return d == RET_F32 ? 4 : 2; }
 
 int check_gamma(const double* gamma, int h) {
   if (!gamma) return fail(RET_E_INVAL, "gamma is NULL");
@@ -116,7 +116,7 @@ int retention_chunkwise_fwd(const void* q, ret_strides sq, const void* k, ret_st
     return fail(RET_E_INVAL, "a continued sequence with RET_NORM_SCORE needs z_in");
   if (!ret::chunkwise_supported(in_dt, d_k, d_v))
     return fail(RET_E_UNSUPPORTED, "no chunkwise kernel for in_dt=%s d_k=%d d_v=%d",
-                in_dt == RET_BF16 ? "bf16" : "f32", d_k, d_v);
+                in_dt == RET_BF16 ? "bf16" : (in_dt == RET_F16 ? "f16" : "f32"), d_k, d_v);
   const size_t need = ret::chunkwise_workspace(b, h, L, d_k, d_v, chunk_B, flags);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(RET_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : 0);
@@ -186,6 +186,18 @@ int msr_gate_norm(const void* y, ret_strides sy, const void* g, void* out,
   a.y = y; a.sy = sy; a.g = g; a.out = out; a.b = b; a.L = L; a.h = h; a.dv = d_v;
   a.w = gn_weight; a.bias = gn_bias; a.eps = eps; a.y_dt = y_dt; a.g_dt = g_dt; a.out_dt = out_dt;
   return hip_status(ret::launch_gate_norm(a, stream), "msr_gate_norm launch");
+}
+
+int msr_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+             hipStream_t stream) {
+  if (M <= 0 || N <= 0 || K <= 0) return fail(RET_E_INVAL, "sizes must be positive (M=%d N=%d K=%d)", M, N, K);
+  if (K % 32) return fail(RET_E_UNSUPPORTED, "K must be a multiple of 32 (got %d)", K);
+  if (!valid_dt(c_dt) || !valid_dt(a_dt)) return fail(RET_E_INVAL, "unknown dtype");
+  if (a_dt == RET_F32) return fail(RET_E_UNSUPPORTED, "A must be bf16 or f16");
+  if (!A || !B || !C) return fail(RET_E_INVAL, "A, B and C must be non-NULL");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16)) return fail(RET_E_ALIGN, "A, B and C must be 16-byte aligned");
+  if (C == A || C == B) return fail(RET_E_INVAL, "C must not alias A or B");
+  return hip_status(ret::launch_gemm(A, a_dt, B, C, c_dt, M, N, K, stream), "msr_gemm launch");
 }
 
 }  // extern "C"

@@ -77,6 +77,15 @@ template <> struct Raw<bf16> {
   __device__ __forceinline__ static float2 f(type u) { return make_float2(lo_bf(u), hi_bf(u)); }
   __device__ __forceinline__ static type zero() { return 0u; }
 };
+template <> struct Raw<half> {
+  typedef uint32_t type;
+  __device__ __forceinline__ static type ld(const half* p) { return *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ static float2 f(type u) {
+    f16x2 v = __builtin_bit_cast(f16x2, u);
+    return make_float2((float)v.x, (float)v.y);
+  }
+  __device__ __forceinline__ static type zero() { return 0u; }
+};
 template <> struct Raw<float> {
   typedef float2 type;
   __device__ __forceinline__ static type ld(const float* p) { return *reinterpret_cast<const float2*>(p); }
@@ -483,15 +492,7 @@ __global__ void __launch_bounds__(NT, 1) chunkwise_kernel(KParams p, HeadParams 
         const int row = e / C4, c4 = e % C4;
         if (row < qvalid) {
           const float* src = sm.Oc + row * CPITCH + 4 * c4;
-          TO* dst = Og + (int64_t)(c0 + r0 + row) * p.so.l + 4 * c4;
-          if constexpr (sizeof(TO) == 2) {
-            uint2 u;
-            u.x = pack_bf2(src[0], src[1]);
-            u.y = pack_bf2(src[2], src[3]);
-            *reinterpret_cast<uint2*>(dst) = u;
-          } else {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{src[0], src[1], src[2], src[3]};
-          }
+          store4(Og + (int64_t)(c0 + r0 + row) * p.so.l + 4 * c4, src);
         }
       }
     }
@@ -536,8 +537,15 @@ static hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
 
 template <typename T, int DK, int DV, int SV>
 static hipError_t launch_o(const ChunkArgs& a, hipStream_t st) {
-  return a.out_dt == RET_BF16 ? launch_t<T, bf16, DK, DV, SV>(a, st) : launch_t<T, float, DK, DV, SV>(a, st);
+  if (a.out_dt == RET_BF16) return launch_t<T, bf16, DK, DV, SV>(a, st);
+  if (a.out_dt == RET_F16) return launch_t<T, half, DK, DV, SV>(a, st);
+  return launch_t<T, float, DK, DV, SV>(a, st);
 }
+
+template <typename T> constexpr ret_dtype dt_of();
+template <> constexpr ret_dtype dt_of<bf16>() { return RET_BF16; }
+template <> constexpr ret_dtype dt_of<half>() { return RET_F16; }
+template <> constexpr ret_dtype dt_of<float>() { return RET_F32; }
 
 #define RET_SHAPES(X)                       \
   X(bf16, 32, 32, 32)                       \
@@ -546,12 +554,14 @@ static hipError_t launch_o(const ChunkArgs& a, hipStream_t st) {
   X(bf16, 128, 256, 64)                     \
   X(bf16, 256, 256, 64)                     \
   X(bf16, 256, 512, 64)                     \
+  X(half, 128, 256, 64)                     \
+  X(half, 256, 512, 64)                     \
   X(float, 32, 32, 32)                      \
   X(float, 64, 64, 64)
 
 bool chunkwise_supported(ret_dtype in_dt, int dk, int dv) {
 #define X(T, DK, DV, SV) \
-  if ((in_dt == RET_BF16) == (sizeof(T) == 2) && dk == DK && dv == DV) return true;
+  if (in_dt == dt_of<T>() && dk == DK && dv == DV) return true;
   RET_SHAPES(X)
 #undef X
   return false;
@@ -562,7 +572,7 @@ size_t chunkwise_workspace(int, int, int, int, int, int, unsigned) { return 0; }
 hipError_t launch_chunkwise(const ChunkArgs& a, hipStream_t st, bool* supported) {
   *supported = true;
 #define X(T, DK, DV, SV) \
-  if ((a.in_dt == RET_BF16) == (sizeof(T) == 2) && a.dk == DK && a.dv == DV) return launch_o<T, DK, DV, SV>(a, st);
+  if (a.in_dt == dt_of<T>() && a.dk == DK && a.dv == DV) return launch_o<T, DK, DV, SV>(a, st);
   RET_SHAPES(X)
 #undef X
   *supported = false;

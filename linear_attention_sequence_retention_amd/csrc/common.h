@@ -57,6 +57,14 @@ template <> struct Elem<bf16> {
     return make_float2(lo_bf(u), hi_bf(u));
   }
 };
+template <> struct Elem<_Float16> {
+  __device__ __forceinline__ static float ld(const _Float16* p) { return (float)*p; }
+  __device__ __forceinline__ static float2 ld2(const _Float16* p) {
+    typedef __attribute__((ext_vector_type(2))) _Float16 h2;
+    h2 v = *reinterpret_cast<const h2*>(p);
+    return make_float2((float)v.x, (float)v.y);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Per-head scalars.  All of them come from gamma in float64 and are rounded to
@@ -162,6 +170,7 @@ template <> struct Mfma<float> {
 // fp16 range converts exactly.
 template <typename T> struct OpOf { typedef float type; };
 template <> struct OpOf<bf16> { typedef half type; };
+template <> struct OpOf<half> { typedef half type; };
 
 // conversions between the compute float and the LDS operand type (RNE)
 template <typename T> __device__ __forceinline__ T to_op(float x);

@@ -23,6 +23,19 @@ template <> struct Vec8<bf16> {
     *reinterpret_cast<uint4*>(p) = u;
   }
 };
+template <> struct Vec8<half> {
+  __device__ __forceinline__ static void ld(const half* p, float* x) {
+    f16x8 v = *reinterpret_cast<const f16x8*>(p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (float)v[j];
+  }
+  __device__ __forceinline__ static void st(half* p, const float* x) {
+    f16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (half)x[j];
+    *reinterpret_cast<f16x8*>(p) = v;
+  }
+};
 template <> struct Vec8<float> {
   __device__ __forceinline__ static void ld(const float* p, float* x) {
     float4 a = *reinterpret_cast<const float4*>(p);
@@ -113,14 +126,20 @@ static hipError_t launch_gn_t(const GateArgs& a, hipStream_t st) {
 
 template <typename TY, typename TG>
 static hipError_t launch_gn_o(const GateArgs& a, hipStream_t st) {
-  return a.out_dt == RET_BF16 ? launch_gn_t<TY, TG, bf16>(a, st) : launch_gn_t<TY, TG, float>(a, st);
+  if (a.out_dt == RET_BF16) return launch_gn_t<TY, TG, bf16>(a, st);
+  if (a.out_dt == RET_F16) return launch_gn_t<TY, TG, half>(a, st);
+  return launch_gn_t<TY, TG, float>(a, st);
 }
 template <typename TY>
 static hipError_t launch_gn_g(const GateArgs& a, hipStream_t st) {
-  return a.g_dt == RET_BF16 ? launch_gn_o<TY, bf16>(a, st) : launch_gn_o<TY, float>(a, st);
+  if (a.g_dt == RET_BF16) return launch_gn_o<TY, bf16>(a, st);
+  if (a.g_dt == RET_F16) return launch_gn_o<TY, half>(a, st);
+  return launch_gn_o<TY, float>(a, st);
 }
 hipError_t launch_gate_norm(const GateArgs& a, hipStream_t st) {
-  return a.y_dt == RET_BF16 ? launch_gn_g<bf16>(a, st) : launch_gn_g<float>(a, st);
+  if (a.y_dt == RET_BF16) return launch_gn_g<bf16>(a, st);
+  if (a.y_dt == RET_F16) return launch_gn_g<half>(a, st);
+  return launch_gn_g<float>(a, st);
 }
 
 }  // namespace ret

@@ -1,0 +1,187 @@
+// Projections of the gated MSR block (RetNet reading notes, §三.2 and §2.1):
+// Q = X W_Q, K = X W_K, V = X W_V, G = X W_G and Out = Z W_O, as
+//   C[M][N] = A[M][K] . B[N][K]^T
+// with B a bf16 weight held as [out_features][in_features] (so both operands
+// are contiguous along K) and fp32 accumulation.  A bf16 A is contracted on
+// v_mfma_f32_32x32x16_bf16 with the operands as given; an fp16 A (the
+// gated, normalised heads) on v_mfma_f32_32x32x16_f16 with B converted to
+// fp16 while it is staged into LDS.
+//
+// Block tile 256 x 256 x 32 on 8 waves (each 64 x 128 = 2 x 4 MFMA tiles);
+// the next K slab is loaded into registers while the current one is
+// multiplied out of LDS (two LDS buffers, one barrier per slab).  Rows and
+// columns beyond M / N are clamped on load and skipped on store; K must be a
+// multiple of 32.
+#include "internal.h"
+
+namespace ret {
+
+namespace {
+
+constexpr int GT = 512;          // threads
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int LP = BK + 8;       // LDS row pitch (elements): 80 bytes, 16-byte aligned
+constexpr int WM = 64, WN = 128; // wave tile
+constexpr int A_LD = BM * BK / 8 / GT;   // 16-byte loads per thread per slab (2)
+constexpr int B_LD = BN * BK / 8 / GT;   // (2)
+
+struct GemmSmem {
+  uint16_t a[2][BM * LP];
+  uint16_t b[2][BN * LP];
+};
+
+// bf16 -> fp16 for eight packed values
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u) {
+  f16x8 h;
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[2 * i] = (half)lo_bf(w[i]);
+    h[2 * i + 1] = (half)hi_bf(w[i]);
+  }
+  return __builtin_bit_cast(uint4, h);
+}
+
+template <typename TA> struct GemmOp;
+template <> struct GemmOp<bf16> {
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static void mma(f32x16& c, const frag& a, const frag& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static uint4 cvt_b(uint4 u) { return u; }
+};
+template <> struct GemmOp<half> {
+  typedef f16x8 frag;
+  __device__ __forceinline__ static void mma(f32x16& c, const frag& a, const frag& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static uint4 cvt_b(uint4 u) { return bf16x8_to_f16x8(u); }
+};
+
+template <typename TA, typename TO>
+__global__ void __launch_bounds__(GT, 1)
+gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, TO* __restrict__ C,
+               int M, int N, int K, int tiles_n) {
+  typedef GemmOp<TA> G;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  GemmSmem& sm = *reinterpret_cast<GemmSmem*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lh = lane >> 5, l32 = lane & 31;
+
+  // tile order: consecutive workgroups (round-robin over the XCDs) walk
+  // along N first so that an XCD keeps reusing one A row panel
+  const int tile = blockIdx.x;
+  const int tm = tile / tiles_n, tn = tile % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm = (wave >> 1) * WM;       // 4 x 2 waves
+  const int wn = (wave & 1) * WN;
+
+  // loader mapping: each 16-byte load covers 8 k of one row; a slab row has
+  // BK / 8 = 4 such pieces
+  uint4 ra[A_LD], rb[B_LD];
+  auto load_slab = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int e = tid + i * GT;
+      const int row = e >> 2, piece = e & 3;
+      const int gr = min(m0 + row, M - 1);
+      ra[i] = *reinterpret_cast<const uint4*>(A + (size_t)gr * K + k0 + piece * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int e = tid + i * GT;
+      const int row = e >> 2, piece = e & 3;
+      const int gr = min(n0 + row, N - 1);
+      rb[i] = *reinterpret_cast<const uint4*>(B + (size_t)gr * K + k0 + piece * 8);
+    }
+  };
+  auto store_slab = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int e = tid + i * GT;
+      *reinterpret_cast<uint4*>(&sm.a[buf][(e >> 2) * LP + (e & 3) * 8]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int e = tid + i * GT;
+      *reinterpret_cast<uint4*>(&sm.b[buf][(e >> 2) * LP + (e & 3) * 8]) = G::cvt_b(rb[i]);
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const int nk = K / BK;
+  load_slab(0);
+  store_slab(0);
+  __syncthreads();
+  for (int kb = 0; kb < nk; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < nk) load_slab((kb + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 16) {
+      typename G::frag af[2], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const typename G::frag*>(&sm.a[cur][(wm + i * 32 + l32) * LP + ks + 8 * lh]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *reinterpret_cast<const typename G::frag*>(&sm.b[cur][(wn + j * 32 + l32) * LP + ks + 8 * lh]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) G::mma(acc[i][j], af[i], bfr[j]);
+    }
+    if (kb + 1 < nk) store_slab(cur ^ 1);
+    __syncthreads();
+  }
+
+  // store: lane holds column l32 of each 32x32 tile, rows acc_row(r)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn + j * 32 + l32;
+      if (col < N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm + i * 32 + acc_row(r, lane);
+          if (row < M) C[(size_t)row * N + col] = Store<TO>::cvt(acc[i][j][r]);
+        }
+      }
+    }
+}
+
+template <typename TA, typename TO>
+static hipError_t launch_gemm_t(const void* A, const void* B, void* C, int M, int N, int K, hipStream_t st) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const size_t sh = sizeof(GemmSmem);
+  auto kern = gemm_nt_kernel<TA, TO>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GT), sh, st, (const uint16_t*)A, (const uint16_t*)B,
+                     (TO*)C, M, N, K, tiles_n);
+  return hipGetLastError();
+}
+
+template <typename TA>
+static hipError_t launch_gemm_a(const void* A, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                                hipStream_t st) {
+  if (c_dt == RET_BF16) return launch_gemm_t<TA, bf16>(A, B, C, M, N, K, st);
+  if (c_dt == RET_F16) return launch_gemm_t<TA, half>(A, B, C, M, N, K, st);
+  return launch_gemm_t<TA, float>(A, B, C, M, N, K, st);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                       hipStream_t st) {
+  return a_dt == RET_F16 ? launch_gemm_a<half>(A, B, C, c_dt, M, N, K, st)
+                         : launch_gemm_a<bf16>(A, B, C, c_dt, M, N, K, st);
+}
+
+}  // namespace ret

@@ -11,6 +11,26 @@ template <> struct Store<float> {
 template <> struct Store<bf16> {
   __device__ __forceinline__ static bf16 cvt(float x) { return bf16{f2bf(x)}; }
 };
+template <> struct Store<half> {
+  __device__ __forceinline__ static half cvt(float x) { return (half)x; }
+};
+
+// four consecutive outputs (8-byte aligned for 16-bit types, 16 for float)
+__device__ __forceinline__ void store4(float* p, const float* x) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+}
+__device__ __forceinline__ void store4(bf16* p, const float* x) {
+  uint2 u;
+  u.x = pack_bf2(x[0], x[1]);
+  u.y = pack_bf2(x[2], x[3]);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+__device__ __forceinline__ void store4(half* p, const float* x) {
+  typedef __attribute__((ext_vector_type(4))) _Float16 h4;
+  h4 v;
+  v[0] = (half)x[0]; v[1] = (half)x[1]; v[2] = (half)x[2]; v[3] = (half)x[3];
+  *reinterpret_cast<h4*>(p) = v;
+}
 
 struct StepArgs {
   const void *q, *k, *v;
@@ -54,5 +74,8 @@ struct ChunkArgs {
 hipError_t launch_chunkwise(const ChunkArgs& a, hipStream_t st, bool* supported);
 bool chunkwise_supported(ret_dtype in_dt, int dk, int dv);
 size_t chunkwise_workspace(int b, int h, int L, int dk, int dv, int B, unsigned flags);
+
+hipError_t launch_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                       hipStream_t st);
 
 }  // namespace ret

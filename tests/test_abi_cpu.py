@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(B):
     names = declared_functions()
-    assert {"retention_chunkwise_fwd", "retention_recurrent_step", "msr_gate_norm"} <= set(names)
+    assert {"retention_chunkwise_fwd", "retention_recurrent_step", "msr_gate_norm", "msr_gemm"} <= set(names)
     for n in names:
         assert hasattr(B.LIB, n), f"libretention.so does not export {n}"
     assert B.LIB.retention_abi_version() == 1
@@ -123,6 +123,17 @@ def test_gate_norm_validation(B):
     assert call(y=None) == 1
     assert call(o=FAKE) == 1
     assert call(g=FAKE_MIS) == 3
+
+
+def test_gemm_validation(B):
+    L = B.LIB
+    A, Bm, C = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    assert L.msr_gemm(A, 1, Bm, C, 1, 16, 16, 48, None) == 2          # K % 32
+    assert L.msr_gemm(A, 0, Bm, C, 1, 16, 16, 64, None) == 2          # f32 A
+    assert L.msr_gemm(A, 1, Bm, C, 7, 16, 16, 64, None) == 1          # bad dtype
+    assert L.msr_gemm(A, 1, Bm, A, 1, 16, 16, 64, None) == 1          # alias
+    assert L.msr_gemm(FAKE_MIS, 1, Bm, C, 1, 16, 16, 64, None) == 3
+    assert L.msr_gemm(A, 1, Bm, C, 1, 0, 16, 64, None) == 1
 
 
 def test_workspace_query(B):

@@ -156,3 +156,18 @@ def test_full_medium(R, B):
 
 def test_full_long(R):
     _full_config_sampled(R, W.CHUNKWISE["long"], 512, [(0, 0), (0, 15)])
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 256), (256, 512)])
+def test_fp16_inputs_and_output(R, dk, dv):
+    """fp16 q/k/v (exact copies of bf16 draws) and an fp16 output."""
+    b, h, L, B = 1, 2, 300, 64
+    flags = XPOS | ALL
+    q, k, v = W.chunkwise_inputs(b, h, L, dk, dv, "bf16", 1 / np.sqrt(dk), seed=21)
+    g, th = W.gamma_vector(h), W.theta_vector(dk)
+    announce(f"fp16 inputs dk{dk} dv{dv}")
+    o = R.chunkwise_fwd(dev(q, "bf16").half(), dev(k, "bf16").half(), dev(v, "bf16").half(), g, th, B, flags,
+                        out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    ref = oracle.retention_chunkwise(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), g, th, flags, B)[0]
+    check(f"fp16 in/out dk{dk} dv{dv}", host64(o), ref, TOL["bf16"])
