@@ -103,7 +103,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true", help="time the primary workload only")
-    ap.add_argument("--secondary", default="medium_B64,long,decode,gate_norm",
+    ap.add_argument("--secondary", default="medium_B64,long,decode,gate_norm,block,copy",
                     help="comma list of secondary measurements to run (empty for none)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -211,6 +211,33 @@ def main():
                            "hbm_frac": round(dbytes / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                            "tokens_per_s": db / (msd * 1e-3), "alg_mb_per_step": round(dbytes / 1e6, 1)}
         del S, qd, kd, vd
+        torch.cuda.empty_cache()
+    if "copy" in todo:
+        # a plain 1 GiB device copy: measured HBM reference and the
+        # calibration kernel for the FETCH_SIZE / WRITE_SIZE counters
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        msc = time_calls(lambda: dst.copy_(src), 5, 1, torch)
+        extra["copy_1GiB"] = {"ms": round(msc, 4), "gbs": round(2 * (1 << 30) / (msc * 1e-3) / 1e9, 1)}
+        del src, dst
+        torch.cuda.empty_cache()
+    if "block" in todo:
+        # full gated MSR block forward: 2 x 8192 tokens, d_model 4096, 16 heads
+        bc = W.BLOCK
+        X, WQ, WK, WV, WG, WO = W.block_inputs(**bc)
+        dT = lambda w: dev(np.ascontiguousarray(w.T))
+        Xd, wq, wk, wv, wg, wo = dev(X), dT(WQ), dT(WK), dT(WV), dT(WG), dT(WO)
+        del X, WQ, WK, WV, WG, WO
+        bg, bth = W.gamma_vector(bc["h"]), W.theta_vector(bc["dk"])
+        msb = time_calls(lambda: R.msr_block_fwd(Xd, wq, wk, wv, wg, wo, bg, bth, bc["chunk"], bc["flags"],
+                                                   bc["eps"]), 3, 1, torch)
+        M, dm, hdk, hdv = bc["b"] * bc["L"], bc["d_model"], bc["h"] * bc["dk"], bc["h"] * bc["dv"]
+        gflop = 2 * M * dm * (2 * hdk + 2 * hdv) + 2 * M * hdv * dm
+        rflop = chunk_flops(bc["b"], bc["h"], bc["L"], bc["dk"], bc["dv"], bc["chunk"])
+        extra["block"] = {"ms": round(msb, 3), "tokens_per_s": M / (msb * 1e-3),
+                          "tflops": round((gflop + rflop) / (msb * 1e-3) / 1e12, 1),
+                          "gemm_gflop": round(gflop / 1e9, 1), "retention_gflop": round(rflop / 1e9, 1)}
+        del Xd, wq, wk, wv, wg, wo
         torch.cuda.empty_cache()
     if "gate_norm" in todo:
         # GroupNorm + gate at the block shape (2 x 8192 tokens, 16 heads x 512)

@@ -1,0 +1,649 @@
+// Chunkwise recurrent retention forward for large chunks (RetNet reading
+// notes, §2.4, with §2.3's xPos rotation and §三.3's normalisations), split
+// into three kernels whose boundaries are the only synchronisation:
+//
+//   delta  (one workgroup per head, chunk and half of d_v)
+//          dR_i = K'_[i]^T (V_[i] (.) zeta),  dz_i = K'_[i]^T zeta
+//          and, once per head and chunk, the rotated keys K' in fp16
+//   scan   (one workgroup per head and block of 32 state columns)
+//          R_i = gamma^(B_i) R_{i-1} + dR_i,  z_i likewise; it stores the
+//          state every chunk starts from, R_{i-1}, as an fp16 operand copy
+//          scaled by a power of two per block of 32 columns
+//   output (one workgroup per head, chunk and 64-row query tile)
+//          O = (Q'K'^T (.) D) V + (Q' R_{i-1}) (.) xi, with the row scales and
+//          score normalisation, written once
+//
+// Every key and value element is rotated / converted once by the delta
+// kernel (the output kernel reads the rotated fp16 keys), and no work is
+// repeated across d_v slices.  Operands are fp16 with fp32 accumulation.
+// Shapes: d_k = 256, d_v = 512, chunk B a multiple of 64 and >= 128.
+#include "internal.h"
+
+namespace ret {
+
+namespace {
+
+constexpr int NT3 = 512;
+constexpr int DK = 256, DV = 512;
+constexpr int TK = 64, TR = 64;
+constexpr int QP = DK + 8;     // fp16 row pitch of Qs / Ks (528 B)
+constexpr int KP = TK + 8;     // fp16 row pitch of key-major tiles (144 B)
+constexpr int NCB = DV / 32;   // column blocks of the state operand
+
+struct Work {
+  half* kt;      // rotated keys       [bh][L][DK]
+  half* dR;      // chunk deltas       [bh][nc][DV][DK]   (column-major: [col][d])
+  float* dRs;    // delta scales       [bh][nc][2]        (2^e per d_v half)
+  float* dz;     // key-sum deltas     [bh][nc][DK]
+  half* Rt;      // state operands     [bh][nc][DV][DK]   (R_{i-1}, [col][d])
+  float* Rs;     // operand scales     [bh][nc][NCB]
+  float* zc;     // z_{i-1}            [bh][nc][DK]
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t carve(void* base, int bh, int L, int nc, Work* w) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t o_kt = take((size_t)bh * L * DK * 2);
+  const size_t o_dR = take((size_t)bh * nc * DV * DK * 2);
+  const size_t o_dRs = take((size_t)bh * nc * 2 * 4);
+  const size_t o_dz = take((size_t)bh * nc * DK * 4);
+  const size_t o_Rt = take((size_t)bh * nc * DV * DK * 2);
+  const size_t o_Rs = take((size_t)bh * nc * NCB * 4);
+  const size_t o_zc = take((size_t)bh * nc * DK * 4);
+  if (w) {
+    char* b = static_cast<char*>(base);
+    w->kt = reinterpret_cast<half*>(b + o_kt);
+    w->dR = reinterpret_cast<half*>(b + o_dR);
+    w->dRs = reinterpret_cast<float*>(b + o_dRs);
+    w->dz = reinterpret_cast<float*>(b + o_dz);
+    w->Rt = reinterpret_cast<half*>(b + o_Rt);
+    w->Rs = reinterpret_cast<float*>(b + o_Rs);
+    w->zc = reinterpret_cast<float*>(b + o_zc);
+  }
+  return off;
+}
+
+template <typename T> struct Raw32;
+template <> struct Raw32<bf16> {
+  __device__ __forceinline__ static float2 f(uint32_t u) { return make_float2(lo_bf(u), hi_bf(u)); }
+};
+template <> struct Raw32<half> {
+  __device__ __forceinline__ static float2 f(uint32_t u) {
+    f16x2 v = __builtin_bit_cast(f16x2, u);
+    return make_float2((float)v.x, (float)v.y);
+  }
+};
+
+struct P3 {
+  const void *q, *k, *v;
+  void* o;
+  ret_strides sq, sk, sv, so;
+  int h, L, B, nc, nrt;
+  int64_t pos0, n_prev;
+  unsigned flags;
+  const float *state_in, *z_in;
+  float *state_out, *z_out;
+  Work w;
+};
+
+// the workgroups of one group (same head and chunk) land on one XCD
+__device__ __forceinline__ int xcd_local(int g, int n) {
+  return ((n & 7) == 0) ? (g & 7) * (n >> 3) + (g >> 3) : g;
+}
+
+__device__ __forceinline__ float maxabs_block(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
+// power-of-two exponent that puts max |x| just below 2^15
+__device__ __forceinline__ int scale_exp(float amax) {
+  if (!(amax > 0.f) || !(amax < 3.0e38f)) return 0;
+  int ex;
+  frexpf(amax, &ex);
+  return min(max(ex - 15, -100), 100);
+}
+
+// ---------------------------------------------------------------- delta
+struct DeltaSmem {
+  half KT[DK * KP];     // zeta-scaled K'^T tile: [d][key]
+  half VT[256 * KP];    // V^T tile of this d_v half: [col][key]
+  float red[NT3 / 64];
+};
+
+template <typename T>
+__global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  DeltaSmem& sm = *reinterpret_cast<DeltaSmem*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lh = lane >> 5, l32 = lane & 31;
+  const int g = xcd_local(blockIdx.x, gridDim.x);
+  const int half_ = g & 1;
+  const int c = (g >> 1) % p.nc;
+  const int bh = (g >> 1) / p.nc;
+  const int bb = bh / p.h, head = bh % p.h;
+  const int c0 = c * p.B;
+  const int Bc = min(p.B, p.L - c0);
+  Decay dec;
+  dec.init(hp.gamma[head]);
+  const bool xpos = (p.flags & RET_XPOS) != 0;
+
+  const T* Kg = reinterpret_cast<const T*>(p.k) + bb * p.sk.b + head * p.sk.h + (int64_t)c0 * p.sk.l;
+  const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + (int64_t)c0 * p.sv.l + half_ * 256;
+  half* ktg = p.w.kt + ((int64_t)bh * p.L + c0) * DK;
+
+  // wave tile: d rows [(wave >> 1) * 64, +64), columns [(wave & 1) * 128, +128)
+  const int d0 = (wave >> 1) * 64, n0 = (wave & 1) * 128;
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  float dz = 0.f;   // d = tid (tid < DK) of the key-sum delta, half 0 only
+
+  const int j = tid & 127, grp = tid >> 7;   // xPos pair / column pair, 16-key group
+  const int nkt = (Bc + TK - 1) / TK;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * TK;
+    const int kvalid = min(TK, Bc - k0);
+    // ---- rotated, zeta-scaled keys -> KT (and the rotated keys -> workspace)
+    {
+      float a[16], b[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = grp * 16 + i;
+        const int kc = min(key, kvalid - 1);
+        float2 x = Elem<T>::ld2(Kg + (uint32_t)((k0 + kc) * (int)p.sk.l + 2 * j));
+        a[i] = key < kvalid ? x.x : 0.f;
+        b[i] = key < kvalid ? x.y : 0.f;
+      }
+      float cs = 1.f, sn = 0.f, c1 = 1.f, s1 = 0.f;
+      if (xpos) {
+        phase(p.pos0 + c0 + k0 + grp * 16, hp.theta[j], cs, sn);
+        phase(1, hp.theta[j], c1, s1);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (xpos) {
+          rot(a[i], b[i], cs, sn);
+          advance(cs, sn, c1, s1);
+        }
+        const int key = grp * 16 + i;
+        if (half_ == 0 && key < kvalid) st2(ktg + (int64_t)(k0 + key) * DK + 2 * j, a[i], b[i]);
+        const float z = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key) * dec.lg2);
+        a[i] *= z;
+        b[i] *= z;
+      }
+      st8(sm.KT + (2 * j) * KP + grp * 16, a);
+      st8(sm.KT + (2 * j) * KP + grp * 16 + 8, a + 8);
+      st8(sm.KT + (2 * j + 1) * KP + grp * 16, b);
+      st8(sm.KT + (2 * j + 1) * KP + grp * 16 + 8, b + 8);
+    }
+    // ---- V^T of this half's 256 columns
+    {
+      float a[16], b[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = grp * 16 + i;
+        const int kc = min(key, kvalid - 1);
+        float2 x = Elem<T>::ld2(Vg + (uint32_t)((k0 + kc) * (int)p.sv.l + 2 * j));
+        a[i] = key < kvalid ? x.x : 0.f;
+        b[i] = key < kvalid ? x.y : 0.f;
+      }
+      st8(sm.VT + (2 * j) * KP + grp * 16, a);
+      st8(sm.VT + (2 * j) * KP + grp * 16 + 8, a + 8);
+      st8(sm.VT + (2 * j + 1) * KP + grp * 16, b);
+      st8(sm.VT + (2 * j + 1) * KP + grp * 16 + 8, b + 8);
+    }
+    __syncthreads();
+    if (half_ == 0 && tid < DK) {
+      float s = 0.f;
+      for (int key = 0; key < TK; ++key) s += (float)sm.KT[tid * KP + key];
+      dz += s;
+    }
+#pragma unroll
+    for (int kb = 0; kb < TK; kb += 16) {
+      f16x8 af[2], bf[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const f16x8*>(sm.KT + (d0 + 32 * i + l32) * KP + kb + 8 * lh);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) bf[jj] = *reinterpret_cast<const f16x8*>(sm.VT + (n0 + 32 * jj + l32) * KP + kb + 8 * lh);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[jj], acc[i][jj], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // ---- store dR (scaled fp16, [col][d]) and its scale, dz
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[i][jj][r]));
+  amax = maxabs_block(amax, sm.red);
+  const int e = scale_exp(amax);
+  const float down = ldexpf(1.f, -e);
+  half* dR = p.w.dR + ((int64_t)bh * p.nc + c) * DV * DK;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int col = half_ * 256 + n0 + 32 * jj + l32;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = d0 + 32 * i + 8 * rg + 4 * lh;   // acc rows 4*rg .. 4*rg+3 are d .. d+3
+        float x[4] = {acc[i][jj][4 * rg] * down, acc[i][jj][4 * rg + 1] * down, acc[i][jj][4 * rg + 2] * down,
+                      acc[i][jj][4 * rg + 3] * down};
+        st4(dR + (int64_t)col * DK + d, x);
+      }
+    }
+  if (tid == 0) p.w.dRs[((int64_t)bh * p.nc + c) * 2 + half_] = ldexpf(1.f, e);
+  if (half_ == 0 && tid < DK) p.w.dz[((int64_t)bh * p.nc + c) * DK + tid] = dz;
+}
+
+// ---------------------------------------------------------------- scan
+// one workgroup (256 threads) per head and block of 32 state columns; thread
+// -> column cb*32 + tid/8 and 32 consecutive d
+__global__ void __launch_bounds__(256) scan_kernel(P3 p, HeadParams hp) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int cb = blockIdx.x % NCB, bh = blockIdx.x / NCB;
+  const int head = bh % p.h;
+  const int col = cb * 32 + (tid >> 3);
+  const int dbase = (tid & 7) * 32;
+  const int half_ = col >> 8;
+  Decay dec;
+  dec.init(hp.gamma[head]);
+  float R[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    R[i] = p.state_in ? p.state_in[((int64_t)bh * DK + dbase + i) * DV + col] : 0.f;
+  float z = 0.f;
+  if (cb == 0 && p.z_in) z = p.z_in[(int64_t)bh * DK + tid];
+  for (int c = 0; c < p.nc; ++c) {
+    const int Bc = min(p.B, p.L - c * p.B);
+    // publish R_{c-1} and z_{c-1}
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(R[i]));
+    amax = maxabs_block(amax, red);
+    const int e = scale_exp(amax);
+    const float down = ldexpf(1.f, -e);
+    half* dst = p.w.Rt + (((int64_t)bh * p.nc + c) * DV + col) * DK + dbase;
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = R[i + u] * down;
+      st8(dst + i, x);
+    }
+    if (tid == 0) p.w.Rs[((int64_t)bh * p.nc + c) * NCB + cb] = ldexpf(1.f, e);
+    if (cb == 0) p.w.zc[((int64_t)bh * p.nc + c) * DK + tid] = z;
+    // advance
+    const float gB = dec.pow((float)Bc);
+    const float ds = p.w.dRs[((int64_t)bh * p.nc + c) * 2 + half_];
+    const half* src = p.w.dR + (((int64_t)bh * p.nc + c) * DV + col) * DK + dbase;
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      f16x8 v = *reinterpret_cast<const f16x8*>(src + i);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) R[i + u] = gB * R[i + u] + (float)v[u] * ds;
+    }
+    if (cb == 0) z = gB * z + p.w.dz[((int64_t)bh * p.nc + c) * DK + tid];
+  }
+  if (p.state_out) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) p.state_out[((int64_t)bh * DK + dbase + i) * DV + col] = R[i];
+  }
+  if (cb == 0 && p.z_out) p.z_out[(int64_t)bh * DK + tid] = z;
+}
+
+// ---------------------------------------------------------------- output
+struct OutSmem {
+  half Qs[TR * QP];
+  union {
+    struct {
+      half Ks[TK * QP];
+      half Vt[DV * KP];     // V^T tile [col][key]
+    } kv;
+    half Rt[DV * KP];       // d-slice of the state operand [col][64 d]
+    float Os[TR * (256 + 4)];   // output staging, half the columns at a time
+  } u;
+  half Ps[TR * KP];
+  float rs[TR], xs[TR], dens[TR];
+  float zs[DK];
+};
+
+template <typename T, typename TO>
+__global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  OutSmem& sm = *reinterpret_cast<OutSmem*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lh = lane >> 5, l32 = lane & 31;
+  const int g = xcd_local(blockIdx.x, gridDim.x);
+  const int rt = p.nrt - 1 - (g % p.nrt);         // heavier query tiles first
+  const int c = (g / p.nrt) % p.nc;
+  const int bh = (g / p.nrt) / p.nc;
+  const int bb = bh / p.h, head = bh % p.h;
+  const int c0 = c * p.B;
+  const int Bc = min(p.B, p.L - c0);
+  const int r0 = rt * TR;
+  if (r0 >= Bc) return;                           // ragged last chunk
+  const int qvalid = min(TR, Bc - r0);
+  Decay dec;
+  dec.init(hp.gamma[head]);
+  const bool xpos = (p.flags & RET_XPOS) != 0;
+  const float qk_scale = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
+
+  const T* Qg = reinterpret_cast<const T*>(p.q) + bb * p.sq.b + head * p.sq.h + (int64_t)(c0 + r0) * p.sq.l;
+  const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + (int64_t)c0 * p.sv.l;
+  const half* Kt = p.w.kt + ((int64_t)bh * p.L + c0) * DK;
+  TO* Og = reinterpret_cast<TO*>(p.o) + bb * p.so.b + head * p.so.h + (int64_t)(c0 + r0) * p.so.l;
+
+  // ---- rotated query tile, row tables
+  {
+    const int j = tid & 127, grp = tid >> 7;      // 16 rows per group
+    float a[16], b[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = grp * 16 + i;
+      const int rc = min(row, qvalid - 1);
+      float2 x = Elem<T>::ld2(Qg + (uint32_t)(rc * (int)p.sq.l + 2 * j));
+      a[i] = row < qvalid ? x.x : 0.f;
+      b[i] = row < qvalid ? x.y : 0.f;
+    }
+    float cs = 1.f, sn = 0.f, c1 = 1.f, s1 = 0.f;
+    if (xpos) {
+      phase(p.pos0 + c0 + r0 + grp * 16, hp.theta[j], cs, sn);
+      phase(1, hp.theta[j], c1, s1);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (xpos) {
+        rot(a[i], b[i], cs, sn);
+        advance(cs, sn, c1, s1);
+      }
+      st2(sm.Qs + (grp * 16 + i) * QP + 2 * j, a[i], b[i]);
+    }
+    if (tid < TR) {
+      float s = qk_scale;
+      if (p.flags & RET_NORM_DROW) s *= dec.drow((float)(p.n_prev + c0 + r0 + tid + 1));
+      sm.rs[tid] = s;
+      sm.xs[tid] = s * dec.pow((float)(r0 + tid + 1));
+      sm.dens[tid] = 0.f;
+    }
+    if (tid < DK) sm.zs[tid] = p.w.zc[((int64_t)bh * p.nc + c) * DK + tid];
+  }
+
+  // ---- staged key / value tile registers
+  uint4 kreg[4];          // 64 keys x 256 d fp16: 2048 16-byte pieces, 4 per thread
+  uint32_t vreg[32];      // 32 keys x one column pair of V
+  const int vcp = tid & 255, vgrp = tid >> 8;     // column pair, 32-key group
+  auto issue = [&](int kt) {
+    const int k0 = kt * TK;
+    const int kvalid = min(TK, Bc - k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + i * NT3;
+      const int key = min(e >> 5, kvalid - 1), piece = e & 31;
+      kreg[i] = *reinterpret_cast<const uint4*>(Kt + (int64_t)(k0 + key) * DK + piece * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int key = vgrp * 32 + i;
+      const int kc = min(key, kvalid - 1);
+      vreg[i] = *reinterpret_cast<const uint32_t*>(Vg + (uint32_t)((k0 + kc) * (int)p.sv.l + 2 * vcp));
+      if (key >= kvalid) vreg[i] = 0u;
+    }
+  };
+  auto commit = [&](int kt) {
+    const int kvalid = min(TK, Bc - kt * TK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + i * NT3;
+      const int key = e >> 5, piece = e & 31;
+      uint4 v = kreg[i];
+      if (key >= kvalid) v = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(sm.u.kv.Ks + key * QP + piece * 8) = v;
+    }
+    float a[32], b[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float2 x = Raw32<T>::f(vreg[i]);
+      a[i] = x.x;
+      b[i] = x.y;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      st8(sm.u.kv.Vt + (2 * vcp) * KP + vgrp * 32 + i, a + i);
+      st8(sm.u.kv.Vt + (2 * vcp + 1) * KP + vgrp * 32 + i, b + i);
+    }
+  };
+
+  // output tiles of this wave: query halves {0,1} x column tiles {2w, 2w+1}
+  f32x16 O[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) O[i][jj] = f32x16{};
+  float den = 0.f;
+  const int sk = wave >> 1, sqh = wave & 1;      // S^T tile of waves 0..3
+
+  issue(rt);
+  for (int idx = 0; idx <= rt; ++idx) {
+    const int kt = (idx == 0) ? rt : idx - 1;    // diagonal tile first
+    const bool diag = (idx == 0);
+    const int k0 = kt * TK;
+    __syncthreads();
+    commit(kt);
+    __syncthreads();
+    if (idx < rt) issue(idx);                     // next: kt = idx
+    if (wave < 4) {
+      const bool skip = diag && sk > sqh;         // keys 32..63 vs queries 0..31 of the diagonal
+      const int qi = r0 + sqh * 32 + l32;
+      if (!skip) {
+        f32x16 S = {};
+#pragma unroll 2
+        for (int kb = 0; kb < DK; kb += 16) {
+          f16x8 a = *reinterpret_cast<const f16x8*>(sm.u.kv.Ks + (sk * 32 + l32) * QP + kb + 8 * lh);
+          f16x8 b = *reinterpret_cast<const f16x8*>(sm.Qs + (sqh * 32 + l32) * QP + kb + 8 * lh);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, S, 0, 0, 0);
+        }
+        const float s_q = sm.rs[sqh * 32 + l32];
+        const float base = (float)(qi - k0 - sk * 32 - 4 * lh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float pv[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float dist = base - (float)(8 * i + jj);
+            float val = 0.f;
+            if (dist >= 0.f) val = S[4 * i + jj] * s_q * __builtin_amdgcn_exp2f(dist * dec.lg2);
+            den += val;
+            pv[jj] = val;
+          }
+          st4(sm.Ps + (sqh * 32 + l32) * KP + sk * 32 + 8 * i + 4 * lh, pv);
+        }
+      } else {
+        const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st4(sm.Ps + (sqh * 32 + l32) * KP + sk * 32 + 8 * i + 4 * lh, zero4);
+      }
+    }
+    __syncthreads();
+    // O += P V
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int kend = (diag && qh == 0) ? 32 : TK;
+      for (int kb = 0; kb < kend; kb += 16) {
+        f16x8 a = *reinterpret_cast<const f16x8*>(sm.Ps + (qh * 32 + l32) * KP + kb + 8 * lh);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          f16x8 b = *reinterpret_cast<const f16x8*>(sm.u.kv.Vt + ((2 * wave + jj) * 32 + l32) * KP + kb + 8 * lh);
+          O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, O[qh][jj], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- cross-chunk term with R_{c-1} (scaled per block of 32 columns)
+  __syncthreads();
+  if (wave < 4) {
+    den += __shfl_xor(den, 32, 64);
+    if (lh == 0) atomicAdd(&sm.dens[sqh * 32 + l32], den);
+  }
+  // query rows scaled by s xi
+  for (int e = tid; e < TR * DK / 8; e += NT3) {
+    const int row = e / (DK / 8), piece = e % (DK / 8);
+    f16x8 v = *reinterpret_cast<const f16x8*>(sm.Qs + row * QP + piece * 8);
+    const float f = sm.xs[row];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (half)((float)v[u] * f);
+    *reinterpret_cast<f16x8*>(sm.Qs + row * QP + piece * 8) = v;
+  }
+  __syncthreads();
+  {
+    // 8 threads per query row for (s xi Q') . z_{c-1}
+    const int row = tid >> 3, part = tid & 7;
+    float acc = 0.f;
+    for (int d = part; d < DK; d += 8) acc += (float)sm.Qs[row * QP + d] * sm.zs[d];
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    acc += __shfl_xor(acc, 4, 64);
+    if (part == 0) atomicAdd(&sm.dens[row], acc);
+  }
+  const float* Rs = p.w.Rs + ((int64_t)bh * p.nc + c) * NCB;
+  float up[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    up[jj] = Rs[2 * wave + jj];
+    const float dn = 1.f / up[jj];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) O[qh][jj] *= dn;
+  }
+  const half* Rg = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK;
+  for (int ds = 0; ds < DK; ds += 64) {
+    __syncthreads();
+    // d-slice [ds, ds+64) of R_{c-1}^T: 512 columns x 64 d = 4096 16-byte pieces
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = tid + i * NT3;
+      const int col = e >> 3, piece = e & 7;
+      *reinterpret_cast<uint4*>(sm.u.Rt + col * KP + piece * 8) =
+          *reinterpret_cast<const uint4*>(Rg + (int64_t)col * DK + ds + piece * 8);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < 64; kb += 16) {
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        f16x8 a = *reinterpret_cast<const f16x8*>(sm.Qs + (qh * 32 + l32) * QP + ds + kb + 8 * lh);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          f16x8 b = *reinterpret_cast<const f16x8*>(sm.u.Rt + ((2 * wave + jj) * 32 + l32) * KP + kb + 8 * lh);
+          O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, O[qh][jj], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) O[qh][jj] *= up[jj];
+
+  // ---- normalise and store, half of the columns at a time through LDS
+  const bool norm = (p.flags & RET_NORM_SCORE) != 0;
+  for (int hc = 0; hc < 2; ++hc) {
+    __syncthreads();
+    if ((wave >> 2) == hc) {
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int colh = ((2 * wave + jj) * 32 + l32) - hc * 256;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = qh * 32 + acc_row(r, lane);
+            float val = O[qh][jj][r];
+            if (norm) val = val / fmaxf(fabsf(sm.dens[row]), 1.f);
+            sm.u.Os[row * (256 + 4) + colh] = val;
+          }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < TR * 64; e += NT3) {
+      const int row = e >> 6, c4 = e & 63;
+      if (row < qvalid) store4(Og + (int64_t)row * p.so.l + hc * 256 + 4 * c4, sm.u.Os + row * (256 + 4) + 4 * c4);
+    }
+  }
+}
+
+template <typename T, typename TO>
+hipError_t run(const ChunkArgs& a, hipStream_t st) {
+  P3 p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o;
+  p.sq = a.sq; p.sk = a.sk; p.sv = a.sv; p.so = a.so;
+  p.h = a.h; p.L = a.L; p.B = a.B;
+  p.nc = (a.L + a.B - 1) / a.B;
+  p.nrt = a.B / TR;
+  p.pos0 = a.pos0; p.n_prev = a.n_prev; p.flags = a.flags;
+  p.state_in = a.state_in; p.z_in = a.z_in; p.state_out = a.state_out; p.z_out = a.z_out;
+  const int bh = a.b * a.h;
+  carve(a.ws, bh, a.L, p.nc, &p.w);
+  hipError_t e;
+  {
+    auto k = delta_kernel<T>;
+    e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(DeltaSmem));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(bh * p.nc * 2), dim3(NT3), sizeof(DeltaSmem), st, p, *a.hp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(scan_kernel, dim3(bh * NCB), dim3(256), 0, st, p, *a.hp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    auto k = output_kernel<T, TO>;
+    e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(OutSmem));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(bh * p.nc * p.nrt), dim3(NT3), sizeof(OutSmem), st, p, *a.hp);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t run_o(const ChunkArgs& a, hipStream_t st) {
+  if (a.out_dt == RET_BF16) return run<T, bf16>(a, st);
+  if (a.out_dt == RET_F16) return run<T, half>(a, st);
+  return run<T, float>(a, st);
+}
+
+}  // namespace
+
+bool three_phase_applies(ret_dtype in_dt, int dk, int dv, int B) {
+  return (in_dt == RET_BF16 || in_dt == RET_F16) && dk == DK && dv == DV && B >= 128 && B % 64 == 0;
+}
+
+size_t three_phase_workspace(int b, int h, int L, int B) {
+  return carve(nullptr, b * h, L, (L + B - 1) / B, nullptr);
+}
+
+hipError_t launch_three_phase(const ChunkArgs& a, hipStream_t st) {
+  return a.in_dt == RET_F16 ? run_o<half>(a, st) : run_o<bf16>(a, st);
+}
+
+}  // namespace ret

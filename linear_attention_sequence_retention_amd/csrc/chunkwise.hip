@@ -567,10 +567,15 @@ bool chunkwise_supported(ret_dtype in_dt, int dk, int dv) {
   return false;
 }
 
-size_t chunkwise_workspace(int, int, int, int, int, int, unsigned) { return 0; }
+size_t chunkwise_workspace(int b, int h, int L, int dk, int dv, int B, unsigned) {
+  // the workspace query has no dtype: the large-chunk path serves bf16 / f16
+  // inputs, and no f32 kernel exists for its shape
+  return three_phase_applies(RET_BF16, dk, dv, B) ? three_phase_workspace(b, h, L, B) : 0;
+}
 
 hipError_t launch_chunkwise(const ChunkArgs& a, hipStream_t st, bool* supported) {
   *supported = true;
+  if (three_phase_applies(a.in_dt, a.dk, a.dv, a.B)) return launch_three_phase(a, st);
 #define X(T, DK, DV, SV) \
   if (a.in_dt == dt_of<T>() && a.dk == DK && a.dv == DV) return launch_o<T, DK, DV, SV>(a, st);
   RET_SHAPES(X)

@@ -74,6 +74,10 @@ struct ChunkArgs {
 hipError_t launch_chunkwise(const ChunkArgs& a, hipStream_t st, bool* supported);
 bool chunkwise_supported(ret_dtype in_dt, int dk, int dv);
 size_t chunkwise_workspace(int b, int h, int L, int dk, int dv, int B, unsigned flags);
+// large-chunk path (delta / scan / output kernels)
+bool three_phase_applies(ret_dtype in_dt, int dk, int dv, int B);
+size_t three_phase_workspace(int b, int h, int L, int B);
+hipError_t launch_three_phase(const ChunkArgs& a, hipStream_t st);
 
 hipError_t launch_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
                        hipStream_t st);
