@@ -155,6 +155,20 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
 
   const int j = tid & 127, grp = tid >> 7;   // xPos pair / column pair, 16-key group
   const int nkt = (Bc + TK - 1) / TK;
+  // raw key / value pairs of the next tile, loaded while the current one is
+  // multiplied
+  uint32_t kr[16], vr[16];
+  auto issue = [&](int kt) {
+    const int k0 = kt * TK;
+    const int kvalid = min(TK, Bc - k0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kc = min(grp * 16 + i, kvalid - 1);
+      kr[i] = *reinterpret_cast<const uint32_t*>(Kg + (uint32_t)((k0 + kc) * (int)p.sk.l + 2 * j));
+      vr[i] = *reinterpret_cast<const uint32_t*>(Vg + (uint32_t)((k0 + kc) * (int)p.sv.l + 2 * j));
+    }
+  };
+  issue(0);
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * TK;
     const int kvalid = min(TK, Bc - k0);
@@ -164,8 +178,7 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = grp * 16 + i;
-        const int kc = min(key, kvalid - 1);
-        float2 x = Elem<T>::ld2(Kg + (uint32_t)((k0 + kc) * (int)p.sk.l + 2 * j));
+        float2 x = Raw32<T>::f(kr[i]);
         a[i] = key < kvalid ? x.x : 0.f;
         b[i] = key < kvalid ? x.y : 0.f;
       }
@@ -197,8 +210,7 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = grp * 16 + i;
-        const int kc = min(key, kvalid - 1);
-        float2 x = Elem<T>::ld2(Vg + (uint32_t)((k0 + kc) * (int)p.sv.l + 2 * j));
+        float2 x = Raw32<T>::f(vr[i]);
         a[i] = key < kvalid ? x.x : 0.f;
         b[i] = key < kvalid ? x.y : 0.f;
       }
@@ -207,13 +219,14 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
       st8(sm.VT + (2 * j + 1) * KP + grp * 16, b);
       st8(sm.VT + (2 * j + 1) * KP + grp * 16 + 8, b + 8);
     }
+    if (kt + 1 < nkt) issue(kt + 1);
     __syncthreads();
     if (half_ == 0 && tid < DK) {
       float s = 0.f;
       for (int key = 0; key < TK; ++key) s += (float)sm.KT[tid * KP + key];
       dz += s;
     }
-#pragma unroll
+#pragma unroll 2
     for (int kb = 0; kb < TK; kb += 16) {
       f16x8 af[2], bf[4];
 #pragma unroll
@@ -276,8 +289,24 @@ __global__ void __launch_bounds__(256) scan_kernel(P3 p, HeadParams hp) {
     R[i] = p.state_in ? p.state_in[((int64_t)bh * DK + dbase + i) * DV + col] : 0.f;
   float z = 0.f;
   if (cb == 0 && p.z_in) z = p.z_in[(int64_t)bh * DK + tid];
+  // the next chunk's delta is loaded while the current state is published
+  u32x4 nx[4];
+  float nds = 0.f, ndz = 0.f;
+  auto load_delta = [&](int c) {
+    const half* src = p.w.dR + (((int64_t)bh * p.nc + c) * DV + col) * DK + dbase;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nx[i] = *reinterpret_cast<const u32x4*>(src + 8 * i);
+    nds = p.w.dRs[((int64_t)bh * p.nc + c) * 2 + half_];
+    if (cb == 0) ndz = p.w.dz[((int64_t)bh * p.nc + c) * DK + tid];
+  };
+  load_delta(0);
   for (int c = 0; c < p.nc; ++c) {
     const int Bc = min(p.B, p.L - c * p.B);
+    u32x4 cur[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] = nx[i];
+    const float ds = nds, dzc = ndz;
+    if (c + 1 < p.nc) load_delta(c + 1);
     // publish R_{c-1} and z_{c-1}
     float amax = 0.f;
 #pragma unroll
@@ -297,15 +326,13 @@ __global__ void __launch_bounds__(256) scan_kernel(P3 p, HeadParams hp) {
     if (cb == 0) p.w.zc[((int64_t)bh * p.nc + c) * DK + tid] = z;
     // advance
     const float gB = dec.pow((float)Bc);
-    const float ds = p.w.dRs[((int64_t)bh * p.nc + c) * 2 + half_];
-    const half* src = p.w.dR + (((int64_t)bh * p.nc + c) * DV + col) * DK + dbase;
 #pragma unroll
-    for (int i = 0; i < 32; i += 8) {
-      f16x8 v = *reinterpret_cast<const f16x8*>(src + i);
+    for (int i = 0; i < 4; ++i) {
+      const f16x8 v = __builtin_bit_cast(f16x8, cur[i]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) R[i + u] = gB * R[i + u] + (float)v[u] * ds;
+      for (int u = 0; u < 8; ++u) R[8 * i + u] = gB * R[8 * i + u] + (float)v[u] * ds;
     }
-    if (cb == 0) z = gB * z + p.w.dz[((int64_t)bh * p.nc + c) * DK + tid];
+    if (cb == 0) z = gB * z + dzc;
   }
   if (p.state_out) {
 #pragma unroll
@@ -323,11 +350,11 @@ struct OutSmem {
       half Vt[DV * KP];     // V^T tile [col][key]
     } kv;
     half Rt[DV * KP];       // d-slice of the state operand [col][64 d]
-    float Os[TR * (256 + 4)];   // output staging, half the columns at a time
   } u;
   half Ps[TR * KP];
   float rs[TR], xs[TR], dens[TR];
   float zs[DK];
+  float ginv[32];           // gamma^-m, m = 0 .. 31
 };
 
 template <typename T, typename TO>
@@ -389,10 +416,11 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       sm.dens[tid] = 0.f;
     }
     if (tid < DK) sm.zs[tid] = p.w.zc[((int64_t)bh * p.nc + c) * DK + tid];
+    if (tid < 32) sm.ginv[tid] = __builtin_amdgcn_exp2f(-(float)tid * dec.lg2);
   }
 
   // ---- staged key / value tile registers
-  uint4 kreg[4];          // 64 keys x 256 d fp16: 2048 16-byte pieces, 4 per thread
+  u32x4 kreg[4];          // 64 keys x 256 d fp16: 2048 16-byte pieces, 4 per thread
   uint32_t vreg[32];      // 32 keys x one column pair of V
   const int vcp = tid & 255, vgrp = tid >> 8;     // column pair, 32-key group
   auto issue = [&](int kt) {
@@ -402,7 +430,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     for (int i = 0; i < 4; ++i) {
       const int e = tid + i * NT3;
       const int key = min(e >> 5, kvalid - 1), piece = e & 31;
-      kreg[i] = *reinterpret_cast<const uint4*>(Kt + (int64_t)(k0 + key) * DK + piece * 8);
+      kreg[i] = *reinterpret_cast<const u32x4*>(Kt + (int64_t)(k0 + key) * DK + piece * 8);
     }
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -418,21 +446,21 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     for (int i = 0; i < 4; ++i) {
       const int e = tid + i * NT3;
       const int key = e >> 5, piece = e & 31;
-      uint4 v = kreg[i];
-      if (key >= kvalid) v = make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(sm.u.kv.Ks + key * QP + piece * 8) = v;
-    }
-    float a[32], b[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      float2 x = Raw32<T>::f(vreg[i]);
-      a[i] = x.x;
-      b[i] = x.y;
+      u32x4 v = kreg[i];
+      if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sm.u.kv.Ks + key * QP + piece * 8) = v;
     }
 #pragma unroll
     for (int i = 0; i < 32; i += 8) {
-      st8(sm.u.kv.Vt + (2 * vcp) * KP + vgrp * 32 + i, a + i);
-      st8(sm.u.kv.Vt + (2 * vcp + 1) * KP + vgrp * 32 + i, b + i);
+      float a[8], b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float2 x = Raw32<T>::f(vreg[i + u]);
+        a[u] = x.x;
+        b[u] = x.y;
+      }
+      st8(sm.u.kv.Vt + (2 * vcp) * KP + vgrp * 32 + i, a);
+      st8(sm.u.kv.Vt + (2 * vcp + 1) * KP + vgrp * 32 + i, b);
     }
   };
 
@@ -442,12 +470,72 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) O[i][jj] = f32x16{};
+
+  // ---- cross-chunk term Q' R_{c-1}, one 64-wide d-slice of the state
+  // operand at a time; the next slice (after the last: the first key / value
+  // tile) is loaded into registers while the current one is multiplied
+  const half* Rg = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK;
+  {
+    u32x4 rreg[8];        // 512 columns x 64 d fp16: 4096 16-byte pieces, 8 per thread
+    auto issue_r = [&](int ds) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = tid + i * NT3;
+        rreg[i] = *reinterpret_cast<const u32x4*>(Rg + (int64_t)(e >> 3) * DK + ds + (e & 7) * 8);
+      }
+    };
+    issue_r(0);
+    for (int ds = 0; ds < DK; ds += 64) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = tid + i * NT3;
+        *reinterpret_cast<u32x4*>(sm.u.Rt + (e >> 3) * KP + (e & 7) * 8) = rreg[i];
+      }
+      __syncthreads();
+      if (ds + 64 < DK) issue_r(ds + 64);
+      else issue(rt);
+#pragma unroll
+      for (int kb = 0; kb < 64; kb += 16) {
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          f16x8 a = *reinterpret_cast<const f16x8*>(sm.Qs + (qh * 32 + l32) * QP + ds + kb + 8 * lh);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            f16x8 b = *reinterpret_cast<const f16x8*>(sm.u.Rt + ((2 * wave + jj) * 32 + l32) * KP + kb + 8 * lh);
+            O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, O[qh][jj], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  {
+    // row scale s xi and the operand's per-block power of two
+    const float* Rs = p.w.Rs + ((int64_t)bh * p.nc + c) * NCB;
+    const float up0 = Rs[2 * wave], up1 = Rs[2 * wave + 1];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = sm.xs[qh * 32 + acc_row(r, lane)];
+        O[qh][0][r] *= x * up0;
+        O[qh][1][r] *= x * up1;
+      }
+    // cross part of the score denominator, s xi (Q' . z_{c-1}): 8 threads per row
+    const int row = tid >> 3, part = tid & 7;
+    float acc = 0.f;
+    for (int d = part; d < DK; d += 8) acc += (float)sm.Qs[row * QP + d] * sm.zs[d];
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    acc += __shfl_xor(acc, 4, 64);
+    if (part == 0) sm.dens[row] = sm.xs[row] * acc;
+  }
+
+  // ---- within-chunk term, diagonal key tile first
   float den = 0.f;
   const int sk = wave >> 1, sqh = wave & 1;      // S^T tile of waves 0..3
-
-  issue(rt);
   for (int idx = 0; idx <= rt; ++idx) {
-    const int kt = (idx == 0) ? rt : idx - 1;    // diagonal tile first
+    const int kt = (idx == 0) ? rt : idx - 1;
     const bool diag = (idx == 0);
     const int k0 = kt * TK;
     __syncthreads();
@@ -465,16 +553,17 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
           f16x8 b = *reinterpret_cast<const f16x8*>(sm.Qs + (sqh * 32 + l32) * QP + kb + 8 * lh);
           S = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, S, 0, 0, 0);
         }
-        const float s_q = sm.rs[sqh * 32 + l32];
-        const float base = (float)(qi - k0 - sk * 32 - 4 * lh);
+        // D = gamma^(q - k) split as gamma^base gamma^-(8i + jj)
+        const int base = qi - k0 - sk * 32 - 4 * lh;
+        const float gq = sm.rs[sqh * 32 + l32] * __builtin_amdgcn_exp2f((float)base * dec.lg2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          const float4 gi = *reinterpret_cast<const float4*>(sm.ginv + 8 * i);
+          const float gv[4] = {gi.x, gi.y, gi.z, gi.w};
           float pv[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const float dist = base - (float)(8 * i + jj);
-            float val = 0.f;
-            if (dist >= 0.f) val = S[4 * i + jj] * s_q * __builtin_amdgcn_exp2f(dist * dec.lg2);
+            const float val = (base >= 8 * i + jj) ? S[4 * i + jj] * gq * gv[jj] : 0.f;
             den += val;
             pv[jj] = val;
           }
@@ -501,96 +590,38 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       }
     }
   }
-
-  // ---- cross-chunk term with R_{c-1} (scaled per block of 32 columns)
-  __syncthreads();
   if (wave < 4) {
     den += __shfl_xor(den, 32, 64);
     if (lh == 0) atomicAdd(&sm.dens[sqh * 32 + l32], den);
   }
-  // query rows scaled by s xi
-  for (int e = tid; e < TR * DK / 8; e += NT3) {
-    const int row = e / (DK / 8), piece = e % (DK / 8);
-    f16x8 v = *reinterpret_cast<const f16x8*>(sm.Qs + row * QP + piece * 8);
-    const float f = sm.xs[row];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = (half)((float)v[u] * f);
-    *reinterpret_cast<f16x8*>(sm.Qs + row * QP + piece * 8) = v;
-  }
   __syncthreads();
-  {
-    // 8 threads per query row for (s xi Q') . z_{c-1}
-    const int row = tid >> 3, part = tid & 7;
-    float acc = 0.f;
-    for (int d = part; d < DK; d += 8) acc += (float)sm.Qs[row * QP + d] * sm.zs[d];
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    if (part == 0) atomicAdd(&sm.dens[row], acc);
-  }
-  const float* Rs = p.w.Rs + ((int64_t)bh * p.nc + c) * NCB;
-  float up[2];
+  if (tid < TR) sm.rs[tid] = (p.flags & RET_NORM_SCORE) ? 1.f / fmaxf(fabsf(sm.dens[tid]), 1.f) : 1.f;
+
+  // ---- normalise and store: the whole tile is staged in LDS in the output
+  // type (over the query / key / value buffers, dead by now), then written
+  // with 16-byte stores
+  __syncthreads();
+  TO* Os = reinterpret_cast<TO*>(smem_raw);
+  constexpr int OV = 16 / (int)sizeof(TO);        // elements per 16 bytes
+  constexpr int OP = DV + OV;                     // staging row pitch
+  static_assert(TR * OP * sizeof(TO) <= offsetof(OutSmem, Ps), "staging overlaps live LDS");
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    up[jj] = Rs[2 * wave + jj];
-    const float dn = 1.f / up[jj];
+  for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) O[qh][jj] *= dn;
-  }
-  const half* Rg = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK;
-  for (int ds = 0; ds < DK; ds += 64) {
-    __syncthreads();
-    // d-slice [ds, ds+64) of R_{c-1}^T: 512 columns x 64 d = 4096 16-byte pieces
+    for (int jj = 0; jj < 2; ++jj) {
+      const int col = (2 * wave + jj) * 32 + l32;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = tid + i * NT3;
-      const int col = e >> 3, piece = e & 7;
-      *reinterpret_cast<uint4*>(sm.u.Rt + col * KP + piece * 8) =
-          *reinterpret_cast<const uint4*>(Rg + (int64_t)col * DK + ds + piece * 8);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < 64; kb += 16) {
-#pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {
-        f16x8 a = *reinterpret_cast<const f16x8*>(sm.Qs + (qh * 32 + l32) * QP + ds + kb + 8 * lh);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          f16x8 b = *reinterpret_cast<const f16x8*>(sm.u.Rt + ((2 * wave + jj) * 32 + l32) * KP + kb + 8 * lh);
-          O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, O[qh][jj], 0, 0, 0);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = qh * 32 + acc_row(r, lane);
+        Os[row * OP + col] = Store<TO>::cvt(O[qh][jj][r] * sm.rs[row]);
       }
     }
-  }
-#pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) O[qh][jj] *= up[jj];
-
-  // ---- normalise and store, half of the columns at a time through LDS
-  const bool norm = (p.flags & RET_NORM_SCORE) != 0;
-  for (int hc = 0; hc < 2; ++hc) {
-    __syncthreads();
-    if ((wave >> 2) == hc) {
-#pragma unroll
-      for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int colh = ((2 * wave + jj) * 32 + l32) - hc * 256;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = qh * 32 + acc_row(r, lane);
-            float val = O[qh][jj][r];
-            if (norm) val = val / fmaxf(fabsf(sm.dens[row]), 1.f);
-            sm.u.Os[row * (256 + 4) + colh] = val;
-          }
-        }
-    }
-    __syncthreads();
-    for (int e = tid; e < TR * 64; e += NT3) {
-      const int row = e >> 6, c4 = e & 63;
-      if (row < qvalid) store4(Og + (int64_t)row * p.so.l + hc * 256 + 4 * c4, sm.u.Os + row * (256 + 4) + 4 * c4);
-    }
+  __syncthreads();
+  for (int e = tid; e < TR * (DV / OV); e += NT3) {
+    const int row = e / (DV / OV), cv = e % (DV / OV);
+    if (row < qvalid)
+      *reinterpret_cast<u32x4*>(Og + (int64_t)row * p.so.l + cv * OV) =
+          *reinterpret_cast<const u32x4*>(Os + row * OP + cv * OV);
   }
 }
 

@@ -12,15 +12,15 @@ namespace ret {
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16> {
   __device__ __forceinline__ static void ld(const bf16* p, float* x) {
-    uint4 u = *reinterpret_cast<const uint4*>(p);
+    u32x4 u = *reinterpret_cast<const u32x4*>(p);
     x[0] = lo_bf(u.x); x[1] = hi_bf(u.x); x[2] = lo_bf(u.y); x[3] = hi_bf(u.y);
     x[4] = lo_bf(u.z); x[5] = hi_bf(u.z); x[6] = lo_bf(u.w); x[7] = hi_bf(u.w);
   }
   __device__ __forceinline__ static void st(bf16* p, const float* x) {
-    uint4 u;
+    u32x4 u;
     u.x = pack_bf2(x[0], x[1]); u.y = pack_bf2(x[2], x[3]);
     u.z = pack_bf2(x[4], x[5]); u.w = pack_bf2(x[6], x[7]);
-    *reinterpret_cast<uint4*>(p) = u;
+    *reinterpret_cast<u32x4*>(p) = u;
   }
 };
 template <> struct Vec8<half> {

@@ -31,7 +31,7 @@ struct GemmSmem {
 };
 
 // bf16 -> fp16 for eight packed values
-__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u) {
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 u) {
   f16x8 h;
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -39,7 +39,7 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u) {
     h[2 * i] = (half)lo_bf(w[i]);
     h[2 * i + 1] = (half)hi_bf(w[i]);
   }
-  return __builtin_bit_cast(uint4, h);
+  return __builtin_bit_cast(u32x4, h);
 }
 
 template <typename TA> struct GemmOp;
@@ -48,14 +48,14 @@ template <> struct GemmOp<bf16> {
   __device__ __forceinline__ static void mma(f32x16& c, const frag& a, const frag& b) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  __device__ __forceinline__ static uint4 cvt_b(uint4 u) { return u; }
+  __device__ __forceinline__ static u32x4 cvt_b(u32x4 u) { return u; }
 };
 template <> struct GemmOp<half> {
   typedef f16x8 frag;
   __device__ __forceinline__ static void mma(f32x16& c, const frag& a, const frag& b) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
-  __device__ __forceinline__ static uint4 cvt_b(uint4 u) { return bf16x8_to_f16x8(u); }
+  __device__ __forceinline__ static u32x4 cvt_b(u32x4 u) { return bf16x8_to_f16x8(u); }
 };
 
 template <typename TA, typename TO>
@@ -79,33 +79,33 @@ gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, T
 
   // loader mapping: each 16-byte load covers 8 k of one row; a slab row has
   // BK / 8 = 4 such pieces
-  uint4 ra[A_LD], rb[B_LD];
+  u32x4 ra[A_LD], rb[B_LD];
   auto load_slab = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
       const int e = tid + i * GT;
       const int row = e >> 2, piece = e & 3;
       const int gr = min(m0 + row, M - 1);
-      ra[i] = *reinterpret_cast<const uint4*>(A + (size_t)gr * K + k0 + piece * 8);
+      ra[i] = *reinterpret_cast<const u32x4*>(A + (size_t)gr * K + k0 + piece * 8);
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const int e = tid + i * GT;
       const int row = e >> 2, piece = e & 3;
       const int gr = min(n0 + row, N - 1);
-      rb[i] = *reinterpret_cast<const uint4*>(B + (size_t)gr * K + k0 + piece * 8);
+      rb[i] = *reinterpret_cast<const u32x4*>(B + (size_t)gr * K + k0 + piece * 8);
     }
   };
   auto store_slab = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
       const int e = tid + i * GT;
-      *reinterpret_cast<uint4*>(&sm.a[buf][(e >> 2) * LP + (e & 3) * 8]) = ra[i];
+      *reinterpret_cast<u32x4*>(&sm.a[buf][(e >> 2) * LP + (e & 3) * 8]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const int e = tid + i * GT;
-      *reinterpret_cast<uint4*>(&sm.b[buf][(e >> 2) * LP + (e & 3) * 8]) = G::cvt_b(rb[i]);
+      *reinterpret_cast<u32x4*>(&sm.b[buf][(e >> 2) * LP + (e & 3) * 8]) = G::cvt_b(rb[i]);
     }
   };
 
