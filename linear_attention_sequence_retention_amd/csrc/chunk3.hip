@@ -29,6 +29,10 @@ constexpr int TK = 64, TR = 64;
 constexpr int QP = DK + 8;     // fp16 row pitch of Qs / Ks (528 B)
 constexpr int KP = TK + 8;     // fp16 row pitch of key-major tiles (144 B)
 constexpr int NCB = DV / 32;   // column blocks of the state operand
+// row pitch (fp16) of a value tile kept in its natural [key][col] layout: 1088
+// bytes, so the four key rows of one transposed read start 64 bytes apart in
+// the bank space and a half-wave touches all 64 banks once
+constexpr int VP = DV + 32;
 
 struct Work {
   half* kt;      // rotated keys       [bh][L][DK]
@@ -79,6 +83,32 @@ template <> struct Raw32<half> {
     return make_float2((float)v.x, (float)v.y);
   }
 };
+
+// eight consecutive 16-bit inputs -> fp16 (the MFMA operand type)
+template <typename T> struct Raw16;
+template <> struct Raw16<bf16> {
+  __device__ __forceinline__ static u32x4 f16(u32x4 u) {
+    f16x8 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[2 * i] = (half)lo_bf(u[i]);
+      h[2 * i + 1] = (half)hi_bf(u[i]);
+    }
+    return __builtin_bit_cast(u32x4, h);
+  }
+};
+template <> struct Raw16<half> {
+  __device__ __forceinline__ static u32x4 f16(u32x4 u) { return u; }
+};
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i returns element (i & 3) of the 8-byte rows addressed by lanes
+// (i >> 2), 4 + (i >> 2), 8 + (i >> 2) and 12 + (i >> 2) of its group.
+__device__ __forceinline__ f16x4 lds_read_tr16(const half* p) {
+  typedef short s16x4 __attribute__((__vector_size__(8)));
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(f16x4, v);
+}
 
 struct P3 {
   const void *q, *k, *v;
@@ -347,7 +377,7 @@ struct OutSmem {
   union {
     struct {
       half Ks[TK * QP];
-      half Vt[DV * KP];     // V^T tile [col][key]
+      half Vn[TK * VP];     // value tile [key][col] (fp16)
     } kv;
     half Rt[DV * KP];       // d-slice of the state operand [col][64 d]
   } u;
@@ -421,8 +451,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
 
   // ---- staged key / value tile registers
   u32x4 kreg[4];          // 64 keys x 256 d fp16: 2048 16-byte pieces, 4 per thread
-  uint32_t vreg[32];      // 32 keys x one column pair of V
-  const int vcp = tid & 255, vgrp = tid >> 8;     // column pair, 32-key group
+  u32x4 vreg[8];          // 64 keys x 512 columns: 4096 16-byte pieces, 8 per thread
   auto issue = [&](int kt) {
     const int k0 = kt * TK;
     const int kvalid = min(TK, Bc - k0);
@@ -433,11 +462,10 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       kreg[i] = *reinterpret_cast<const u32x4*>(Kt + (int64_t)(k0 + key) * DK + piece * 8);
     }
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int key = vgrp * 32 + i;
-      const int kc = min(key, kvalid - 1);
-      vreg[i] = *reinterpret_cast<const uint32_t*>(Vg + (uint32_t)((k0 + kc) * (int)p.sv.l + 2 * vcp));
-      if (key >= kvalid) vreg[i] = 0u;
+    for (int i = 0; i < 8; ++i) {
+      const int e = tid + i * NT3;
+      const int key = min(e >> 6, kvalid - 1), piece = e & 63;
+      vreg[i] = *reinterpret_cast<const u32x4*>(Vg + (uint32_t)((k0 + key) * (int)p.sv.l + piece * 8));
     }
   };
   auto commit = [&](int kt) {
@@ -451,18 +479,17 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       *reinterpret_cast<u32x4*>(sm.u.kv.Ks + key * QP + piece * 8) = v;
     }
 #pragma unroll
-    for (int i = 0; i < 32; i += 8) {
-      float a[8], b[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        float2 x = Raw32<T>::f(vreg[i + u]);
-        a[u] = x.x;
-        b[u] = x.y;
-      }
-      st8(sm.u.kv.Vt + (2 * vcp) * KP + vgrp * 32 + i, a);
-      st8(sm.u.kv.Vt + (2 * vcp + 1) * KP + vgrp * 32 + i, b);
+    for (int i = 0; i < 8; ++i) {
+      const int e = tid + i * NT3;
+      const int key = e >> 6, piece = e & 63;
+      u32x4 v = Raw16<T>::f16(vreg[i]);
+      if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sm.u.kv.Vn + key * VP + piece * 8) = v;
     }
   };
+  // this lane's transposed-read origin in a value tile: key 8 (lane / 32) +
+  // (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
+  const int vtr = (8 * (lane >> 5) + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // output tiles of this wave: query halves {0,1} x column tiles {2w, 2w+1}
   f32x16 O[2][2];
@@ -495,17 +522,25 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       __syncthreads();
       if (ds + 64 < DK) issue_r(ds + 64);
       else issue(rt);
+      f16x8 qa[2][2], rb[2][2];
+      auto load_x = [&](int kb, int buf) {
 #pragma unroll
-      for (int kb = 0; kb < 64; kb += 16) {
-#pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
-          f16x8 a = *reinterpret_cast<const f16x8*>(sm.Qs + (qh * 32 + l32) * QP + ds + kb + 8 * lh);
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            f16x8 b = *reinterpret_cast<const f16x8*>(sm.u.Rt + ((2 * wave + jj) * 32 + l32) * KP + kb + 8 * lh);
-            O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, O[qh][jj], 0, 0, 0);
-          }
+        for (int i = 0; i < 2; ++i) {
+          qa[buf][i] = *reinterpret_cast<const f16x8*>(sm.Qs + (i * 32 + l32) * QP + ds + kb + 8 * lh);
+          rb[buf][i] = *reinterpret_cast<const f16x8*>(sm.u.Rt + ((2 * wave + i) * 32 + l32) * KP + kb + 8 * lh);
         }
+      };
+      load_x(0, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t + 1 < 4) load_x(16 * (t + 1), (t + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t & 1][qh], rb[t & 1][jj], O[qh][jj], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -532,66 +567,98 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   }
 
   // ---- within-chunk term, diagonal key tile first
+  // waves 0..3 form S^T = K' Q'^T as 32 x 32 tiles (keys 32 (w / 2) .., queries
+  // 32 (w % 2) ..) and write P; all eight waves then accumulate P V
   float den = 0.f;
-  const int sk = wave >> 1, sqh = wave & 1;      // S^T tile of waves 0..3
+  const int sk = wave >> 1, sqh = wave & 1;
   for (int idx = 0; idx <= rt; ++idx) {
     const int kt = (idx == 0) ? rt : idx - 1;
     const bool diag = (idx == 0);
     const int k0 = kt * TK;
     __syncthreads();
     commit(kt);
-    __syncthreads();
     if (idx < rt) issue(idx);                     // next: kt = idx
+    __syncthreads();
     if (wave < 4) {
       const bool skip = diag && sk > sqh;         // keys 32..63 vs queries 0..31 of the diagonal
-      const int qi = r0 + sqh * 32 + l32;
+      float pv[16];
       if (!skip) {
-        f32x16 S = {};
-#pragma unroll 2
-        for (int kb = 0; kb < DK; kb += 16) {
-          f16x8 a = *reinterpret_cast<const f16x8*>(sm.u.kv.Ks + (sk * 32 + l32) * QP + kb + 8 * lh);
-          f16x8 b = *reinterpret_cast<const f16x8*>(sm.Qs + (sqh * 32 + l32) * QP + kb + 8 * lh);
-          S = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, S, 0, 0, 0);
+        // fragments of step s + 3 are read while step s multiplies
+        const half* kp = sm.u.kv.Ks + (sk * 32 + l32) * QP + 8 * lh;
+        const half* qp = sm.Qs + (sqh * 32 + l32) * QP + 8 * lh;
+        constexpr int NS = DK / 16, PD = 4;
+        f16x8 ka[PD], qb[PD];
+#pragma unroll
+        for (int t = 0; t < PD - 1; ++t) {
+          ka[t] = *reinterpret_cast<const f16x8*>(kp + 16 * t);
+          qb[t] = *reinterpret_cast<const f16x8*>(qp + 16 * t);
         }
-        // D = gamma^(q - k) split as gamma^base gamma^-(8i + jj)
-        const int base = qi - k0 - sk * 32 - 4 * lh;
+        f32x16 S = {};
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          if (t + PD - 1 < NS) {
+            ka[(t + PD - 1) % PD] = *reinterpret_cast<const f16x8*>(kp + 16 * (t + PD - 1));
+            qb[(t + PD - 1) % PD] = *reinterpret_cast<const f16x8*>(qp + 16 * (t + PD - 1));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t % PD], qb[t % PD], S, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);      // keep the reads ahead of the multiplies
+        }
+        // D = gamma^(q - k) split as gamma^base gamma^-(8i + j), base = q - (first key of the lane)
+        const int base = r0 + sqh * 32 + l32 - k0 - sk * 32 - 4 * lh;
         const float gq = sm.rs[sqh * 32 + l32] * __builtin_amdgcn_exp2f((float)base * dec.lg2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float4 gi = *reinterpret_cast<const float4*>(sm.ginv + 8 * i);
           const float gv[4] = {gi.x, gi.y, gi.z, gi.w};
-          float pv[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float val = (base >= 8 * i + jj) ? S[4 * i + jj] * gq * gv[jj] : 0.f;
+          for (int j = 0; j < 4; ++j) {
+            const float val = (base >= 8 * i + j) ? S[4 * i + j] * gq * gv[j] : 0.f;
             den += val;
-            pv[jj] = val;
+            pv[4 * i + j] = val;
           }
-          st4(sm.Ps + (sqh * 32 + l32) * KP + sk * 32 + 8 * i + 4 * lh, pv);
         }
       } else {
-        const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st4(sm.Ps + (sqh * 32 + l32) * KP + sk * 32 + 8 * i + 4 * lh, zero4);
+        for (int i = 0; i < 16; ++i) pv[i] = 0.f;
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st4(sm.Ps + (sqh * 32 + l32) * KP + sk * 32 + 8 * i + 4 * lh, pv + 4 * i);
     }
     __syncthreads();
-    // O += P V
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      const int kend = (diag && qh == 0) ? 32 : TK;
-      for (int kb = 0; kb < kend; kb += 16) {
-        f16x8 a = *reinterpret_cast<const f16x8*>(sm.Ps + (qh * 32 + l32) * KP + kb + 8 * lh);
+    // O += P V: the value fragment of a column tile serves both query halves
+    // (rows 0..31 of P are zero against keys 32..63 of the diagonal tile);
+    // the fragments of step s + 1 are read while step s multiplies
+    {
+      f16x8 pa[2][2], bv[2][2];
+      auto load_pv = [&](int kb, int buf) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          f16x8 b = *reinterpret_cast<const f16x8*>(sm.u.kv.Vt + ((2 * wave + jj) * 32 + l32) * KP + kb + 8 * lh);
-          O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, O[qh][jj], 0, 0, 0);
+          // keys kb + 8 (lane / 32) + 0..7 of column (2w + jj) 32 + lane % 32
+          const half* vp = sm.u.kv.Vn + kb * VP + (2 * wave + jj) * 32 + vtr;
+          const f16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * VP);
+          bv[buf][jj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+          pa[buf][qh] = *reinterpret_cast<const f16x8*>(sm.Ps + (qh * 32 + l32) * KP + kb + 8 * lh);
+      };
+      load_pv(0, 0);
+#pragma unroll
+      for (int t = 0; t < TK / 16; ++t) {
+        if (t + 1 < TK / 16) load_pv(16 * (t + 1), (t + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[t & 1][qh], bv[t & 1][jj], O[qh][jj], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
   if (wave < 4) {
-    den += __shfl_xor(den, 32, 64);
+    den += __shfl_xor(den, 32, 64);               // lanes l and l + 32 hold the same query
     if (lh == 0) atomicAdd(&sm.dens[sqh * 32 + l32], den);
   }
   __syncthreads();

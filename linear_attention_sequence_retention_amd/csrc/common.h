@@ -16,6 +16,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;   // 16-byte raw piece (a native vector, so arrays of it stay in registers)
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef _Float16 half;
 
@@ -205,7 +206,6 @@ __device__ __forceinline__ void st4(float* p, const float* x) {
   *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
 }
 __device__ __forceinline__ void st4(half* p, const float* x) {
-  typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
   f16x4 v;
   v[0] = (half)x[0]; v[1] = (half)x[1]; v[2] = (half)x[2]; v[3] = (half)x[3];
   *reinterpret_cast<f16x4*>(p) = v;
