@@ -13,8 +13,10 @@ position 8192) and the GroupNorm + gate epilogue at the block shape.
 Prints ONE JSON line.  Only N = 1 GPU is supported.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,6 +27,34 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+# counter summary of the primary step and the sources its kernels are built from
+TRAFFIC_PROFILE = os.path.join("profiles", "chunkwise_medium_B512_traffic.md")
+TRAFFIC_SOURCES = [os.path.join("linear_attention_sequence_retention_amd", "csrc", f)
+                   for f in ("chunk3.hip", "common.h", "internal.h")]
+
+
+def sources_sha256(root=ROOT):
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(root=ROOT):
+    """HBM bytes per call of the primary step from the committed FETCH_SIZE /
+    WRITE_SIZE summary (copy-calibrated), or None when the kernel sources have
+    changed since the counters were taken."""
+    try:
+        with open(os.path.join(root, TRAFFIC_PROFILE)) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^(traffic_bytes_per_call|kernel_sources_sha256): (\S+)$", text, re.M))
+    if vals.get("kernel_sources_sha256") != sources_sha256(root) or "traffic_bytes_per_call" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_call"])
 
 
 def chunk_flops(b, h, L, dk, dv, B, with_state_out=False):
@@ -148,14 +178,18 @@ def main():
     intensity = flops / nbytes
     ridge = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     bound = "hbm" if intensity < ridge else "mfma"
+    traffic = profiled_traffic()
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "traffic": None}
+                "frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "traffic": traffic}
 
-    extra = {"primary": {"kernel": "chunkwise_kernel", "ms": round(ms, 4), "tflops": round(tflops, 1),
+    extra = {"primary": {"kernel": "retention_chunkwise_fwd (delta, scan, output kernels)",
+                         "arithmetic": "bf16 in and out, fp16 MFMA operands, fp32 accumulate",
+                         "traffic_x_compulsory": None if traffic is None else round(traffic / nbytes, 2),
+                         "ms": round(ms, 4), "tflops": round(tflops, 1),
                          "mfma_frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "gbs": round(gbs, 1),
                          "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "alg_gflop": round(flops / 1e9, 2),
                          "alg_mb": round(nbytes / 1e6, 1), "wall_s": round(wall, 3)}}
@@ -261,7 +295,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in/out, fp16 MFMA operands, fp32 accumulate",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "chunkwise_fwd " + W.workload_name(cfg, B) + " xpos+all_norms",
                    "global_batch": b, "seq_len": L, "heads": h, "d_k": dk, "d_v": dv, "chunk": B,
