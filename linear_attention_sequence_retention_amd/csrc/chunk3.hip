@@ -16,7 +16,7 @@
 // Every key and value element is rotated / converted once by the delta
 // kernel (the output kernel reads the rotated fp16 keys), and no work is
 // repeated across d_v slices.  Operands are fp16 with fp32 accumulation.
-// Shapes: d_k = 256, d_v = 512, chunk B a multiple of 64 and >= 128.
+// Shapes: d_k = 256, d_v = 512, chunk B a multiple of 64.
 #include "internal.h"
 
 namespace ret {
@@ -733,7 +733,7 @@ hipError_t run_o(const ChunkArgs& a, hipStream_t st) {
 }  // namespace
 
 bool three_phase_applies(ret_dtype in_dt, int dk, int dv, int B) {
-  return (in_dt == RET_BF16 || in_dt == RET_F16) && dk == DK && dv == DV && B >= 128 && B % 64 == 0;
+  return (in_dt == RET_BF16 || in_dt == RET_F16) && dk == DK && dv == DV && B >= 64 && B % 64 == 0;
 }
 
 size_t three_phase_workspace(int b, int h, int L, int B) {
