@@ -84,9 +84,16 @@ template <> struct Raw32<half> {
   }
 };
 
-// eight consecutive 16-bit inputs -> fp16 (the MFMA operand type)
+// eight consecutive 16-bit inputs -> float (exact) or fp16 (the MFMA operand type)
 template <typename T> struct Raw16;
 template <> struct Raw16<bf16> {
+  __device__ __forceinline__ static void f32(u32x4 u, float* x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = lo_bf(u[i]);
+      x[2 * i + 1] = hi_bf(u[i]);
+    }
+  }
   __device__ __forceinline__ static u32x4 f16(u32x4 u) {
     f16x8 h;
 #pragma unroll
@@ -98,6 +105,11 @@ template <> struct Raw16<bf16> {
   }
 };
 template <> struct Raw16<half> {
+  __device__ __forceinline__ static void f32(u32x4 u, float* x) {
+    const f16x8 h = __builtin_bit_cast(f16x8, u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
+  }
   __device__ __forceinline__ static u32x4 f16(u32x4 u) { return u; }
 };
 
@@ -147,10 +159,15 @@ __device__ __forceinline__ int scale_exp(float amax) {
 }
 
 // ---------------------------------------------------------------- delta
+// natural-layout fp16 tiles ([key][d] and [key][col]); both MFMA operands
+// (k = key) are read with the transposed LDS read.  Row pitch 576 bytes: the
+// four key rows of one transposed read start 64 bytes apart in the bank space.
+constexpr int DP = 256 + 32;
 struct DeltaSmem {
-  half KT[DK * KP];     // zeta-scaled K'^T tile: [d][key]
-  half VT[256 * KP];    // V^T tile of this d_v half: [col][key]
-  float red[NT3 / 64];
+  half Kz[TK * DP];     // zeta-scaled rotated keys [key][d]
+  half Vh[TK * DP];     // this half of the value tile [key][col]
+  float dzs[DK];
+  float4 step[DK / 2];  // per pair: e^{i theta} and e^{i TK theta} as (c1, s1, cT, sT)
 };
 
 template <typename T>
@@ -158,7 +175,6 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   DeltaSmem& sm = *reinterpret_cast<DeltaSmem*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lh = lane >> 5, l32 = lane & 31;
   const int g = xcd_local(blockIdx.x, gridDim.x);
   const int half_ = g & 1;
   const int c = (g >> 1) % p.nc;
@@ -181,94 +197,122 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  float dz = 0.f;   // d = tid (tid < DK) of the key-sum delta, half 0 only
 
-  const int j = tid & 127, grp = tid >> 7;   // xPos pair / column pair, 16-key group
+  // thread -> 16-byte piece cq (d or columns 8 cq .. 8 cq + 7) of keys
+  // 4 (tid / 32) + 0..3 of every tile
+  const int cq = tid & 31, kq = 4 * (tid >> 5);
+  float dzp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // key-sum of d 8 cq .. +7
+  // xPos phase of this thread's first key in the current tile for its four
+  // pairs, the one-key and the one-tile steps
+  float pc[4], ps[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    pc[u] = 1.f;
+    ps[u] = 0.f;
+    if (xpos) phase(p.pos0 + c0 + kq, hp.theta[4 * cq + u], pc[u], ps[u]);
+  }
+  if (xpos && tid < DK / 2) {
+    float4 t;
+    phase(1, hp.theta[tid], t.x, t.y);
+    phase(TK, hp.theta[tid], t.z, t.w);
+    sm.step[tid] = t;
+  }
+  __syncthreads();
+
   const int nkt = (Bc + TK - 1) / TK;
-  // raw key / value pairs of the next tile, loaded while the current one is
-  // multiplied
-  uint32_t kr[16], vr[16];
+  u32x4 kr[4], vr[4];
   auto issue = [&](int kt) {
     const int k0 = kt * TK;
     const int kvalid = min(TK, Bc - k0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kc = min(grp * 16 + i, kvalid - 1);
-      kr[i] = *reinterpret_cast<const uint32_t*>(Kg + (uint32_t)((k0 + kc) * (int)p.sk.l + 2 * j));
-      vr[i] = *reinterpret_cast<const uint32_t*>(Vg + (uint32_t)((k0 + kc) * (int)p.sv.l + 2 * j));
+    for (int i = 0; i < 4; ++i) {
+      const int kc = min(kq + i, kvalid - 1);
+      kr[i] = *reinterpret_cast<const u32x4*>(Kg + (uint32_t)((k0 + kc) * (int)p.sk.l + 8 * cq));
+      vr[i] = *reinterpret_cast<const u32x4*>(Vg + (uint32_t)((k0 + kc) * (int)p.sv.l + 8 * cq));
     }
   };
+  // transposed-read origin of this lane (see lds_read_tr16): key 8 (lane / 32)
+  // + (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
+  const int tro = (8 * (lane >> 5) + ((lane & 15) >> 2)) * DP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   issue(0);
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * TK;
     const int kvalid = min(TK, Bc - k0);
-    // ---- rotated, zeta-scaled keys -> KT (and the rotated keys -> workspace)
-    {
-      float a[16], b[16];
+    // ---- rotate the keys (-> workspace), scale by zeta (-> LDS, key-sum);
+    // convert the values (-> LDS)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = grp * 16 + i;
-        float2 x = Raw32<T>::f(kr[i]);
-        a[i] = key < kvalid ? x.x : 0.f;
-        b[i] = key < kvalid ? x.y : 0.f;
-      }
-      float cs = 1.f, sn = 0.f, c1 = 1.f, s1 = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int key = kq + i;
+      const bool ok = key < kvalid;
+      float x[8];
+      Raw16<T>::f32(kr[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = ok ? x[e] : 0.f;
       if (xpos) {
-        phase(p.pos0 + c0 + k0 + grp * 16, hp.theta[j], cs, sn);
-        phase(1, hp.theta[j], c1, s1);
-      }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (xpos) {
-          rot(a[i], b[i], cs, sn);
-          advance(cs, sn, c1, s1);
+        for (int u = 0; u < 4; ++u) {
+          const float4 t1 = sm.step[4 * cq + u];
+          float cs = pc[u], sn = ps[u];
+          for (int t = 0; t < i; ++t) advance(cs, sn, t1.x, t1.y);
+          rot(x[2 * u], x[2 * u + 1], cs, sn);
         }
-        const int key = grp * 16 + i;
-        if (half_ == 0 && key < kvalid) st2(ktg + (int64_t)(k0 + key) * DK + 2 * j, a[i], b[i]);
-        const float z = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key) * dec.lg2);
-        a[i] *= z;
-        b[i] *= z;
       }
-      st8(sm.KT + (2 * j) * KP + grp * 16, a);
-      st8(sm.KT + (2 * j) * KP + grp * 16 + 8, a + 8);
-      st8(sm.KT + (2 * j + 1) * KP + grp * 16, b);
-      st8(sm.KT + (2 * j + 1) * KP + grp * 16 + 8, b + 8);
-    }
-    // ---- V^T of this half's 256 columns
-    {
-      float a[16], b[16];
+      if (half_ == 0 && ok) st8(ktg + (int64_t)(k0 + key) * DK + 8 * cq, x);
+      const float z = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key) * dec.lg2);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = grp * 16 + i;
-        float2 x = Raw32<T>::f(vr[i]);
-        a[i] = key < kvalid ? x.x : 0.f;
-        b[i] = key < kvalid ? x.y : 0.f;
+      for (int e = 0; e < 8; ++e) {
+        x[e] *= z;
+        dzp[e] += x[e];
       }
-      st8(sm.VT + (2 * j) * KP + grp * 16, a);
-      st8(sm.VT + (2 * j) * KP + grp * 16 + 8, a + 8);
-      st8(sm.VT + (2 * j + 1) * KP + grp * 16, b);
-      st8(sm.VT + (2 * j + 1) * KP + grp * 16 + 8, b + 8);
+      st8(sm.Kz + key * DP + 8 * cq, x);
+      u32x4 v = Raw16<T>::f16(vr[i]);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sm.Vh + key * DP + 8 * cq) = v;
+    }
+    if (xpos) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 t1 = sm.step[4 * cq + u];
+        advance(pc[u], ps[u], t1.z, t1.w);
+      }
     }
     if (kt + 1 < nkt) issue(kt + 1);
     __syncthreads();
-    if (half_ == 0 && tid < DK) {
-      float s = 0.f;
-      for (int key = 0; key < TK; ++key) s += (float)sm.KT[tid * KP + key];
-      dz += s;
-    }
-#pragma unroll 2
+#pragma unroll
     for (int kb = 0; kb < TK; kb += 16) {
       f16x8 af[2], bf[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const f16x8*>(sm.KT + (d0 + 32 * i + l32) * KP + kb + 8 * lh);
+      for (int i = 0; i < 2; ++i) {
+        const half* ap = sm.Kz + kb * DP + d0 + 32 * i + tro;
+        const f16x4 lo = lds_read_tr16(ap), hi = lds_read_tr16(ap + 4 * DP);
+        af[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) bf[jj] = *reinterpret_cast<const f16x8*>(sm.VT + (n0 + 32 * jj + l32) * KP + kb + 8 * lh);
+      for (int jj = 0; jj < 4; ++jj) {
+        const half* bp = sm.Vh + kb * DP + n0 + 32 * jj + tro;
+        const f16x4 lo = lds_read_tr16(bp), hi = lds_read_tr16(bp + 4 * DP);
+        bf[jj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[jj], acc[i][jj], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
+  }
+
+  // ---- key-sum delta: lanes l and l + 32 share a piece; then the 8 waves
+  if (half_ == 0) {
+    if (tid < DK) sm.dzs[tid] = 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dzp[e] += __shfl_xor(dzp[e], 32, 64);
+    if (lane < 32) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) atomicAdd(&sm.dzs[8 * cq + e], dzp[e]);
+    }
   }
 
   // ---- store dR (scaled fp16, [col][d]) and its scale, dz
@@ -279,7 +323,7 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[i][jj][r]));
-  amax = maxabs_block(amax, sm.red);
+  amax = maxabs_block(amax, reinterpret_cast<float*>(sm.Kz));
   const int e = scale_exp(amax);
   const float down = ldexpf(1.f, -e);
   half* dR = p.w.dR + ((int64_t)bh * p.nc + c) * DV * DK;
@@ -287,17 +331,17 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int col = half_ * 256 + n0 + 32 * jj + l32;
+      const int col = half_ * 256 + n0 + 32 * jj + (lane & 31);
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int d = d0 + 32 * i + 8 * rg + 4 * lh;   // acc rows 4*rg .. 4*rg+3 are d .. d+3
+        const int d = d0 + 32 * i + 8 * rg + 4 * (lane >> 5);   // acc rows 4*rg .. 4*rg+3 are d .. d+3
         float x[4] = {acc[i][jj][4 * rg] * down, acc[i][jj][4 * rg + 1] * down, acc[i][jj][4 * rg + 2] * down,
                       acc[i][jj][4 * rg + 3] * down};
         st4(dR + (int64_t)col * DK + d, x);
       }
     }
   if (tid == 0) p.w.dRs[((int64_t)bh * p.nc + c) * 2 + half_] = ldexpf(1.f, e);
-  if (half_ == 0 && tid < DK) p.w.dz[((int64_t)bh * p.nc + c) * DK + tid] = dz;
+  if (half_ == 0 && tid < DK) p.w.dz[((int64_t)bh * p.nc + c) * DK + tid] = sm.dzs[tid];
 }
 
 // ---------------------------------------------------------------- scan
