@@ -127,6 +127,7 @@ struct P3 {
   void* o;
   ret_strides sq, sk, sv, so;
   int h, L, B, nc, nrt;
+  int nbh;          // b * h
   int64_t pos0, n_prev;
   unsigned flags;
   const float *state_in, *z_in;
@@ -434,306 +435,343 @@ struct OutSmem {
 template <typename T, typename TO>
 __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  OutSmem& sm = *reinterpret_cast<OutSmem*>(smem_raw);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lh = lane >> 5, l32 = lane & 31;
-  const int g = xcd_local(blockIdx.x, gridDim.x);
-  const int rt = p.nrt - 1 - (g % p.nrt);         // heavier query tiles first
-  const int c = (g / p.nrt) % p.nc;
-  const int bh = (g / p.nrt) / p.nc;
-  const int bb = bh / p.h, head = bh % p.h;
-  const int c0 = c * p.B;
-  const int Bc = min(p.B, p.L - c0);
-  const int r0 = rt * TR;
-  if (r0 >= Bc) return;                           // ragged last chunk
-  const int qvalid = min(TR, Bc - r0);
-  Decay dec;
-  dec.init(hp.gamma[head]);
-  const bool xpos = (p.flags & RET_XPOS) != 0;
-  const float qk_scale = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
+  // Persistent schedule: one workgroup per CU walks a static list of units.
+  // A unit is the pair of query tiles (rt, nrt - 1 - rt) of one (head, chunk),
+  // so every unit costs about the same; the units of a chunk go to the
+  // workgroups of one XCD (workgroup i runs on XCD i mod 8) and run side by
+  // side there, sharing the chunk's keys, values and state in that L2.
+  const int NX = min(8, (int)gridDim.x);
+  const int xw = blockIdx.x % NX, jw = blockIdx.x / NX;
+  const int wx = ((int)gridDim.x - xw + NX - 1) / NX;      // workgroups of this XCD
+  const int ngroups = p.nbh * p.nc;
+  const int gx = (ngroups - xw + NX - 1) / NX;             // (head, chunk) groups of this XCD
+  const int U = (p.nrt + 1) / 2;
+  const int nk = 2 * ((gx * U - jw + wx - 1) / wx);
+  for (int k = 0; k < nk; ++k) {
+    const int un = jw + wx * (k >> 1), pi = k & 1;         // unit, and which of its two tiles
+    const int uu = un % U;
+    if (pi == 1 && uu == p.nrt - 1 - uu) continue;         // middle tile of an odd count
+    const int rt = pi == 0 ? p.nrt - 1 - uu : uu;          // heavier tile first
+    const int grp = xw + NX * (un / U);
+    const int c = grp % p.nc, bh = grp / p.nc;
+    if (rt * TR >= min(p.B, p.L - c * p.B)) continue;      // ragged last chunk
+    __syncthreads();                                       // the previous item's LDS reads are done
+    {
+    OutSmem& sm = *reinterpret_cast<OutSmem*>(smem_raw);
+    // the thread index passes through an empty asm each item, so per-lane
+    // addressing is recomputed inside the item rather than hoisted out of the
+    // persistent loop (where it would stay live across the whole item)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lh = lane >> 5, l32 = lane & 31;
+    const int bb = bh / p.h, head = bh % p.h;
+    const int c0 = c * p.B;
+    const int Bc = min(p.B, p.L - c0);
+    const int r0 = rt * TR;
+    const int qvalid = min(TR, Bc - r0);
+    Decay dec;
+    dec.init(hp.gamma[head]);
+    const bool xpos = (p.flags & RET_XPOS) != 0;
+    const float qk_scale = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
 
-  const T* Qg = reinterpret_cast<const T*>(p.q) + bb * p.sq.b + head * p.sq.h + (int64_t)(c0 + r0) * p.sq.l;
-  const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + (int64_t)c0 * p.sv.l;
-  const half* Kt = p.w.kt + ((int64_t)bh * p.L + c0) * DK;
-  TO* Og = reinterpret_cast<TO*>(p.o) + bb * p.so.b + head * p.so.h + (int64_t)(c0 + r0) * p.so.l;
+    const T* Qg = reinterpret_cast<const T*>(p.q) + bb * p.sq.b + head * p.sq.h + (int64_t)(c0 + r0) * p.sq.l;
+    const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + (int64_t)c0 * p.sv.l;
+    const half* Kt = p.w.kt + ((int64_t)bh * p.L + c0) * DK;
+    TO* Og = reinterpret_cast<TO*>(p.o) + bb * p.so.b + head * p.so.h + (int64_t)(c0 + r0) * p.so.l;
 
-  // ---- rotated query tile, row tables
-  {
-    const int j = tid & 127, grp = tid >> 7;      // 16 rows per group
-    float a[16], b[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = grp * 16 + i;
-      const int rc = min(row, qvalid - 1);
-      float2 x = Elem<T>::ld2(Qg + (uint32_t)(rc * (int)p.sq.l + 2 * j));
-      a[i] = row < qvalid ? x.x : 0.f;
-      b[i] = row < qvalid ? x.y : 0.f;
-    }
-    float cs = 1.f, sn = 0.f, c1 = 1.f, s1 = 0.f;
-    if (xpos) {
-      phase(p.pos0 + c0 + r0 + grp * 16, hp.theta[j], cs, sn);
-      phase(1, hp.theta[j], c1, s1);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (xpos) {
-        rot(a[i], b[i], cs, sn);
-        advance(cs, sn, c1, s1);
+    // ---- rotated query tile, row tables
+    {
+      const int j = tid & 127, grp = tid >> 7;      // 16 rows per group
+      float a[16], b[16];
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = grp * 16 + i;
+        const int rc = min(row, qvalid - 1);
+        float2 x = Elem<T>::ld2(Qg + (uint32_t)(rc * (int)p.sq.l + 2 * j));
+        a[i] = row < qvalid ? x.x : 0.f;
+        b[i] = row < qvalid ? x.y : 0.f;
       }
-      st2(sm.Qs + (grp * 16 + i) * QP + 2 * j, a[i], b[i]);
+      float cs = 1.f, sn = 0.f, c1 = 1.f, s1 = 0.f;
+      if (xpos) {
+        phase(p.pos0 + c0 + r0 + grp * 16, hp.theta[j], cs, sn);
+        phase(1, hp.theta[j], c1, s1);
+      }
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (xpos) {
+          rot(a[i], b[i], cs, sn);
+          advance(cs, sn, c1, s1);
+        }
+        st2(sm.Qs + (grp * 16 + i) * QP + 2 * j, a[i], b[i]);
+      }
+      if (tid < TR) {
+        float s = qk_scale;
+        if (p.flags & RET_NORM_DROW) s *= dec.drow((float)(p.n_prev + c0 + r0 + tid + 1));
+        sm.rs[tid] = s;
+        sm.xs[tid] = s * dec.pow((float)(r0 + tid + 1));
+        sm.dens[tid] = 0.f;
+      }
+      if (tid < DK) sm.zs[tid] = p.w.zc[((int64_t)bh * p.nc + c) * DK + tid];
+      if (tid < 32) sm.ginv[tid] = __builtin_amdgcn_exp2f(-(float)tid * dec.lg2);
     }
-    if (tid < TR) {
-      float s = qk_scale;
-      if (p.flags & RET_NORM_DROW) s *= dec.drow((float)(p.n_prev + c0 + r0 + tid + 1));
-      sm.rs[tid] = s;
-      sm.xs[tid] = s * dec.pow((float)(r0 + tid + 1));
-      sm.dens[tid] = 0.f;
-    }
-    if (tid < DK) sm.zs[tid] = p.w.zc[((int64_t)bh * p.nc + c) * DK + tid];
-    if (tid < 32) sm.ginv[tid] = __builtin_amdgcn_exp2f(-(float)tid * dec.lg2);
-  }
 
-  // ---- staged key / value tile registers
-  u32x4 kreg[4];          // 64 keys x 256 d fp16: 2048 16-byte pieces, 4 per thread
-  u32x4 vreg[8];          // 64 keys x 512 columns: 4096 16-byte pieces, 8 per thread
-  auto issue = [&](int kt) {
-    const int k0 = kt * TK;
-    const int kvalid = min(TK, Bc - k0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + i * NT3;
-      const int key = min(e >> 5, kvalid - 1), piece = e & 31;
-      kreg[i] = *reinterpret_cast<const u32x4*>(Kt + (int64_t)(k0 + key) * DK + piece * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = tid + i * NT3;
-      const int key = min(e >> 6, kvalid - 1), piece = e & 63;
-      vreg[i] = *reinterpret_cast<const u32x4*>(Vg + (uint32_t)((k0 + key) * (int)p.sv.l + piece * 8));
-    }
-  };
-  auto commit = [&](int kt) {
-    const int kvalid = min(TK, Bc - kt * TK);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + i * NT3;
-      const int key = e >> 5, piece = e & 31;
-      u32x4 v = kreg[i];
-      if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(sm.u.kv.Ks + key * QP + piece * 8) = v;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = tid + i * NT3;
-      const int key = e >> 6, piece = e & 63;
-      u32x4 v = Raw16<T>::f16(vreg[i]);
-      if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(sm.u.kv.Vn + key * VP + piece * 8) = v;
-    }
-  };
-  // this lane's transposed-read origin in a value tile: key 8 (lane / 32) +
-  // (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
-  const int vtr = (8 * (lane >> 5) + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  // output tiles of this wave: query halves {0,1} x column tiles {2w, 2w+1}
-  f32x16 O[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) O[i][jj] = f32x16{};
-
-  // ---- cross-chunk term Q' R_{c-1}, one 64-wide d-slice of the state
-  // operand at a time; the next slice (after the last: the first key / value
-  // tile) is loaded into registers while the current one is multiplied
-  const half* Rg = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK;
-  {
-    u32x4 rreg[8];        // 512 columns x 64 d fp16: 4096 16-byte pieces, 8 per thread
-    auto issue_r = [&](int ds) {
-#pragma unroll
+    // ---- staged key / value tile registers
+    u32x4 kreg[4];          // 64 keys x 256 d fp16: 2048 16-byte pieces, 4 per thread
+    u32x4 vreg[8];          // 64 keys x 512 columns: 4096 16-byte pieces, 8 per thread
+    auto issue = [&](int kt) {
+      const int k0 = kt * TK;
+      const int kvalid = min(TK, Bc - k0);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tid + i * NT3;
+        const int key = min(e >> 5, kvalid - 1), piece = e & 31;
+        kreg[i] = *reinterpret_cast<const u32x4*>(Kt + (int64_t)(k0 + key) * DK + piece * 8);
+      }
+  #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int e = tid + i * NT3;
-        rreg[i] = *reinterpret_cast<const u32x4*>(Rg + (int64_t)(e >> 3) * DK + ds + (e & 7) * 8);
+        const int key = min(e >> 6, kvalid - 1), piece = e & 63;
+        vreg[i] = *reinterpret_cast<const u32x4*>(Vg + (uint32_t)((k0 + key) * (int)p.sv.l + piece * 8));
       }
     };
-    issue_r(0);
-    for (int ds = 0; ds < DK; ds += 64) {
-      __syncthreads();
-#pragma unroll
+    auto commit = [&](int kt) {
+      const int kvalid = min(TK, Bc - kt * TK);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tid + i * NT3;
+        const int key = e >> 5, piece = e & 31;
+        u32x4 v = kreg[i];
+        if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(sm.u.kv.Ks + key * QP + piece * 8) = v;
+      }
+  #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int e = tid + i * NT3;
-        *reinterpret_cast<u32x4*>(sm.u.Rt + (e >> 3) * KP + (e & 7) * 8) = rreg[i];
+        const int key = e >> 6, piece = e & 63;
+        u32x4 v = Raw16<T>::f16(vreg[i]);
+        if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(sm.u.kv.Vn + key * VP + piece * 8) = v;
+      }
+    };
+    // this lane's transposed-read origin in a value tile: key 8 (lane / 32) +
+    // (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
+    const int vtr = (8 * (lane >> 5) + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    // output tiles of this wave: query halves {0,1} x column tiles {2w, 2w+1}
+    f32x16 O[2][2];
+  #pragma unroll
+    for (int i = 0; i < 2; ++i)
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) O[i][jj] = f32x16{};
+
+    // ---- cross-chunk term Q' R_{c-1}, one 64-wide d-slice of the state
+    // operand at a time; the next slice (after the last: the first key / value
+    // tile) is loaded into registers while the current one is multiplied
+    const half* Rg = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK;
+    {
+      u32x4 rreg[8];        // 512 columns x 64 d fp16: 4096 16-byte pieces, 8 per thread
+      auto issue_r = [&](int ds) {
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = tid + i * NT3;
+          rreg[i] = *reinterpret_cast<const u32x4*>(Rg + (int64_t)(e >> 3) * DK + ds + (e & 7) * 8);
+        }
+      };
+      issue_r(0);
+      for (int ds = 0; ds < DK; ds += 64) {
+        __syncthreads();
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = tid + i * NT3;
+          *reinterpret_cast<u32x4*>(sm.u.Rt + (e >> 3) * KP + (e & 7) * 8) = rreg[i];
+        }
+        __syncthreads();
+        if (ds + 64 < DK) issue_r(ds + 64);
+        else issue(rt);
+        f16x8 qa[2][2], rb[2][2];
+        auto load_x = [&](int kb, int buf) {
+  #pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            qa[buf][i] = *reinterpret_cast<const f16x8*>(sm.Qs + (i * 32 + l32) * QP + ds + kb + 8 * lh);
+            rb[buf][i] = *reinterpret_cast<const f16x8*>(sm.u.Rt + ((2 * wave + i) * 32 + l32) * KP + kb + 8 * lh);
+          }
+        };
+        load_x(0, 0);
+  #pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t + 1 < 4) load_x(16 * (t + 1), (t + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int qh = 0; qh < 2; ++qh)
+  #pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+              O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t & 1][qh], rb[t & 1][jj], O[qh][jj], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    {
+      // row scale s xi and the operand's per-block power of two
+      const float* Rs = p.w.Rs + ((int64_t)bh * p.nc + c) * NCB;
+      const float up0 = Rs[2 * wave], up1 = Rs[2 * wave + 1];
+  #pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = sm.xs[qh * 32 + acc_row(r, lane)];
+          O[qh][0][r] *= x * up0;
+          O[qh][1][r] *= x * up1;
+        }
+      // cross part of the score denominator, s xi (Q' . z_{c-1}): 8 threads per row
+      const int row = tid >> 3, part = tid & 7;
+      float acc = 0.f;
+      for (int d = part; d < DK; d += 8) acc += (float)sm.Qs[row * QP + d] * sm.zs[d];
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      acc += __shfl_xor(acc, 4, 64);
+      if (part == 0) sm.dens[row] = sm.xs[row] * acc;
+    }
+
+    // ---- within-chunk term, diagonal key tile first
+    // waves 0..3 form S^T = K' Q'^T as 32 x 32 tiles (keys 32 (w / 2) .., queries
+    // 32 (w % 2) ..) and write P; all eight waves then accumulate P V
+    float den = 0.f;
+    const int sk = wave >> 1, sqh = wave & 1;
+    for (int idx = 0; idx <= rt; ++idx) {
+      const int kt = (idx == 0) ? rt : idx - 1;
+      const bool diag = (idx == 0);
+      const int k0 = kt * TK;
+      __syncthreads();
+      commit(kt);
+      if (idx < rt) issue(idx);                     // next: kt = idx
+      __syncthreads();
+      if (wave < 4) {
+        const bool skip = diag && sk > sqh;         // keys 32..63 vs queries 0..31 of the diagonal
+        float pv[16];
+        if (!skip) {
+          // fragments of step s + 3 are read while step s multiplies
+          const half* kp = sm.u.kv.Ks + (sk * 32 + l32) * QP + 8 * lh;
+          const half* qp = sm.Qs + (sqh * 32 + l32) * QP + 8 * lh;
+          constexpr int NS = DK / 16, PD = 4;
+          f16x8 ka[PD], qb[PD];
+  #pragma unroll
+          for (int t = 0; t < PD - 1; ++t) {
+            ka[t] = *reinterpret_cast<const f16x8*>(kp + 16 * t);
+            qb[t] = *reinterpret_cast<const f16x8*>(qp + 16 * t);
+          }
+          f32x16 S = {};
+  #pragma unroll
+          for (int t = 0; t < NS; ++t) {
+            if (t + PD - 1 < NS) {
+              ka[(t + PD - 1) % PD] = *reinterpret_cast<const f16x8*>(kp + 16 * (t + PD - 1));
+              qb[(t + PD - 1) % PD] = *reinterpret_cast<const f16x8*>(qp + 16 * (t + PD - 1));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t % PD], qb[t % PD], S, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);      // keep the reads ahead of the multiplies
+          }
+          // D = gamma^(q - k) split as gamma^base gamma^-(8i + j), base = q - (first key of the lane)
+          const int base = r0 + sqh * 32 + l32 - k0 - sk * 32 - 4 * lh;
+          const float gq = sm.rs[sqh * 32 + l32] * __builtin_amdgcn_exp2f((float)base * dec.lg2);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float4 gi = *reinterpret_cast<const float4*>(sm.ginv + 8 * i);
+            const float gv[4] = {gi.x, gi.y, gi.z, gi.w};
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float val = (base >= 8 * i + j) ? S[4 * i + j] * gq * gv[j] : 0.f;
+              den += val;
+              pv[4 * i + j] = val;
+            }
+          }
+        } else {
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) pv[i] = 0.f;
+        }
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) st4(sm.Ps + (sqh * 32 + l32) * KP + sk * 32 + 8 * i + 4 * lh, pv + 4 * i);
       }
       __syncthreads();
-      if (ds + 64 < DK) issue_r(ds + 64);
-      else issue(rt);
-      f16x8 qa[2][2], rb[2][2];
-      auto load_x = [&](int kb, int buf) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          qa[buf][i] = *reinterpret_cast<const f16x8*>(sm.Qs + (i * 32 + l32) * QP + ds + kb + 8 * lh);
-          rb[buf][i] = *reinterpret_cast<const f16x8*>(sm.u.Rt + ((2 * wave + i) * 32 + l32) * KP + kb + 8 * lh);
-        }
-      };
-      load_x(0, 0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (t + 1 < 4) load_x(16 * (t + 1), (t + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t & 1][qh], rb[t & 1][jj], O[qh][jj], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  {
-    // row scale s xi and the operand's per-block power of two
-    const float* Rs = p.w.Rs + ((int64_t)bh * p.nc + c) * NCB;
-    const float up0 = Rs[2 * wave], up1 = Rs[2 * wave + 1];
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = sm.xs[qh * 32 + acc_row(r, lane)];
-        O[qh][0][r] *= x * up0;
-        O[qh][1][r] *= x * up1;
-      }
-    // cross part of the score denominator, s xi (Q' . z_{c-1}): 8 threads per row
-    const int row = tid >> 3, part = tid & 7;
-    float acc = 0.f;
-    for (int d = part; d < DK; d += 8) acc += (float)sm.Qs[row * QP + d] * sm.zs[d];
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    if (part == 0) sm.dens[row] = sm.xs[row] * acc;
-  }
-
-  // ---- within-chunk term, diagonal key tile first
-  // waves 0..3 form S^T = K' Q'^T as 32 x 32 tiles (keys 32 (w / 2) .., queries
-  // 32 (w % 2) ..) and write P; all eight waves then accumulate P V
-  float den = 0.f;
-  const int sk = wave >> 1, sqh = wave & 1;
-  for (int idx = 0; idx <= rt; ++idx) {
-    const int kt = (idx == 0) ? rt : idx - 1;
-    const bool diag = (idx == 0);
-    const int k0 = kt * TK;
-    __syncthreads();
-    commit(kt);
-    if (idx < rt) issue(idx);                     // next: kt = idx
-    __syncthreads();
-    if (wave < 4) {
-      const bool skip = diag && sk > sqh;         // keys 32..63 vs queries 0..31 of the diagonal
-      float pv[16];
-      if (!skip) {
-        // fragments of step s + 3 are read while step s multiplies
-        const half* kp = sm.u.kv.Ks + (sk * 32 + l32) * QP + 8 * lh;
-        const half* qp = sm.Qs + (sqh * 32 + l32) * QP + 8 * lh;
-        constexpr int NS = DK / 16, PD = 4;
-        f16x8 ka[PD], qb[PD];
-#pragma unroll
-        for (int t = 0; t < PD - 1; ++t) {
-          ka[t] = *reinterpret_cast<const f16x8*>(kp + 16 * t);
-          qb[t] = *reinterpret_cast<const f16x8*>(qp + 16 * t);
-        }
-        f32x16 S = {};
-#pragma unroll
-        for (int t = 0; t < NS; ++t) {
-          if (t + PD - 1 < NS) {
-            ka[(t + PD - 1) % PD] = *reinterpret_cast<const f16x8*>(kp + 16 * (t + PD - 1));
-            qb[(t + PD - 1) % PD] = *reinterpret_cast<const f16x8*>(qp + 16 * (t + PD - 1));
+      // O += P V: the value fragment of a column tile serves both query halves
+      // (rows 0..31 of P are zero against keys 32..63 of the diagonal tile);
+      // the fragments of step s + 1 are read while step s multiplies
+      {
+        f16x8 pa[2][2], bv[2][2];
+        auto load_pv = [&](int kb, int buf) {
+  #pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            // keys kb + 8 (lane / 32) + 0..7 of column (2w + jj) 32 + lane % 32
+            const half* vp = sm.u.kv.Vn + kb * VP + (2 * wave + jj) * 32 + vtr;
+            const f16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * VP);
+            bv[buf][jj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           }
+  #pragma unroll
+          for (int qh = 0; qh < 2; ++qh)
+            pa[buf][qh] = *reinterpret_cast<const f16x8*>(sm.Ps + (qh * 32 + l32) * KP + kb + 8 * lh);
+        };
+        load_pv(0, 0);
+  #pragma unroll
+        for (int t = 0; t < TK / 16; ++t) {
+          if (t + 1 < TK / 16) load_pv(16 * (t + 1), (t + 1) & 1);
           __builtin_amdgcn_sched_barrier(0);
-          S = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t % PD], qb[t % PD], S, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);      // keep the reads ahead of the multiplies
+  #pragma unroll
+          for (int qh = 0; qh < 2; ++qh)
+  #pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+              O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[t & 1][qh], bv[t & 1][jj], O[qh][jj], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // D = gamma^(q - k) split as gamma^base gamma^-(8i + j), base = q - (first key of the lane)
-        const int base = r0 + sqh * 32 + l32 - k0 - sk * 32 - 4 * lh;
-        const float gq = sm.rs[sqh * 32 + l32] * __builtin_amdgcn_exp2f((float)base * dec.lg2);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 gi = *reinterpret_cast<const float4*>(sm.ginv + 8 * i);
-          const float gv[4] = {gi.x, gi.y, gi.z, gi.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float val = (base >= 8 * i + j) ? S[4 * i + j] * gq * gv[j] : 0.f;
-            den += val;
-            pv[4 * i + j] = val;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pv[i] = 0.f;
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st4(sm.Ps + (sqh * 32 + l32) * KP + sk * 32 + 8 * i + 4 * lh, pv + 4 * i);
+    }
+    if (wave < 4) {
+      den += __shfl_xor(den, 32, 64);               // lanes l and l + 32 hold the same query
+      if (lh == 0) atomicAdd(&sm.dens[sqh * 32 + l32], den);
     }
     __syncthreads();
-    // O += P V: the value fragment of a column tile serves both query halves
-    // (rows 0..31 of P are zero against keys 32..63 of the diagonal tile);
-    // the fragments of step s + 1 are read while step s multiplies
-    {
-      f16x8 pa[2][2], bv[2][2];
-      auto load_pv = [&](int kb, int buf) {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          // keys kb + 8 (lane / 32) + 0..7 of column (2w + jj) 32 + lane % 32
-          const half* vp = sm.u.kv.Vn + kb * VP + (2 * wave + jj) * 32 + vtr;
-          const f16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * VP);
-          bv[buf][jj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int qh = 0; qh < 2; ++qh)
-          pa[buf][qh] = *reinterpret_cast<const f16x8*>(sm.Ps + (qh * 32 + l32) * KP + kb + 8 * lh);
-      };
-      load_pv(0, 0);
-#pragma unroll
-      for (int t = 0; t < TK / 16; ++t) {
-        if (t + 1 < TK / 16) load_pv(16 * (t + 1), (t + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[t & 1][qh], bv[t & 1][jj], O[qh][jj], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  if (wave < 4) {
-    den += __shfl_xor(den, 32, 64);               // lanes l and l + 32 hold the same query
-    if (lh == 0) atomicAdd(&sm.dens[sqh * 32 + l32], den);
-  }
-  __syncthreads();
-  if (tid < TR) sm.rs[tid] = (p.flags & RET_NORM_SCORE) ? 1.f / fmaxf(fabsf(sm.dens[tid]), 1.f) : 1.f;
+    if (tid < TR) sm.rs[tid] = (p.flags & RET_NORM_SCORE) ? 1.f / fmaxf(fabsf(sm.dens[tid]), 1.f) : 1.f;
 
-  // ---- normalise and store: the whole tile is staged in LDS in the output
-  // type (over the query / key / value buffers, dead by now), then written
-  // with 16-byte stores
-  __syncthreads();
-  TO* Os = reinterpret_cast<TO*>(smem_raw);
-  constexpr int OV = 16 / (int)sizeof(TO);        // elements per 16 bytes
-  constexpr int OP = DV + OV;                     // staging row pitch
-  static_assert(TR * OP * sizeof(TO) <= offsetof(OutSmem, Ps), "staging overlaps live LDS");
-#pragma unroll
-  for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int col = (2 * wave + jj) * 32 + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = qh * 32 + acc_row(r, lane);
-        Os[row * OP + col] = Store<TO>::cvt(O[qh][jj][r] * sm.rs[row]);
+    // ---- normalise and store: the whole tile is staged in LDS in the output
+    // type (over the query / key / value buffers, dead by now), then written
+    // with 16-byte stores
+    __syncthreads();
+    TO* Os = reinterpret_cast<TO*>(smem_raw);
+    constexpr int OV = 16 / (int)sizeof(TO);        // elements per 16 bytes
+    constexpr int OP = DV + OV;                     // staging row pitch
+    static_assert(TR * OP * sizeof(TO) <= offsetof(OutSmem, Ps), "staging overlaps live LDS");
+  #pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+  #pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int col = (2 * wave + jj) * 32 + l32;
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = qh * 32 + acc_row(r, lane);
+          Os[row * OP + col] = Store<TO>::cvt(O[qh][jj][r] * sm.rs[row]);
+        }
       }
+    __syncthreads();
+    for (int e = tid; e < TR * (DV / OV); e += NT3) {
+      const int row = e / (DV / OV), cv = e % (DV / OV);
+      if (row < qvalid)
+        *reinterpret_cast<u32x4*>(Og + (int64_t)row * p.so.l + cv * OV) =
+            *reinterpret_cast<const u32x4*>(Os + row * OP + cv * OV);
     }
-  __syncthreads();
-  for (int e = tid; e < TR * (DV / OV); e += NT3) {
-    const int row = e / (DV / OV), cv = e % (DV / OV);
-    if (row < qvalid)
-      *reinterpret_cast<u32x4*>(Og + (int64_t)row * p.so.l + cv * OV) =
-          *reinterpret_cast<const u32x4*>(Os + row * OP + cv * OV);
+    }
   }
+}
+
+// workgroups of the persistent output kernel: one per CU of the current device
+int persistent_workgroups() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 template <typename T, typename TO>
@@ -744,6 +782,7 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
   p.h = a.h; p.L = a.L; p.B = a.B;
   p.nc = (a.L + a.B - 1) / a.B;
   p.nrt = a.B / TR;
+  p.nbh = a.b * a.h;
   p.pos0 = a.pos0; p.n_prev = a.n_prev; p.flags = a.flags;
   p.state_in = a.state_in; p.z_in = a.z_in; p.state_out = a.state_out; p.z_out = a.z_out;
   const int bh = a.b * a.h;
@@ -762,7 +801,10 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
     auto k = output_kernel<T, TO>;
     e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(OutSmem));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(bh * p.nc * p.nrt), dim3(NT3), sizeof(OutSmem), st, p, *a.hp);
+    const int units = bh * p.nc * ((p.nrt + 1) / 2);
+    int W = min(units, persistent_workgroups());
+    if (W >= 8) W -= W % 8;
+    hipLaunchKernelGGL(k, dim3(W), dim3(NT3), sizeof(OutSmem), st, p, *a.hp);
   }
   return hipGetLastError();
 }
