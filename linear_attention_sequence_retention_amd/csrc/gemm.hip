@@ -7,11 +7,12 @@
 // gated, normalised heads) on v_mfma_f32_32x32x16_f16 with B converted to
 // fp16 while it is staged into LDS.
 //
-// Block tile 256 x 256 x 32 on 8 waves (each 64 x 128 = 2 x 4 MFMA tiles);
-// the next K slab is loaded into registers while the current one is
-// multiplied out of LDS (two LDS buffers, one barrier per slab).  Rows and
-// columns beyond M / N are clamped on load and skipped on store; K must be a
-// multiple of 32.
+// Block tile 256 x 256 x 64 (x 32 when K is not a multiple of 64) on 8 waves
+// (each 64 x 128 = 2 x 4 MFMA tiles); the next K slab is loaded into
+// registers while the current one is multiplied out of LDS (two LDS buffers,
+// one barrier per slab), and within a slab the fragments of step s + 1 are
+// read while step s multiplies.  Rows and columns beyond M / N are clamped on
+// load and skipped on store; K must be a multiple of 32.
 #include "internal.h"
 
 namespace ret {
@@ -19,13 +20,13 @@ namespace ret {
 namespace {
 
 constexpr int GT = 512;          // threads
-constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int LP = BK + 8;       // LDS row pitch (elements): 80 bytes, 16-byte aligned
+constexpr int BM = 256, BN = 256;
 constexpr int WM = 64, WN = 128; // wave tile
-constexpr int A_LD = BM * BK / 8 / GT;   // 16-byte loads per thread per slab (2)
-constexpr int B_LD = BN * BK / 8 / GT;   // (2)
 
-struct GemmSmem {
+// K slab of BK (64, or 32 when K is not a multiple of 64); LDS row pitch
+// BK + 8 elements keeps the fragment reads of 16 rows on distinct banks
+template <int BK> struct GemmSmem {
+  static constexpr int LP = BK + 8;
   uint16_t a[2][BM * LP];
   uint16_t b[2][BN * LP];
 };
@@ -58,13 +59,16 @@ template <> struct GemmOp<half> {
   __device__ __forceinline__ static u32x4 cvt_b(u32x4 u) { return bf16x8_to_f16x8(u); }
 };
 
-template <typename TA, typename TO>
+template <typename TA, typename TO, int BK>
 __global__ void __launch_bounds__(GT, 1)
 gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, TO* __restrict__ C,
                int M, int N, int K, int tiles_n) {
   typedef GemmOp<TA> G;
+  constexpr int LP = GemmSmem<BK>::LP;
+  constexpr int A_LD = BM * BK / 8 / GT;   // 16-byte loads per thread per slab
+  constexpr int B_LD = BN * BK / 8 / GT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  GemmSmem& sm = *reinterpret_cast<GemmSmem*>(smem_raw);
+  GemmSmem<BK>& sm = *reinterpret_cast<GemmSmem<BK>*>(smem_raw);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lh = lane >> 5, l32 = lane & 31;
@@ -78,20 +82,20 @@ gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, T
   const int wn = (wave & 1) * WN;
 
   // loader mapping: each 16-byte load covers 8 k of one row; a slab row has
-  // BK / 8 = 4 such pieces
+  // BK / 8 such pieces
   u32x4 ra[A_LD], rb[B_LD];
   auto load_slab = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
       const int e = tid + i * GT;
-      const int row = e >> 2, piece = e & 3;
+      const int row = e / (BK / 8), piece = e % (BK / 8);
       const int gr = min(m0 + row, M - 1);
       ra[i] = *reinterpret_cast<const u32x4*>(A + (size_t)gr * K + k0 + piece * 8);
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const int e = tid + i * GT;
-      const int row = e >> 2, piece = e & 3;
+      const int row = e / (BK / 8), piece = e % (BK / 8);
       const int gr = min(n0 + row, N - 1);
       rb[i] = *reinterpret_cast<const u32x4*>(B + (size_t)gr * K + k0 + piece * 8);
     }
@@ -100,12 +104,12 @@ gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, T
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
       const int e = tid + i * GT;
-      *reinterpret_cast<u32x4*>(&sm.a[buf][(e >> 2) * LP + (e & 3) * 8]) = ra[i];
+      *reinterpret_cast<u32x4*>(&sm.a[buf][(e / (BK / 8)) * LP + (e % (BK / 8)) * 8]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const int e = tid + i * GT;
-      *reinterpret_cast<u32x4*>(&sm.b[buf][(e >> 2) * LP + (e & 3) * 8]) = G::cvt_b(rb[i]);
+      *reinterpret_cast<u32x4*>(&sm.b[buf][(e / (BK / 8)) * LP + (e % (BK / 8)) * 8]) = G::cvt_b(rb[i]);
     }
   };
 
@@ -122,19 +126,25 @@ gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, T
   for (int kb = 0; kb < nk; ++kb) {
     const int cur = kb & 1;
     if (kb + 1 < nk) load_slab((kb + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < BK; ks += 16) {
-      typename G::frag af[2], bfr[4];
+    typename G::frag af[2][2], bfr[2][4];
+    auto ldf = [&](int ks, int bsel) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const typename G::frag*>(&sm.a[cur][(wm + i * 32 + l32) * LP + ks + 8 * lh]);
+        af[bsel][i] = *reinterpret_cast<const typename G::frag*>(&sm.a[cur][(wm + i * 32 + l32) * LP + ks + 8 * lh]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const typename G::frag*>(&sm.b[cur][(wn + j * 32 + l32) * LP + ks + 8 * lh]);
+        bfr[bsel][j] = *reinterpret_cast<const typename G::frag*>(&sm.b[cur][(wn + j * 32 + l32) * LP + ks + 8 * lh]);
+    };
+    ldf(0, 0);
+#pragma unroll
+    for (int t = 0; t < BK / 16; ++t) {
+      if (t + 1 < BK / 16) ldf(16 * (t + 1), (t + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) G::mma(acc[i][j], af[i], bfr[j]);
+        for (int j = 0; j < 4; ++j) G::mma(acc[i][j], af[t & 1][i], bfr[t & 1][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (kb + 1 < nk) store_slab(cur ^ 1);
     __syncthreads();
@@ -156,16 +166,21 @@ gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, T
     }
 }
 
-template <typename TA, typename TO>
-static hipError_t launch_gemm_t(const void* A, const void* B, void* C, int M, int N, int K, hipStream_t st) {
+template <typename TA, typename TO, int BK>
+static hipError_t launch_gemm_k(const void* A, const void* B, void* C, int M, int N, int K, hipStream_t st) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const size_t sh = sizeof(GemmSmem);
-  auto kern = gemm_nt_kernel<TA, TO>;
+  const size_t sh = sizeof(GemmSmem<BK>);
+  auto kern = gemm_nt_kernel<TA, TO, BK>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GT), sh, st, (const uint16_t*)A, (const uint16_t*)B,
                      (TO*)C, M, N, K, tiles_n);
   return hipGetLastError();
+}
+
+template <typename TA, typename TO>
+static hipError_t launch_gemm_t(const void* A, const void* B, void* C, int M, int N, int K, hipStream_t st) {
+  return K % 64 == 0 ? launch_gemm_k<TA, TO, 64>(A, B, C, M, N, K, st) : launch_gemm_k<TA, TO, 32>(A, B, C, M, N, K, st);
 }
 
 template <typename TA>
