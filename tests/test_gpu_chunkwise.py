@@ -171,3 +171,14 @@ def test_fp16_inputs_and_output(R, dk, dv):
     torch.cuda.synchronize()
     ref = oracle.retention_chunkwise(f64(q, "bf16"), f64(k, "bf16"), f64(v, "bf16"), g, th, flags, B)[0]
     check(f"fp16 in/out dk{dk} dv{dv}", host64(o), ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("B,L", [(192, 2048), (320, 1100), (128, 2048)])
+def test_large_chunk_schedules(R, B, L):
+    """Large-chunk path with an odd number of 64-row query tiles per chunk (a
+    tile without a partner in the paired schedule), several units per
+    workgroup (more units than CUs) and a ragged last chunk; the oracle
+    recomputes sampled (batch, head) sequences in full."""
+    cfg = dict(W.CHUNKWISE["medium"])
+    cfg.update(b=2, L=L, seed=31)
+    _full_config_sampled(R, cfg, B, [(0, 0), (1, 5), (1, 7)])
