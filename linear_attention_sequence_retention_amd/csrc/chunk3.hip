@@ -165,8 +165,8 @@ __device__ __forceinline__ int scale_exp(float amax) {
 // four key rows of one transposed read start 64 bytes apart in the bank space.
 constexpr int DP = 256 + 32;
 struct DeltaSmem {
-  half Kz[TK * DP];     // zeta-scaled rotated keys [key][d]
-  half Vh[TK * DP];     // this half of the value tile [key][col]
+  half Kz[2][TK * DP];  // zeta-scaled rotated keys [key][d], two tiles
+  half Vh[2][TK * DP];  // this half of the value tile [key][col], two tiles
   float dzs[DK];
   float4 step[DK / 2];  // per pair: e^{i theta} and e^{i TK theta} as (c1, s1, cT, sT)
 };
@@ -235,12 +235,11 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   // transposed-read origin of this lane (see lds_read_tr16): key 8 (lane / 32)
   // + (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
   const int tro = (8 * (lane >> 5) + ((lane & 15) >> 2)) * DP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  issue(0);
-  for (int kt = 0; kt < nkt; ++kt) {
+  // ---- rotate the keys (-> workspace), scale by zeta (-> LDS, key-sum);
+  // convert the values (-> LDS), tile kt into LDS buffer buf
+  auto stage = [&](int kt, int buf) {
     const int k0 = kt * TK;
     const int kvalid = min(TK, Bc - k0);
-    // ---- rotate the keys (-> workspace), scale by zeta (-> LDS, key-sum);
-    // convert the values (-> LDS)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = kq + i;
@@ -265,10 +264,10 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
         x[e] *= z;
         dzp[e] += x[e];
       }
-      st8(sm.Kz + key * DP + 8 * cq, x);
+      st8(sm.Kz[buf] + key * DP + 8 * cq, x);
       u32x4 v = Raw16<T>::f16(vr[i]);
       if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(sm.Vh + key * DP + 8 * cq) = v;
+      *reinterpret_cast<u32x4*>(sm.Vh[buf] + key * DP + 8 * cq) = v;
     }
     if (xpos) {
 #pragma unroll
@@ -277,20 +276,20 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
         advance(pc[u], ps[u], t1.z, t1.w);
       }
     }
-    if (kt + 1 < nkt) issue(kt + 1);
-    __syncthreads();
+  };
+  auto mma = [&](int buf) {
 #pragma unroll
     for (int kb = 0; kb < TK; kb += 16) {
       f16x8 af[2], bf[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const half* ap = sm.Kz + kb * DP + d0 + 32 * i + tro;
+        const half* ap = sm.Kz[buf] + kb * DP + d0 + 32 * i + tro;
         const f16x4 lo = lds_read_tr16(ap), hi = lds_read_tr16(ap + 4 * DP);
         af[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const half* bp = sm.Vh + kb * DP + n0 + 32 * jj + tro;
+        const half* bp = sm.Vh[buf] + kb * DP + n0 + 32 * jj + tro;
         const f16x4 lo = lds_read_tr16(bp), hi = lds_read_tr16(bp + 4 * DP);
         bf[jj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
@@ -301,18 +300,38 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
         for (int jj = 0; jj < 4; ++jj) acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[jj], acc[i][jj], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // two LDS buffers: tile kt + 1 is staged while tile kt is multiplied (one
+  // barrier per tile); tile kt + 2 is then loaded into registers
+  issue(0);
+  stage(0, 0);
+  if (nkt > 1) issue(1);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    mma(kt & 1);
+    if (kt + 1 < nkt) {
+      stage(kt + 1, (kt + 1) & 1);
+      if (kt + 2 < nkt) issue(kt + 2);
+    }
     __syncthreads();
   }
 
-  // ---- key-sum delta: lanes l and l + 32 share a piece; then the 8 waves
+  // ---- key-sum delta: lanes l and l + 32 share a piece; the 8 waves'
+  // partials are summed in a fixed order (bit-reproducible)
   if (half_ == 0) {
-    if (tid < DK) sm.dzs[tid] = 0.f;
-    __syncthreads();
+    float* part = reinterpret_cast<float*>(&sm.Kz[0][0]);   // [8 waves][DK], LDS free after the loop
 #pragma unroll
     for (int e = 0; e < 8; ++e) dzp[e] += __shfl_xor(dzp[e], 32, 64);
     if (lane < 32) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) atomicAdd(&sm.dzs[8 * cq + e], dzp[e]);
+      for (int e = 0; e < 8; ++e) part[wave * DK + 8 * cq + e] = dzp[e];
+    }
+    __syncthreads();
+    if (tid < DK) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NT3 / 64; ++w) sum += part[w * DK + tid];
+      sm.dzs[tid] = sum;
     }
   }
 
@@ -324,7 +343,7 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[i][jj][r]));
-  amax = maxabs_block(amax, reinterpret_cast<float*>(sm.Kz));
+  amax = maxabs_block(amax, reinterpret_cast<float*>(&sm.Vh[0][0]));
   const int e = scale_exp(amax);
   const float down = ldexpf(1.f, -e);
   half* dR = p.w.dR + ((int64_t)bh * p.nc + c) * DV * DK;
@@ -428,6 +447,7 @@ struct OutSmem {
   } u;
   half Ps[TR * KP];
   float rs[TR], xs[TR], dens[TR];
+  float dpart[2][TR];       // within-chunk row sums of key halves 0 / 1
   float zs[DK];
   float ginv[32];           // gamma^-m, m = 0 .. 31
 };
@@ -726,10 +746,14 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     }
     if (wave < 4) {
       den += __shfl_xor(den, 32, 64);               // lanes l and l + 32 hold the same query
-      if (lh == 0) atomicAdd(&sm.dens[sqh * 32 + l32], den);
+      if (lh == 0) sm.dpart[sk][sqh * 32 + l32] = den;
     }
     __syncthreads();
-    if (tid < TR) sm.rs[tid] = (p.flags & RET_NORM_SCORE) ? 1.f / fmaxf(fabsf(sm.dens[tid]), 1.f) : 1.f;
+    // cross part plus the two key halves, summed in a fixed order
+    if (tid < TR) {
+      const float d = sm.dens[tid] + sm.dpart[0][tid] + sm.dpart[1][tid];
+      sm.rs[tid] = (p.flags & RET_NORM_SCORE) ? 1.f / fmaxf(fabsf(d), 1.f) : 1.f;
+    }
 
     // ---- normalise and store: the whole tile is staged in LDS in the output
     // type (over the query / key / value buffers, dead by now), then written
@@ -760,6 +784,8 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     }
   }
 }
+
+static_assert(sizeof(OutSmem) <= 160 * 1024 && sizeof(DeltaSmem) <= 160 * 1024, "LDS of one workgroup");
 
 // workgroups of the persistent output kernel: one per CU of the current device
 int persistent_workgroups() {

@@ -51,7 +51,8 @@ struct Smem {
   float Oc[TR * CP];   // scaled cross term of the query tile
   float zs[DK];        // z_{c-1}
   float zeta[TK];      // zeta of the keys of the diagonal tile
-  float dens[TR];      // scaled score row sums of the query tile
+  float dens[TR];      // scaled score row sums of the query tile (cross part)
+  float dpart[2][TR];  // within-chunk row sums of key halves 0 / 1
   float rs[TR];        // s_i of the query tile
   float xs[TR];        // s_i xi_i (cross-term row factor)
   float wmax[NT / 64];
@@ -359,6 +360,8 @@ __global__ void __launch_bounds__(NT, 1) chunkwise_kernel(KParams p, HeadParams 
         sm.rs[tid] = sc;
         sm.xs[tid] = sc * dec.pow((float)(r0 + tid + 1));
         sm.dens[tid] = 0.f;
+        sm.dpart[0][tid] = 0.f;
+        sm.dpart[1][tid] = 0.f;
       }
     }
     __syncthreads();
@@ -472,8 +475,11 @@ __global__ void __launch_bounds__(NT, 1) chunkwise_kernel(KParams p, HeadParams 
     if (last_of_rt) {
       if (score_wave) {
         den += __shfl_xor(den, 32, 64);
-        if (lh == 0) atomicAdd(&sm.dens[sq_q * 32 + l32], den);
+        if (lh == 0) sm.dpart[sq_k][sq_q * 32 + l32] = den;
       }
+      __syncthreads();
+      // cross part plus the two key halves, summed in a fixed order
+      if (tid < TR) sm.dens[tid] += sm.dpart[0][tid] + sm.dpart[1][tid];
       __syncthreads();
       if (score_wave && w4 < NOT) {
         const int col = ot_c * 32 + l32;
@@ -520,6 +526,7 @@ template <typename T, typename TO, int DK, int DV, int SV>
 static hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
   static_assert(DK / 2 <= NT, "pairs per row exceed the workgroup");
   static_assert((TR / 32) * (SV / 32) <= 4, "one output tile per wave");
+  static_assert(sizeof(Smem<typename OpOf<T>::type, DK, SV>) <= 160 * 1024, "LDS of one workgroup");
   KParams p;
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o;
   p.sq = a.sq; p.sk = a.sk; p.sv = a.sv; p.so = a.so;

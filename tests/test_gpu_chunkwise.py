@@ -130,6 +130,34 @@ def test_deterministic(R):
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
+@pytest.mark.parametrize("B", [512, 192])
+def test_deterministic_large_chunks(R, B):
+    """Repeated calls give bit-identical outputs, states and key-sums (the
+    row-sum and key-sum reductions have a fixed order).  The queries are scaled
+    by 512 (exact in bf16) so that about half the rows have |s row sum| > 1:
+    the score normaliser's clamp is active there, where the summation order
+    would show."""
+    dtype, b, h, L, dk, dv = "bf16", 2, 4, 1100, 256, 512
+    q, k, v = W.chunkwise_inputs(b, h, L, dk, dv, dtype, 1 / 16, seed=12)
+    q = W.f32_to_bf16_bits(W.as_f32(q, dtype) * 512.0)
+    g, th = W.gamma_vector(h), W.theta_vector(dk)
+    qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    announce(f"determinism B={B}")
+    outs = []
+    for _ in range(2):
+        st = torch.empty((b, h, dk, dv), dtype=torch.float32, device="cuda")
+        zz = torch.empty((b, h, dk), dtype=torch.float32, device="cuda")
+        o = R.chunkwise_fwd(qd, kd, vd, g, th, B, XPOS | ALL, state_out=st, z_out=zz, out_dtype=torch.float32)
+        outs.append((o, st, zz))
+    torch.cuda.synchronize()
+    for x, y in zip(outs[0], outs[1]):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    # the clamp is active on some rows
+    ref = oracle.retention_chunkwise(f64(q[:1, :1], dtype), f64(k[:1, :1], dtype), f64(v[:1, :1], dtype),
+                                     g[:1], th, XPOS | ALL, B)[0]
+    check(f"clamp-active rows B={B}", host64(outs[0][0][:1, :1]), ref, TOL[dtype])
+
+
 def _full_config_sampled(R, cfg, B, heads):
     """The full workload on the GPU (the launch the bench times); the oracle
     recomputes the listed (batch, head) sequences in full."""
