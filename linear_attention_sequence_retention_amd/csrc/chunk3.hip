@@ -240,41 +240,43 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   auto stage = [&](int kt, int buf) {
     const int k0 = kt * TK;
     const int kvalid = min(TK, Bc - k0);
+    float x[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = kq + i;
-      const bool ok = key < kvalid;
-      float x[8];
-      Raw16<T>::f32(kr[i], x);
+      Raw16<T>::f32(kr[i], x[i]);
+      if (kq + i >= kvalid) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = ok ? x[e] : 0.f;
-      if (xpos) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float4 t1 = sm.step[4 * cq + u];
-          float cs = pc[u], sn = ps[u];
-          for (int t = 0; t < i; ++t) advance(cs, sn, t1.x, t1.y);
-          rot(x[2 * u], x[2 * u + 1], cs, sn);
-        }
+        for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
       }
-      if (half_ == 0 && ok) st8(ktg + (int64_t)(k0 + key) * DK + 8 * cq, x);
-      const float z = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key) * dec.lg2);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] *= z;
-        dzp[e] += x[e];
-      }
-      st8(sm.Kz[buf] + key * DP + 8 * cq, x);
-      u32x4 v = Raw16<T>::f16(vr[i]);
-      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(sm.Vh[buf] + key * DP + 8 * cq) = v;
     }
     if (xpos) {
+      // pair-outer: each pair's phase advances once per key
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float4 t1 = sm.step[4 * cq + u];
+        float cs = pc[u], sn = ps[u];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          rot(x[i][2 * u], x[i][2 * u + 1], cs, sn);
+          if (i < 3) advance(cs, sn, t1.x, t1.y);
+        }
         advance(pc[u], ps[u], t1.z, t1.w);
       }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kq + i;
+      if (half_ == 0 && key < kvalid) st8(ktg + (int64_t)(k0 + key) * DK + 8 * cq, x[i]);
+      const float z = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key) * dec.lg2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[i][e] *= z;
+        dzp[e] += x[i][e];
+      }
+      st8(sm.Kz[buf] + key * DP + 8 * cq, x[i]);
+      u32x4 v = Raw16<T>::f16(vr[i]);
+      if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sm.Vh[buf] + key * DP + 8 * cq) = v;
     }
   };
   auto mma = [&](int buf) {
@@ -307,12 +309,17 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   stage(0, 0);
   if (nkt > 1) issue(1);
   __syncthreads();
+  // waves 4..7 (the second wave on each SIMD) stage before they multiply, so
+  // the two waves of a SIMD overlap VALU staging with MFMA
+  const bool stage_first = wave >= 4;
   for (int kt = 0; kt < nkt; ++kt) {
-    mma(kt & 1);
-    if (kt + 1 < nkt) {
+    const bool more = kt + 1 < nkt;
+    if (!stage_first) mma(kt & 1);
+    if (more) {
       stage(kt + 1, (kt + 1) & 1);
       if (kt + 2 < nkt) issue(kt + 2);
     }
+    if (stage_first) mma(kt & 1);
     __syncthreads();
   }
 
