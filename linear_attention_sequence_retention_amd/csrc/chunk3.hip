@@ -462,24 +462,39 @@ struct OutSmem {
 template <typename T, typename TO>
 __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  // Persistent schedule: one workgroup per CU walks a static list of units.
-  // A unit is the pair of query tiles (rt, nrt - 1 - rt) of one (head, chunk),
-  // so every unit costs about the same; the units of a chunk go to the
-  // workgroups of one XCD (workgroup i runs on XCD i mod 8) and run side by
-  // side there, sharing the chunk's keys, values and state in that L2.
+  // Persistent schedule: one workgroup per CU walks a static list of query
+  // tiles.  Every workgroup's tiles pair up as rt and nrt - 1 - rt, so all
+  // workgroups carry the same work; a chunk's tiles run side by side on the
+  // workgroups of one XCD (workgroup i runs on XCD i mod 8), sharing the
+  // chunk's keys, values and state in that L2.
   const int NX = min(8, (int)gridDim.x);
   const int xw = blockIdx.x % NX, jw = blockIdx.x / NX;
   const int wx = ((int)gridDim.x - xw + NX - 1) / NX;      // workgroups of this XCD
   const int ngroups = p.nbh * p.nc;
   const int gx = (ngroups - xw + NX - 1) / NX;             // (head, chunk) groups of this XCD
   const int U = (p.nrt + 1) / 2;
-  const int nk = 2 * ((gx * U - jw + wx - 1) / wx);
+  // teams of nrt workgroups (when the XCD has at least nrt): a team takes two
+  // chunks at a time, member r query tile r of the first and nrt - 1 - r of
+  // the second; otherwise units of two tiles of one chunk, round robin
+  const bool teams = wx >= p.nrt;
+  const int nteams = teams ? wx / p.nrt : 1, team = jw / p.nrt, mem = jw % p.nrt;
+  const int npairs = (gx + 1) / 2;
+  const int nk = teams ? (team < nteams ? 2 * ((npairs - team + nteams - 1) / nteams) : 0)
+                       : 2 * ((gx * U - jw + wx - 1) / wx);
   for (int k = 0; k < nk; ++k) {
-    const int un = jw + wx * (k >> 1), pi = k & 1;         // unit, and which of its two tiles
-    const int uu = un % U;
-    if (pi == 1 && uu == p.nrt - 1 - uu) continue;         // middle tile of an odd count
-    const int rt = pi == 0 ? p.nrt - 1 - uu : uu;          // heavier tile first
-    const int grp = xw + NX * (un / U);
+    int rt, m;
+    if (teams) {
+      m = 2 * (team + nteams * (k >> 1)) + (k & 1);
+      if (m >= gx) continue;
+      rt = (k & 1) ? p.nrt - 1 - mem : mem;
+    } else {
+      const int un = jw + wx * (k >> 1), pi = k & 1;       // unit, and which of its two tiles
+      const int uu = un % U;
+      if (pi == 1 && uu == p.nrt - 1 - uu) continue;       // middle tile of an odd count
+      rt = pi == 0 ? p.nrt - 1 - uu : uu;                  // heavier tile first
+      m = un / U;
+    }
+    const int grp = xw + NX * m;
     const int c = grp % p.nc, bh = grp / p.nc;
     if (rt * TR >= min(p.B, p.L - c * p.B)) continue;      // ragged last chunk
     __syncthreads();                                       // the previous item's LDS reads are done
