@@ -13,9 +13,12 @@
 //          O = (Q'K'^T (.) D) V + (Q' R_{i-1}) (.) xi, with the row scales and
 //          score normalisation, written once
 //
-// Every key and value element is rotated / converted once by the delta
-// kernel (the output kernel reads the rotated fp16 keys), and no work is
-// repeated across d_v slices.  Operands are fp16 with fp32 accumulation.
+// Chunks of at most 128 keys replace delta and scan by one state-scan kernel
+// (one workgroup per head and block of 64 state columns, walking the chunks
+// in order with the state in MFMA accumulators), which also rotates the keys.
+//
+// Every key element is rotated once (the output kernel reads the rotated fp16
+// keys), and no work is repeated across d_v slices.  Operands are fp16 with fp32 accumulation.
 // Shapes: d_k = 256, d_v = 512, chunk B a multiple of 64.
 #include "internal.h"
 
@@ -46,7 +49,13 @@ struct Work {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t carve(void* base, int bh, int L, int nc, Work* w) {
+// chunks of at most this many keys take the state-scan kernel instead of the
+// delta and scan kernels (no per-chunk delta in the workspace)
+constexpr int SSCAN_MAX_B = 128;
+
+size_t carve(void* base, int bh, int L, int B, Work* w) {
+  const int nc = (L + B - 1) / B;
+  const bool deltas = B > SSCAN_MAX_B;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -54,9 +63,9 @@ size_t carve(void* base, int bh, int L, int nc, Work* w) {
     return o;
   };
   const size_t o_kt = take((size_t)bh * L * DK * 2);
-  const size_t o_dR = take((size_t)bh * nc * DV * DK * 2);
-  const size_t o_dRs = take((size_t)bh * nc * 2 * 4);
-  const size_t o_dz = take((size_t)bh * nc * DK * 4);
+  const size_t o_dR = take(deltas ? (size_t)bh * nc * DV * DK * 2 : 0);
+  const size_t o_dRs = take(deltas ? (size_t)bh * nc * 2 * 4 : 0);
+  const size_t o_dz = take(deltas ? (size_t)bh * nc * DK * 4 : 0);
   const size_t o_Rt = take((size_t)bh * nc * DV * DK * 2);
   const size_t o_Rs = take((size_t)bh * nc * NCB * 4);
   const size_t o_zc = take((size_t)bh * nc * DK * 4);
@@ -442,6 +451,247 @@ __global__ void __launch_bounds__(256) scan_kernel(P3 p, HeadParams hp) {
   if (cb == 0 && p.z_out) p.z_out[(int64_t)bh * DK + tid] = z;
 }
 
+// ---------------------------------------------------------------- state scan (small chunks)
+// For small chunks the state update of a chunk, K'_[i]^T (V_[i] (.) zeta), is
+// a rank-B update.  Instead of writing it out per chunk and scanning it (the
+// delta and scan kernels, whose per-chunk state traffic dominates when B is
+// small), one workgroup per head and block of 64 state columns walks the
+// chunks in order: it keeps its 256 x 64 block of R in fp32 MFMA accumulators,
+// publishes R_{c-1} (fp16, a power of two per 32 columns) and z_{c-1} for the
+// output kernel, and applies the update on MFMA from the chunk's rotated,
+// zeta-scaled keys and its values.  The workgroups of column block 0 also
+// write the rotated keys for the output kernel and carry the key-sum z.
+constexpr int SCB = 64;             // state columns per workgroup
+constexpr int VBP = SCB + 32;       // fp16 pitch of the value block [key][col] (192 bytes)
+constexpr int RSP = DK + 8;         // fp16 pitch of the published block [col][d]
+struct SScanSmem {
+  half Kz[TK * DP];                 // zeta-scaled rotated keys of one 64-key tile [key][d]
+  half Vb[TK * VBP];                // the block's value columns of the tile [key][col]
+  half Rst[SCB * RSP];              // R_{c-1} operand [col][d] before it is stored
+  float amaxw[NT3 / 64][2];         // per wave and 32-column block: max |R|
+  float dzw[NT3 / 64][DK];          // per wave: key-sum partials of the chunk
+  float4 step[DK / 2];              // per pair: e^{i theta} and e^{i TK theta}
+};
+
+template <typename T>
+__global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  SScanSmem& sm = *reinterpret_cast<SScanSmem*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31;
+  constexpr int NCB64 = DV / SCB;
+  const int g = xcd_local(blockIdx.x, gridDim.x);   // the column blocks of a head share an XCD
+  const int cb = g % NCB64, bh = g / NCB64;
+  const int bb = bh / p.h, head = bh % p.h;
+  const bool lead = cb == 0;
+  Decay dec;
+  dec.init(hp.gamma[head]);
+  const bool xpos = (p.flags & RET_XPOS) != 0;
+  const T* Kg = reinterpret_cast<const T*>(p.k) + bb * p.sk.b + head * p.sk.h;
+  const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + cb * SCB;
+  half* ktg = p.w.kt + (int64_t)bh * p.L * DK;
+
+  if (xpos && tid < DK / 2) {
+    float4 t;
+    phase(1, hp.theta[tid], t.x, t.y);
+    phase(TK, hp.theta[tid], t.z, t.w);
+    sm.step[tid] = t;
+  }
+
+  // R block: wave w holds d rows [32 w, +32) of column tiles jj = 0, 1
+  const int d0 = 32 * wave;
+  f32x16 acc[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      acc[jj][r] = p.state_in ? p.state_in[((int64_t)bh * DK + d0 + acc_row(r, lane)) * DV + cb * SCB + 32 * jj + l32]
+                              : 0.f;
+  float z = (lead && p.z_in && tid < DK) ? p.z_in[(int64_t)bh * DK + tid] : 0.f;
+
+  // staging maps: keys kq .. kq + 3, d 8 cq .. 8 cq + 7; value key vk, columns 8 vp ..
+  const int cq = tid & 31, kq = 4 * (tid >> 5);
+  const int vk = tid >> 3, vp = tid & 7;
+  float pc[4], ps[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    pc[u] = 1.f;
+    ps[u] = 0.f;
+    if (xpos) phase(p.pos0 + kq, hp.theta[4 * cq + u], pc[u], ps[u]);
+  }
+  const int tro = (8 * (lane >> 5) + ((lane & 15) >> 2)) * DP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int trv = (8 * (lane >> 5) + ((lane & 15) >> 2)) * VBP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  // 64-key tiles are numbered over the whole sequence (chunks hold B / 64)
+  u32x4 kr[4], vr;
+  auto issue = [&](int kt) {
+    const int k0 = kt * TK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(k0 + kq + i, p.L - 1);
+      kr[i] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)key * p.sk.l + 8 * cq);
+    }
+    const int key = min(k0 + vk, p.L - 1);
+    vr = *reinterpret_cast<const u32x4*>(Vg + (int64_t)key * p.sv.l + 8 * vp);
+  };
+  const int ntiles = (p.L + TK - 1) / TK;
+  const int tpc = p.B / TK;                          // tiles per full chunk
+  issue(0);
+  float dzp[8];
+  float gprev = 1.f;                                 // gamma^(B of the previous chunk)
+  __syncthreads();                                   // step table
+  for (int c = 0; c < p.nc; ++c) {
+    const int c0 = c * p.B;
+    const int Bc = min(p.B, p.L - c0);
+    const int nt = (Bc + TK - 1) / TK;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dzp[e] = 0.f;
+    for (int s = 0; s < nt; ++s) {
+      const int kt = c * tpc + s;
+      const int k0 = s * TK;                         // chunk-local first key of the tile
+      const int kvalid = min(TK, Bc - k0);
+      // ---- stage the tile: rotate the keys (-> workspace), scale by zeta (->
+      // LDS, key-sum); convert the value block (-> LDS)
+      {
+        float x[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Raw16<T>::f32(kr[i], x[i]);
+          if (kq + i >= kvalid) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+          }
+        }
+        if (xpos) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float4 t1 = sm.step[4 * cq + u];
+            float cs = pc[u], sn = ps[u];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              rot(x[i][2 * u], x[i][2 * u + 1], cs, sn);
+              if (i < 3) advance(cs, sn, t1.x, t1.y);
+            }
+            advance(pc[u], ps[u], t1.z, t1.w);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kq + i;
+          if (lead && key < kvalid) st8(ktg + (int64_t)(c0 + k0 + key) * DK + 8 * cq, x[i]);
+          const float zt = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key) * dec.lg2);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x[i][e] *= zt;
+            dzp[e] += x[i][e];
+          }
+          st8(sm.Kz + key * DP + 8 * cq, x[i]);
+        }
+        u32x4 v = Raw16<T>::f16(vr);
+        if (vk >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(sm.Vb + vk * VBP + 8 * vp) = v;
+      }
+      if (kt + 1 < ntiles) issue(kt + 1);
+      if (s == 0) {
+        // ---- publish R_{c-1}: per 32-column block, a power of two puts max |R| in [2^14, 2^15)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          float m = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[jj][r]));
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          if (lane == 0) sm.amaxw[wave][jj] = m;
+        }
+      }
+      __syncthreads();
+      if (s == 0) {
+        float down[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          float m = 0.f;
+#pragma unroll
+          for (int w = 0; w < NT3 / 64; ++w) m = fmaxf(m, sm.amaxw[w][jj]);
+          const int e = scale_exp(m);
+          down[jj] = ldexpf(1.f, -e);
+          if (tid == 0) p.w.Rs[((int64_t)bh * p.nc + c) * NCB + 2 * cb + jj] = ldexpf(1.f, e);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            // acc rows 4 rg .. 4 rg + 3 are d .. d + 3
+            const int d = d0 + 8 * rg + 4 * (lane >> 5);
+            float x4[4] = {acc[jj][4 * rg] * down[jj], acc[jj][4 * rg + 1] * down[jj],
+                           acc[jj][4 * rg + 2] * down[jj], acc[jj][4 * rg + 3] * down[jj]};
+            st4(sm.Rst + (32 * jj + l32) * RSP + d, x4);
+          }
+        if (lead && tid < DK) {
+          // z_{c-1}: the key-sum of the previous chunk, summed over the waves in order
+          if (c > 0) {
+            float dz = 0.f;
+#pragma unroll
+            for (int w = 0; w < NT3 / 64; ++w) dz += sm.dzw[w][tid];
+            z = gprev * z + dz;
+          }
+          p.w.zc[((int64_t)bh * p.nc + c) * DK + tid] = z;
+        }
+        __syncthreads();
+        half* dst = p.w.Rt + (((int64_t)bh * p.nc + c) * DV + cb * SCB) * DK;
+#pragma unroll
+        for (int i = 0; i < SCB * DK / 8 / NT3; ++i) {
+          const int e = tid + i * NT3;
+          const int col = e / (DK / 8), piece = e % (DK / 8);
+          *reinterpret_cast<u32x4*>(dst + (int64_t)col * DK + piece * 8) =
+              *reinterpret_cast<const u32x4*>(sm.Rst + col * RSP + piece * 8);
+        }
+        const float gB = dec.pow((float)Bc);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[jj] *= gB;
+        gprev = gB;
+      }
+      // ---- R += (K' zeta)^T V over the tile's keys
+#pragma unroll
+      for (int kb = 0; kb < TK; kb += 16) {
+        const half* ap = sm.Kz + kb * DP + d0 + tro;
+        const f16x4 alo = lds_read_tr16(ap), ahi = lds_read_tr16(ap + 4 * DP);
+        const f16x8 af = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const half* bp = sm.Vb + kb * VBP + 32 * jj + trv;
+          const f16x4 lo = lds_read_tr16(bp), hi = lds_read_tr16(bp + 4 * VBP);
+          const f16x8 bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, acc[jj], 0, 0, 0);
+        }
+      }
+      if (s == nt - 1 && lead) {
+        // this chunk's key-sum partials: lanes l and l + 32 share a piece
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dzp[e] += __shfl_xor(dzp[e], 32, 64);
+        if (lane < 32) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sm.dzw[wave][8 * cq + e] = dzp[e];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (lead && tid < DK) {
+    float dz = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT3 / 64; ++w) dz += sm.dzw[w][tid];
+    z = gprev * z + dz;
+    if (p.z_out) p.z_out[(int64_t)bh * DK + tid] = z;
+  }
+  if (p.state_out) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        p.state_out[((int64_t)bh * DK + d0 + acc_row(r, lane)) * DV + cb * SCB + 32 * jj + l32] = acc[jj][r];
+  }
+}
+
 // ---------------------------------------------------------------- output
 struct OutSmem {
   half Qs[TR * QP];
@@ -807,7 +1057,8 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   }
 }
 
-static_assert(sizeof(OutSmem) <= 160 * 1024 && sizeof(DeltaSmem) <= 160 * 1024, "LDS of one workgroup");
+static_assert(sizeof(OutSmem) <= 160 * 1024 && sizeof(DeltaSmem) <= 160 * 1024 && sizeof(SScanSmem) <= 160 * 1024,
+              "LDS of one workgroup");
 
 // workgroups of the persistent output kernel: one per CU of the current device
 int persistent_workgroups() {
@@ -834,17 +1085,23 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
   p.pos0 = a.pos0; p.n_prev = a.n_prev; p.flags = a.flags;
   p.state_in = a.state_in; p.z_in = a.z_in; p.state_out = a.state_out; p.z_out = a.z_out;
   const int bh = a.b * a.h;
-  carve(a.ws, bh, a.L, p.nc, &p.w);
+  carve(a.ws, bh, a.L, a.B, &p.w);
   hipError_t e;
-  {
+  if (a.B <= SSCAN_MAX_B) {
+    auto k = sscan_kernel<T>;
+    e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SScanSmem));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(bh * (DV / SCB)), dim3(NT3), sizeof(SScanSmem), st, p, *a.hp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
     auto k = delta_kernel<T>;
     e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(DeltaSmem));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(bh * p.nc * 2), dim3(NT3), sizeof(DeltaSmem), st, p, *a.hp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(scan_kernel, dim3(bh * NCB), dim3(256), 0, st, p, *a.hp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(scan_kernel, dim3(bh * NCB), dim3(256), 0, st, p, *a.hp);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     auto k = output_kernel<T, TO>;
     e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(OutSmem));
@@ -871,7 +1128,7 @@ bool three_phase_applies(ret_dtype in_dt, int dk, int dv, int B) {
 }
 
 size_t three_phase_workspace(int b, int h, int L, int B) {
-  return carve(nullptr, b * h, L, (L + B - 1) / B, nullptr);
+  return carve(nullptr, b * h, L, B, nullptr);
 }
 
 hipError_t launch_three_phase(const ChunkArgs& a, hipStream_t st) {
