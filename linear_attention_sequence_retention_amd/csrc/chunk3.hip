@@ -42,7 +42,7 @@ struct Work {
   half* dR;      // chunk deltas       [bh][nc][DV][DK]   (column-major: [col][d])
   float* dRs;    // delta scales       [bh][nc][2]        (2^e per d_v half)
   float* dz;     // key-sum deltas     [bh][nc][DK]
-  half* Rt;      // state operands     [bh][nc][DV][DK]   (R_{i-1}, [col][d])
+  half* Rt;      // state operands     [bh][nc][DV*DK]    (R_{i-1}, fragment order, rt_frag)
   float* Rs;     // operand scales     [bh][nc][NCB]
   float* zc;     // z_{i-1}            [bh][nc][DK]
 };
@@ -147,6 +147,14 @@ struct P3 {
 // the workgroups of one group (same head and chunk) land on one XCD
 __device__ __forceinline__ int xcd_local(int g, int n) {
   return ((n & 7) == 0) ? (g & 7) * (n >> 3) + (g >> 3) : g;
+}
+
+// offset of state operand element (col, d) within one chunk's DV x DK block,
+// stored in MFMA B-fragment order: the block of 32 columns and 16 d is 1 KB,
+// in which lane 32 ((d / 8) % 2) + col % 32 holds its 8 consecutive d as 16
+// contiguous bytes (the fragment of a 32x32x16 MFMA with k = d)
+__device__ __forceinline__ int rt_frag(int col, int d) {
+  return (((col >> 5) * (DK / 16) + (d >> 4)) * 64 + ((d >> 3) & 1) * 32 + (col & 31)) * 8 + (d & 7);
 }
 
 __device__ __forceinline__ float maxabs_block(float v, float* red) {
@@ -424,13 +432,13 @@ __global__ void __launch_bounds__(256) scan_kernel(P3 p, HeadParams hp) {
     amax = maxabs_block(amax, red);
     const int e = scale_exp(amax);
     const float down = ldexpf(1.f, -e);
-    half* dst = p.w.Rt + (((int64_t)bh * p.nc + c) * DV + col) * DK + dbase;
+    half* dst = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK;
 #pragma unroll
     for (int i = 0; i < 32; i += 8) {
       float x[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) x[u] = R[i + u] * down;
-      st8(dst + i, x);
+      st8(dst + rt_frag(col, dbase + i), x);
     }
     if (tid == 0) p.w.Rs[((int64_t)bh * p.nc + c) * NCB + cb] = ldexpf(1.f, e);
     if (cb == 0) p.w.zc[((int64_t)bh * p.nc + c) * DK + tid] = z;
@@ -637,13 +645,14 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
           p.w.zc[((int64_t)bh * p.nc + c) * DK + tid] = z;
         }
         __syncthreads();
-        half* dst = p.w.Rt + (((int64_t)bh * p.nc + c) * DV + cb * SCB) * DK;
+        // fragment order: the 64 pieces of one (32 columns, 16 d) block are contiguous
+        half* dst = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK + (int64_t)cb * SCB * DK;
 #pragma unroll
         for (int i = 0; i < SCB * DK / 8 / NT3; ++i) {
           const int e = tid + i * NT3;
-          const int col = e / (DK / 8), piece = e % (DK / 8);
-          *reinterpret_cast<u32x4*>(dst + (int64_t)col * DK + piece * 8) =
-              *reinterpret_cast<const u32x4*>(sm.Rst + col * RSP + piece * 8);
+          const int blk = e >> 6, slot = e & 63;
+          const int col = (blk >> 4) * 32 + (slot & 31), d = 16 * (blk & 15) + 8 * (slot >> 5);
+          *reinterpret_cast<u32x4*>(dst + (int64_t)e * 8) = *reinterpret_cast<const u32x4*>(sm.Rst + col * RSP + d);
         }
         const float gB = dec.pow((float)Bc);
 #pragma unroll
@@ -700,7 +709,6 @@ struct OutSmem {
       half Ks[TK * QP];
       half Vn[TK * VP];     // value tile [key][col] (fp16)
     } kv;
-    half Rt[DV * KP];       // d-slice of the state operand [col][64 d]
   } u;
   half Ps[TR * KP];
   float rs[TR], xs[TR], dens[TR];
@@ -857,49 +865,41 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   #pragma unroll
       for (int jj = 0; jj < 2; ++jj) O[i][jj] = f32x16{};
 
-    // ---- cross-chunk term Q' R_{c-1}, one 64-wide d-slice of the state
-    // operand at a time; the next slice (after the last: the first key / value
-    // tile) is loaded into registers while the current one is multiplied
-    const half* Rg = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK;
+    // ---- cross-chunk term Q' R_{c-1}.  Wave w owns state columns 64 w ..
+    // 64 w + 63.  The state operand is stored in MFMA fragment order (a
+    // 32-column x 16-d block is one 1 KB wave load), so each wave streams its
+    // B fragments straight from global memory, XR steps ahead, with no LDS
+    // staging and no barriers.  The first key / value tile is loaded meanwhile.
+    issue(rt);
+    __syncthreads();                                // the query tile and the row tables
     {
-      u32x4 rreg[8];        // 512 columns x 64 d fp16: 4096 16-byte pieces, 8 per thread
-      auto issue_r = [&](int ds) {
+      constexpr int NSX = DK / 16, XR = 4;
+      const half* rp = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK + (int64_t)(2 * wave * NSX * 64 + lane) * 8;
+      f16x8 rb[XR][2], qa[2][2];
   #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int e = tid + i * NT3;
-          rreg[i] = *reinterpret_cast<const u32x4*>(Rg + (int64_t)(e >> 3) * DK + ds + (e & 7) * 8);
-        }
+      for (int t = 0; t < XR; ++t)
+  #pragma unroll
+        for (int jj = 0; jj < 2; ++jj) rb[t][jj] = *reinterpret_cast<const f16x8*>(rp + (int64_t)(jj * NSX + t) * 512);
+      auto load_q = [&](int t, int buf) {
+  #pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+          qa[buf][qh] = *reinterpret_cast<const f16x8*>(sm.Qs + (qh * 32 + l32) * QP + 16 * t + 8 * lh);
       };
-      issue_r(0);
-      for (int ds = 0; ds < DK; ds += 64) {
-        __syncthreads();
+      load_q(0, 0);
   #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int e = tid + i * NT3;
-          *reinterpret_cast<u32x4*>(sm.u.Rt + (e >> 3) * KP + (e & 7) * 8) = rreg[i];
-        }
-        __syncthreads();
-        if (ds + 64 < DK) issue_r(ds + 64);
-        else issue(rt);
-        f16x8 qa[2][2], rb[2][2];
-        auto load_x = [&](int kb, int buf) {
+      for (int t = 0; t < NSX; ++t) {
+        if (t + 1 < NSX) load_q(t + 1, (t + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
   #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            qa[buf][i] = *reinterpret_cast<const f16x8*>(sm.Qs + (i * 32 + l32) * QP + ds + kb + 8 * lh);
-            rb[buf][i] = *reinterpret_cast<const f16x8*>(sm.u.Rt + ((2 * wave + i) * 32 + l32) * KP + kb + 8 * lh);
-          }
-        };
-        load_x(0, 0);
+        for (int qh = 0; qh < 2; ++qh)
   #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (t + 1 < 4) load_x(16 * (t + 1), (t + 1) & 1);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int jj = 0; jj < 2; ++jj)
+            O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t & 1][qh], rb[t % XR][jj], O[qh][jj], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + XR < NSX) {
   #pragma unroll
-          for (int qh = 0; qh < 2; ++qh)
-  #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-              O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t & 1][qh], rb[t & 1][jj], O[qh][jj], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int jj = 0; jj < 2; ++jj)
+            rb[t % XR][jj] = *reinterpret_cast<const f16x8*>(rp + (int64_t)(jj * NSX + t + XR) * 512);
         }
       }
     }
