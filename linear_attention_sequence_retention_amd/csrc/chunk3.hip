@@ -739,22 +739,47 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   const int npairs = (gx + 1) / 2;
   const int nk = teams ? (team < nteams ? 2 * ((npairs - team + nteams - 1) / nteams) : 0)
                        : 2 * ((gx * U - jw + wx - 1) / wx);
-  for (int k = 0; k < nk; ++k) {
-    int rt, m;
+  // item k of this workgroup -> query tile rt of chunk c of head bh; false
+  // when the slot is empty
+  auto decode = [&](int k, int& rt, int& c, int& bh) -> bool {
+    int m;
     if (teams) {
       m = 2 * (team + nteams * (k >> 1)) + (k & 1);
-      if (m >= gx) continue;
+      if (m >= gx) return false;
       rt = (k & 1) ? p.nrt - 1 - mem : mem;
     } else {
       const int un = jw + wx * (k >> 1), pi = k & 1;       // unit, and which of its two tiles
       const int uu = un % U;
-      if (pi == 1 && uu == p.nrt - 1 - uu) continue;       // middle tile of an odd count
+      if (pi == 1 && uu == p.nrt - 1 - uu) return false;   // middle tile of an odd count
       rt = pi == 0 ? p.nrt - 1 - uu : uu;                  // heavier tile first
       m = un / U;
     }
     const int grp = xw + NX * m;
-    const int c = grp % p.nc, bh = grp / p.nc;
-    if (rt * TR >= min(p.B, p.L - c * p.B)) continue;      // ragged last chunk
+    c = grp % p.nc;
+    bh = grp / p.nc;
+    return rt * TR < min(p.B, p.L - c * p.B);              // ragged last chunk
+  };
+  // the query tile of an item, as raw element pairs: thread -> pair column
+  // tid % 128 of rows 16 (tid / 128) + 0..15.  The next item's tile is loaded
+  // while the current item is normalised and stored.
+  uint32_t qraw[16];
+  auto issue_q = [&](int rt, int c, int bh) {
+    const int j = threadIdx.x & 127, grp = threadIdx.x >> 7;
+    const int bb = bh / p.h, head = bh % p.h;
+    const int r0 = rt * TR;
+    const int qvalid = min(TR, min(p.B, p.L - c * p.B) - r0);
+    const T* Qg = reinterpret_cast<const T*>(p.q) + bb * p.sq.b + head * p.sq.h + (int64_t)(c * p.B + r0) * p.sq.l;
+  #pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rc = min(grp * 16 + i, qvalid - 1);
+      qraw[i] = *reinterpret_cast<const uint32_t*>(Qg + (uint32_t)(rc * (int)p.sq.l + 2 * j));
+    }
+  };
+  int k = 0, rt = 0, c = 0, bh = 0;
+  while (k < nk && !decode(k, rt, c, bh)) ++k;
+  if (k < nk) issue_q(rt, c, bh);
+  while (k < nk) {
+    int kn = k + 1, rtn = 0, cn = 0, bhn = 0;
     __syncthreads();                                       // the previous item's LDS reads are done
     {
     OutSmem& sm = *reinterpret_cast<OutSmem*>(smem_raw);
@@ -775,7 +800,6 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     const bool xpos = (p.flags & RET_XPOS) != 0;
     const float qk_scale = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
 
-    const T* Qg = reinterpret_cast<const T*>(p.q) + bb * p.sq.b + head * p.sq.h + (int64_t)(c0 + r0) * p.sq.l;
     const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + (int64_t)c0 * p.sv.l;
     const half* Kt = p.w.kt + ((int64_t)bh * p.L + c0) * DK;
     TO* Og = reinterpret_cast<TO*>(p.o) + bb * p.so.b + head * p.so.h + (int64_t)(c0 + r0) * p.so.l;
@@ -787,8 +811,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = grp * 16 + i;
-        const int rc = min(row, qvalid - 1);
-        float2 x = Elem<T>::ld2(Qg + (uint32_t)(rc * (int)p.sq.l + 2 * j));
+        const float2 x = Raw32<T>::f(qraw[i]);
         a[i] = row < qvalid ? x.x : 0.f;
         b[i] = row < qvalid ? x.y : 0.f;
       }
@@ -916,9 +939,18 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
           O[qh][1][r] *= x * up1;
         }
       // cross part of the score denominator, s xi (Q' . z_{c-1}): 8 threads per row
-      const int row = tid >> 3, part = tid & 7;
+      const int row = tid >> 3, part = tid & 7;     // d 32 part .. 32 part + 31
       float acc = 0.f;
-      for (int d = part; d < DK; d += 8) acc += (float)sm.Qs[row * QP + d] * sm.zs[d];
+  #pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f16x8 qv = *reinterpret_cast<const f16x8*>(sm.Qs + row * QP + 32 * part + 8 * u);
+        const f32x4 z0 = *reinterpret_cast<const f32x4*>(sm.zs + 32 * part + 8 * u);
+        const f32x4 z1 = *reinterpret_cast<const f32x4*>(sm.zs + 32 * part + 8 * u + 4);
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) acc += (float)qv[e] * z0[e];
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) acc += (float)qv[4 + e] * z1[e];
+      }
       acc += __shfl_xor(acc, 1, 64);
       acc += __shfl_xor(acc, 2, 64);
       acc += __shfl_xor(acc, 4, 64);
@@ -1016,6 +1048,9 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
         }
       }
     }
+    // the next item's query tile
+    while (kn < nk && !decode(kn, rtn, cn, bhn)) ++kn;
+    if (kn < nk) issue_q(rtn, cn, bhn);
     if (wave < 4) {
       den += __shfl_xor(den, 32, 64);               // lanes l and l + 32 hold the same query
       if (lh == 0) sm.dpart[sk][sqh * 32 + l32] = den;
@@ -1054,6 +1089,10 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
             *reinterpret_cast<const u32x4*>(Os + row * OP + cv * OV);
     }
     }
+    k = kn;
+    rt = rtn;
+    c = cn;
+    bh = bhn;
   }
 }
 
