@@ -842,7 +842,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     // ---- staged key / value tile registers
     u32x4 kreg[4];          // 64 keys x 256 d fp16: 2048 16-byte pieces, 4 per thread
     u32x4 vreg[8];          // 64 keys x 512 columns: 4096 16-byte pieces, 8 per thread
-    auto issue = [&](int kt) {
+    auto issue_k = [&](int kt) {
       const int k0 = kt * TK;
       const int kvalid = min(TK, Bc - k0);
   #pragma unroll
@@ -851,6 +851,10 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
         const int key = min(e >> 5, kvalid - 1), piece = e & 31;
         kreg[i] = *reinterpret_cast<const u32x4*>(Kt + (int64_t)(k0 + key) * DK + piece * 8);
       }
+    };
+    auto issue_v = [&](int kt) {
+      const int k0 = kt * TK;
+      const int kvalid = min(TK, Bc - k0);
   #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int e = tid + i * NT3;
@@ -858,7 +862,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
         vreg[i] = *reinterpret_cast<const u32x4*>(Vg + (uint32_t)((k0 + key) * (int)p.sv.l + piece * 8));
       }
     };
-    auto commit = [&](int kt) {
+    auto commit_k = [&](int kt) {
       const int kvalid = min(TK, Bc - kt * TK);
   #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -868,6 +872,9 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
         if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(sm.u.kv.Ks + key * QP + piece * 8) = v;
       }
+    };
+    auto commit_v = [&](int kt) {
+      const int kvalid = min(TK, Bc - kt * TK);
   #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int e = tid + i * NT3;
@@ -893,7 +900,8 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     // 32-column x 16-d block is one 1 KB wave load), so each wave streams its
     // B fragments straight from global memory, XR steps ahead, with no LDS
     // staging and no barriers.  The first key / value tile is loaded meanwhile.
-    issue(rt);
+    issue_k(rt);
+    issue_v(rt);
     __syncthreads();                                // the query tile and the row tables
     {
       constexpr int NSX = DK / 16, XR = 4;
@@ -957,19 +965,22 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       if (part == 0) sm.dens[row] = sm.xs[row] * acc;
     }
 
-    // ---- within-chunk term, diagonal key tile first
-    // waves 0..3 form S^T = K' Q'^T as 32 x 32 tiles (keys 32 (w / 2) .., queries
-    // 32 (w % 2) ..) and write P; all eight waves then accumulate P V
+    // ---- within-chunk term, diagonal key tile first (tile order rt, 0, 1, ..)
+    // Two phases per key tile, one barrier after each:
+    //   1. waves 0..3 form S^T = K' Q'^T as 32 x 32 tiles (keys 32 (w / 2) ..,
+    //      queries 32 (w % 2) ..) and write P; then every wave commits its
+    //      share of the value tile and loads the next one
+    //   2. all eight waves accumulate P V, then commit the next key tile and
+    //      load the one after
     float den = 0.f;
     const int sk = wave >> 1, sqh = wave & 1;
+    commit_k(rt);                                   // the key / value region is free since the item began
+    if (rt > 0) issue_k(0);
+    __syncthreads();
     for (int idx = 0; idx <= rt; ++idx) {
       const int kt = (idx == 0) ? rt : idx - 1;
       const bool diag = (idx == 0);
       const int k0 = kt * TK;
-      __syncthreads();
-      commit(kt);
-      if (idx < rt) issue(idx);                     // next: kt = idx
-      __syncthreads();
       if (wave < 4) {
         const bool skip = diag && sk > sqh;         // keys 32..63 vs queries 0..31 of the diagonal
         float pv[16];
@@ -1016,6 +1027,8 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   #pragma unroll
         for (int i = 0; i < 4; ++i) st4(sm.Ps + (sqh * 32 + l32) * KP + sk * 32 + 8 * i + 4 * lh, pv + 4 * i);
       }
+      commit_v(kt);
+      if (idx < rt) issue_v(idx);                   // next tile: kt = idx
       __syncthreads();
       // O += P V: the value fragment of a column tile serves both query halves
       // (rows 0..31 of P are zero against keys 32..63 of the diagonal tile);
@@ -1047,6 +1060,11 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if (idx < rt) {
+        commit_k(idx);                              // next tile: kt = idx
+        if (idx + 1 < rt) issue_k(idx + 1);
+      }
+      __syncthreads();
     }
     // the next item's query tile
     while (kn < nk && !decode(kn, rtn, cn, bhn)) ++kn;
