@@ -1009,17 +1009,23 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
           // D = gamma^(q - k) split as gamma^base gamma^-(8i + j), base = q - (first key of the lane)
           const int base = r0 + sqh * 32 + l32 - k0 - sk * 32 - 4 * lh;
           const float gq = sm.rs[sqh * 32 + l32] * __builtin_amdgcn_exp2f((float)base * dec.lg2);
+          // the causal mask q >= k only bites on the diagonal tile
+          auto scale = [&](auto masked) {
   #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float4 gi = *reinterpret_cast<const float4*>(sm.ginv + 8 * i);
-            const float gv[4] = {gi.x, gi.y, gi.z, gi.w};
+            for (int i = 0; i < 4; ++i) {
+              const float4 gi = *reinterpret_cast<const float4*>(sm.ginv + 8 * i);
+              const float gv[4] = {gi.x, gi.y, gi.z, gi.w};
   #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float val = (base >= 8 * i + j) ? S[4 * i + j] * gq * gv[j] : 0.f;
-              den += val;
-              pv[4 * i + j] = val;
+              for (int j = 0; j < 4; ++j) {
+                float val = S[4 * i + j] * gq * gv[j];
+                if (decltype(masked)::value) val = (base >= 8 * i + j) ? val : 0.f;
+                den += val;
+                pv[4 * i + j] = val;
+              }
             }
-          }
+          };
+          if (diag) scale(std::true_type{});
+          else scale(std::false_type{});
         } else {
   #pragma unroll
           for (int i = 0; i < 16; ++i) pv[i] = 0.f;
