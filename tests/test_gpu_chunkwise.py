@@ -81,23 +81,25 @@ def test_single_token_and_chunk_beyond_L(R):
 
 def test_continuation_through_state(R):
     """Prefill in two calls handing (state, z) over equals one pass (and the
-    oracle), with positions and token counts continuing."""
+    oracle), with positions and token counts continuing.  The second call's
+    chunk size picks the kernel path that starts from the handed-over state:
+    100 the fused kernel, 128 the state scan, 192 delta + scan."""
     dtype, b, h, L, dk, dv, B = "bf16", 1, 2, 300, 256, 512, 64
     flags = XPOS | ALL
     q, k, v = W.chunkwise_inputs(b, h, L, dk, dv, dtype, 1 / 16, seed=8)
     g, th = W.gamma_vector(h), W.theta_vector(dk)
     o_ref = oracle.retention_chunkwise(f64(q, dtype), f64(k, dtype), f64(v, dtype), g, th, flags, 64)[0]
     qd, kd, vd = dev(q, dtype), dev(k, dtype), dev(v, dtype)
-    for L1 in (77, 128):
-        announce(f"continuation split at {L1}")
+    for L1, B2 in ((77, 100), (128, 128), (128, 192), (77, 128)):
+        announce(f"continuation split at {L1}, second chunk size {B2}")
         S = torch.zeros((b, h, dk, dv), dtype=torch.float32, device="cuda")
         z = torch.zeros((b, h, dk), dtype=torch.float32, device="cuda")
         o1 = R.chunkwise_fwd(qd[:, :, :L1], kd[:, :, :L1], vd[:, :, :L1], g, th, B, flags, state_out=S, z_out=z)
-        o2 = R.chunkwise_fwd(qd[:, :, L1:], kd[:, :, L1:], vd[:, :, L1:], g, th, 100, flags, pos0=L1,
+        o2 = R.chunkwise_fwd(qd[:, :, L1:], kd[:, :, L1:], vd[:, :, L1:], g, th, B2, flags, pos0=L1,
                              n_prev=L1, state_in=S, z_in=z, state_out=S, z_out=z)
         torch.cuda.synchronize()
         got = np.concatenate([host64(o1), host64(o2)], axis=2)
-        check_bf16_out(f"continuation at {L1}", got, o_ref, TOL[dtype])
+        check_bf16_out(f"continuation at {L1}, B2={B2}", got, o_ref, TOL[dtype])
 
 
 def test_strided_views(R):
@@ -130,7 +132,7 @@ def test_deterministic(R):
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
-@pytest.mark.parametrize("B", [512, 192])
+@pytest.mark.parametrize("B", [512, 192, 128])
 def test_deterministic_large_chunks(R, B):
     """Repeated calls give bit-identical outputs, states and key-sums (the
     row-sum and key-sum reductions have a fixed order).  The queries are scaled
