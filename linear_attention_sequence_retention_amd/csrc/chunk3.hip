@@ -801,6 +801,12 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     const float qk_scale = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
 
     const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + (int64_t)c0 * p.sv.l;
+    // z_{c-1} (thread -> d) and the power-of-two scales of this wave's two
+    // state column blocks, requested first: they are used after the query
+    // rotation and after the cross term
+    const int64_t ci = (int64_t)bh * p.nc + c;
+    const float zpre = p.w.zc[ci * DK + (tid & (DK - 1))];
+    const float up0 = p.w.Rs[ci * NCB + 2 * wave], up1 = p.w.Rs[ci * NCB + 2 * wave + 1];
     const half* Kt = p.w.kt + ((int64_t)bh * p.L + c0) * DK;
     TO* Og = reinterpret_cast<TO*>(p.o) + bb * p.so.b + head * p.so.h + (int64_t)(c0 + r0) * p.so.l;
 
@@ -835,7 +841,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
         sm.xs[tid] = s * dec.pow((float)(r0 + tid + 1));
         sm.dens[tid] = 0.f;
       }
-      if (tid < DK) sm.zs[tid] = p.w.zc[((int64_t)bh * p.nc + c) * DK + tid];
+      if (tid < DK) sm.zs[tid] = zpre;
       if (tid < 32) sm.ginv[tid] = __builtin_amdgcn_exp2f(-(float)tid * dec.lg2);
     }
 
@@ -936,8 +942,6 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     }
     {
       // row scale s xi and the operand's per-block power of two
-      const float* Rs = p.w.Rs + ((int64_t)bh * p.nc + c) * NCB;
-      const float up0 = Rs[2 * wave], up1 = Rs[2 * wave + 1];
   #pragma unroll
       for (int qh = 0; qh < 2; ++qh)
   #pragma unroll
