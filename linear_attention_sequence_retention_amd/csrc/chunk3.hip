@@ -32,10 +32,11 @@ constexpr int TK = 64, TR = 64;
 constexpr int QP = DK + 8;     // fp16 row pitch of Qs / Ks (528 B)
 constexpr int KP = TK + 8;     // fp16 row pitch of key-major tiles (144 B)
 constexpr int NCB = DV / 32;   // column blocks of the state operand
-// row pitch (fp16) of a value tile kept in its natural [key][col] layout: 1088
-// bytes, so the four key rows of one transposed read start 64 bytes apart in
-// the bank space and a half-wave touches all 64 banks once
-constexpr int VP = DV + 32;
+// a value tile is kept in its natural [key][col] layout with unpadded 1 KB rows;
+// the 16-byte column pieces of key row r are XOR-swizzled by 4 (r % 4), so the
+// four key rows of one transposed read start 64 bytes apart in the bank space
+// and a half-wave touches all 64 banks once
+__host__ __device__ constexpr int vswz(int key, int piece) { return piece ^ ((key & 3) << 2); }
 
 struct Work {
   half* kt;      // rotated keys       [bh][L][DK]
@@ -707,7 +708,7 @@ struct OutSmem {
   union {
     struct {
       half Ks[TK * QP];
-      half Vn[TK * VP];     // value tile [key][col] (fp16)
+      half Vn[TK * DV];     // value tile [key][col] (fp16), pieces swizzled (vswz)
     } kv;
   } u;
   half Ps[TR * KP];
@@ -887,12 +888,14 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
         const int key = e >> 6, piece = e & 63;
         u32x4 v = Raw16<T>::f16(vreg[i]);
         if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(sm.u.kv.Vn + key * VP + piece * 8) = v;
+        *reinterpret_cast<u32x4*>(sm.u.kv.Vn + key * DV + vswz(key, piece) * 8) = v;
       }
     };
     // this lane's transposed-read origin in a value tile: key 8 (lane / 32) +
     // (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
-    const int vtr = (8 * (lane >> 5) + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // (swizzled: the lane's key row has r % 4 = (lane / 4) % 4)
+    const int vtr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * DV + 4 * (lane & 1);
+    const int vtr_sw = ((lane >> 2) & 3) << 2, vtr_lo = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 
     // output tiles of this wave: query halves {0,1} x column tiles {2w, 2w+1}
     f32x16 O[2][2];
@@ -1049,8 +1052,8 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             // keys kb + 8 (lane / 32) + 0..7 of column (2w + jj) 32 + lane % 32
-            const half* vp = sm.u.kv.Vn + kb * VP + (2 * wave + jj) * 32 + vtr;
-            const f16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * VP);
+            const half* vp = sm.u.kv.Vn + kb * DV + vtr_row + ((((2 * wave + jj) * 4) ^ vtr_sw) + vtr_lo) * 8;
+            const f16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * DV);
             bv[buf][jj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           }
   #pragma unroll
