@@ -46,6 +46,7 @@ struct Work {
   half* Rt;      // state operands     [bh][nc][DV*DK]    (R_{i-1}, fragment order, rt_frag)
   float* Rs;     // operand scales     [bh][nc][NCB]
   float* zc;     // z_{i-1}            [bh][nc][DK]
+  half* dump;    // 8 KB that masked lanes of the state scan store to (never read)
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -70,6 +71,7 @@ size_t carve(void* base, int bh, int L, int B, Work* w) {
   const size_t o_Rt = take((size_t)bh * nc * DV * DK * 2);
   const size_t o_Rs = take((size_t)bh * nc * NCB * 4);
   const size_t o_zc = take((size_t)bh * nc * DK * 4);
+  const size_t o_dump = take(deltas ? 0 : NT3 * 16);
   if (w) {
     char* b = static_cast<char*>(base);
     w->kt = reinterpret_cast<half*>(b + o_kt);
@@ -79,6 +81,7 @@ size_t carve(void* base, int bh, int L, int B, Work* w) {
     w->Rt = reinterpret_cast<half*>(b + o_Rt);
     w->Rs = reinterpret_cast<float*>(b + o_Rs);
     w->zc = reinterpret_cast<float*>(b + o_zc);
+    w->dump = reinterpret_cast<half*>(b + o_dump);
   }
   return off;
 }
@@ -482,7 +485,13 @@ struct SScanSmem {
   float4 step[DK / 2];              // per pair: e^{i theta} and e^{i TK theta}
 };
 
-template <typename T>
+// Every global load and store in the tile loop is unconditional (phantom
+// tiles pad a short last chunk, masked lanes store to a scratch slot or repeat
+// a value another lane stores), and the next tile is loaded into the second
+// register set before any store of the current one: the waits for a tile's
+// loads then never include the (write-bandwidth-bound) stores of the
+// published states.  TPC = tiles per chunk (1 or 2); LEAD = column block 0.
+template <typename T, int TPC>
 __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SScanSmem& sm = *reinterpret_cast<SScanSmem*>(smem_raw);
@@ -492,13 +501,13 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
   const int g = xcd_local(blockIdx.x, gridDim.x);   // the column blocks of a head share an XCD
   const int cb = g % NCB64, bh = g / NCB64;
   const int bb = bh / p.h, head = bh % p.h;
-  const bool lead = cb == 0;
   Decay dec;
   dec.init(hp.gamma[head]);
   const bool xpos = (p.flags & RET_XPOS) != 0;
   const T* Kg = reinterpret_cast<const T*>(p.k) + bb * p.sk.b + head * p.sk.h;
   const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + cb * SCB;
   half* ktg = p.w.kt + (int64_t)bh * p.L * DK;
+  half* dump = p.w.dump + tid * 8;                   // 16-byte scratch slot of this thread
 
   if (xpos && tid < DK / 2) {
     float4 t;
@@ -516,7 +525,9 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
     for (int r = 0; r < 16; ++r)
       acc[jj][r] = p.state_in ? p.state_in[((int64_t)bh * DK + d0 + acc_row(r, lane)) * DV + cb * SCB + 32 * jj + l32]
                               : 0.f;
-  float z = (lead && p.z_in && tid < DK) ? p.z_in[(int64_t)bh * DK + tid] : 0.f;
+  // key-sum z of d = tid % 256 (threads tid and tid + 256 carry the same value)
+  const int zd = tid & (DK - 1);
+  float z = p.z_in ? p.z_in[(int64_t)bh * DK + zd] : 0.f;
 
   // staging maps: keys kq .. kq + 3, d 8 cq .. 8 cq + 7; value key vk, columns 8 vp ..
   const int cq = tid & 31, kq = 4 * (tid >> 5);
@@ -531,41 +542,49 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
   const int tro = (8 * (lane >> 5) + ((lane & 15) >> 2)) * DP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int trv = (8 * (lane >> 5) + ((lane & 15) >> 2)) * VBP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  // 64-key tiles are numbered over the whole sequence (chunks hold B / 64)
-  u32x4 kr[4], vr;
-  auto issue = [&](int kt) {
+  // 64-key tiles are numbered over the whole sequence, TPC per chunk (the
+  // last chunk's missing tiles are phantoms with no valid key)
+  struct Regs {
+    u32x4 k[4], v;
+  } ra, rb;
+  const int ntiles = p.nc * TPC;
+  auto issue = [&](int kt, Regs& R) {
     const int k0 = kt * TK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = min(k0 + kq + i, p.L - 1);
-      kr[i] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)key * p.sk.l + 8 * cq);
+      R.k[i] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)key * p.sk.l + 8 * cq);
     }
     const int key = min(k0 + vk, p.L - 1);
-    vr = *reinterpret_cast<const u32x4*>(Vg + (int64_t)key * p.sv.l + 8 * vp);
+    R.v = *reinterpret_cast<const u32x4*>(Vg + (int64_t)key * p.sv.l + 8 * vp);
   };
-  const int ntiles = (p.L + TK - 1) / TK;
-  const int tpc = p.B / TK;                          // tiles per full chunk
-  issue(0);
-  float dzp[8];
-  float gprev = 1.f;                                 // gamma^(B of the previous chunk)
+  issue(0, ra);
   __syncthreads();                                   // step table
-  for (int c = 0; c < p.nc; ++c) {
-    const int c0 = c * p.B;
-    const int Bc = min(p.B, p.L - c0);
-    const int nt = (Bc + TK - 1) / TK;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dzp[e] = 0.f;
-    for (int s = 0; s < nt; ++s) {
-      const int kt = c * tpc + s;
+
+  auto body = [&](auto lead_c) {
+    constexpr bool LEAD = decltype(lead_c)::value;
+    float dzp[8];
+    float gprev = 1.f;                               // gamma^(B of the previous chunk)
+    // tile s of chunk c from register set cur; the next tile goes to nxt
+    auto step = [&](int c, auto s_c, Regs& cur, Regs& nxt) {
+      constexpr int s = decltype(s_c)::value;
+      const int kt = c * TPC + s;
+      issue(min(kt + 1, ntiles - 1), nxt);
+      const int c0 = c * p.B;
+      const int Bc = min(p.B, p.L - c0);
       const int k0 = s * TK;                         // chunk-local first key of the tile
-      const int kvalid = min(TK, Bc - k0);
+      const int kvalid = min(TK, Bc - k0);           // <= 0 for a phantom tile
+      if (s == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dzp[e] = 0.f;
+      }
       // ---- stage the tile: rotate the keys (-> workspace), scale by zeta (->
       // LDS, key-sum); convert the value block (-> LDS)
       {
         float x[4][8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          Raw16<T>::f32(kr[i], x[i]);
+          Raw16<T>::f32(cur.k[i], x[i]);
           if (kq + i >= kvalid) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
@@ -587,7 +606,7 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kq + i;
-          if (lead && key < kvalid) st8(ktg + (int64_t)(c0 + k0 + key) * DK + 8 * cq, x[i]);
+          if (LEAD) st8(key < kvalid ? ktg + (int64_t)(c0 + k0 + key) * DK + 8 * cq : dump, x[i]);
           const float zt = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key) * dec.lg2);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -596,11 +615,10 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
           }
           st8(sm.Kz + key * DP + 8 * cq, x[i]);
         }
-        u32x4 v = Raw16<T>::f16(vr);
+        u32x4 v = Raw16<T>::f16(cur.v);
         if (vk >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(sm.Vb + vk * VBP + 8 * vp) = v;
       }
-      if (kt + 1 < ntiles) issue(kt + 1);
       if (s == 0) {
         // ---- publish R_{c-1}: per 32-column block, a power of two puts max |R| in [2^14, 2^15)
 #pragma unroll
@@ -623,7 +641,7 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
           for (int w = 0; w < NT3 / 64; ++w) m = fmaxf(m, sm.amaxw[w][jj]);
           const int e = scale_exp(m);
           down[jj] = ldexpf(1.f, -e);
-          if (tid == 0) p.w.Rs[((int64_t)bh * p.nc + c) * NCB + 2 * cb + jj] = ldexpf(1.f, e);
+          p.w.Rs[((int64_t)bh * p.nc + c) * NCB + 2 * cb + jj] = ldexpf(1.f, e);   // every thread: one value
         }
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
@@ -635,15 +653,15 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
                            acc[jj][4 * rg + 2] * down[jj], acc[jj][4 * rg + 3] * down[jj]};
             st4(sm.Rst + (32 * jj + l32) * RSP + d, x4);
           }
-        if (lead && tid < DK) {
+        if (LEAD) {
           // z_{c-1}: the key-sum of the previous chunk, summed over the waves in order
           if (c > 0) {
             float dz = 0.f;
 #pragma unroll
-            for (int w = 0; w < NT3 / 64; ++w) dz += sm.dzw[w][tid];
+            for (int w = 0; w < NT3 / 64; ++w) dz += sm.dzw[w][zd];
             z = gprev * z + dz;
           }
-          p.w.zc[((int64_t)bh * p.nc + c) * DK + tid] = z;
+          p.w.zc[((int64_t)bh * p.nc + c) * DK + zd] = z;
         }
         __syncthreads();
         // fragment order: the 64 pieces of one (32 columns, 16 d) block are contiguous
@@ -674,7 +692,7 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
           acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf, acc[jj], 0, 0, 0);
         }
       }
-      if (s == nt - 1 && lead) {
+      if (s == TPC - 1 && LEAD) {
         // this chunk's key-sum partials: lanes l and l + 32 share a piece
 #pragma unroll
         for (int e = 0; e < 8; ++e) dzp[e] += __shfl_xor(dzp[e], 32, 64);
@@ -684,15 +702,32 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
         }
       }
       __syncthreads();
+    };
+    typedef std::integral_constant<int, 0> S0;
+    typedef std::integral_constant<int, 1> S1;
+    if (TPC == 2) {
+      for (int c = 0; c < p.nc; ++c) {
+        step(c, S0{}, ra, rb);
+        step(c, S1{}, rb, ra);
+      }
+    } else {
+      int c = 0;
+      for (; c + 1 < p.nc; c += 2) {
+        step(c, S0{}, ra, rb);
+        step(c + 1, S0{}, rb, ra);
+      }
+      if (c < p.nc) step(c, S0{}, ra, rb);
     }
-  }
-  if (lead && tid < DK) {
-    float dz = 0.f;
+    if (LEAD) {
+      float dz = 0.f;
 #pragma unroll
-    for (int w = 0; w < NT3 / 64; ++w) dz += sm.dzw[w][tid];
-    z = gprev * z + dz;
-    if (p.z_out) p.z_out[(int64_t)bh * DK + tid] = z;
-  }
+      for (int w = 0; w < NT3 / 64; ++w) dz += sm.dzw[w][zd];
+      z = gprev * z + dz;
+      if (p.z_out && tid < DK) p.z_out[(int64_t)bh * DK + tid] = z;
+    }
+  };
+  if (cb == 0) body(std::true_type{});
+  else body(std::false_type{});
   if (p.state_out) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
@@ -1158,7 +1193,7 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
   carve(a.ws, bh, a.L, a.B, &p.w);
   hipError_t e;
   if (a.B <= SSCAN_MAX_B) {
-    auto k = sscan_kernel<T>;
+    auto k = a.B == 2 * TK ? sscan_kernel<T, 2> : sscan_kernel<T, 1>;
     e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SScanSmem));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(bh * (DV / SCB)), dim3(NT3), sizeof(SScanSmem), st, p, *a.hp);
