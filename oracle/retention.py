@@ -15,7 +15,8 @@ next to the code.  Sources (page title, section):
 * RetNet reading notes (mzeromiko.github.io, "阅读笔记：RetNet"):
   §2.1 architecture motivation (the complex-phase derivation),
   §2.2 recurrent mode, §2.3 parallel mode, §2.4 chunkwise recurrent mode,
-  §三.2 MSR module, §三.3 normalisation.
+  §三.2 MSR module, §三.3 normalisation, §四.4 single-layer structure
+  (LN, residuals and the gelu FFN around the MSR module).
 * zyxy.net lecture ("RetNet（Retentive Network）：多尺度指数衰减…"), §5
   multi-scale grouping: the head split of d_model into contiguous column
   blocks, shape (batch, heads, seq, d_head).
@@ -33,8 +34,12 @@ Parity status of each function (what pins it) is recorded in the test files
 under tests/ that start with ``test_oracle``.  Readings that are choices
 rather than facts of the pages ("parity unpinned" by the pages themselves):
 the real xPos layout (interleaved pairs, both q and k rotated by +p*theta),
-GroupNorm epsilon and affine, and the meaning of sigma in N(0, sigma).
+GroupNorm epsilon and affine, the meaning of sigma in N(0, sigma), and for
+the layer of §四.4 the LayerNorm variant (biased variance, eps, affine), the
+exact gelu x Phi(x), and the FFN width (a parameter).
 """
+
+import math
 
 import numpy as np
 
@@ -315,3 +320,59 @@ def msr_forward(X, WQ, WK, WV, WG, WO, h, theta, flags, chunk, eps):
     Y, _, _ = retention_chunkwise(Q, K, V, gammas(h), theta, flags, chunk)
     Z = gate_norm(Y, G, eps)
     return Z @ _f64(WO)
+
+
+# ---------------------------------------------------------------------------
+# One RetNet layer (reading notes §四.4, the single-layer structure):
+#   Y = MSR(LN(X)) + X,   X' = FFN(LN(Y)) + Y,   FFN(X) = gelu(X W_1) W_2
+# The page names LN and gelu without their variants; the readings taken are
+# LayerNorm over the model width with the biased variance, eps under the
+# square root and an optional per-channel affine, and the exact gelu
+# x Phi(x).  The FFN width is a parameter (the page does not state it).
+# ---------------------------------------------------------------------------
+
+_ERF = np.vectorize(math.erf, otypes=[np.float64])
+
+
+def _erf(x):
+    """erf of every element, by the standard library's math.erf (correctly
+    rounded to within an ulp or so)."""
+    return _ERF(_f64(x))
+
+
+def layer_norm(x, eps, weight=None, bias=None):
+    """LN over the last axis (d_model): (x - mean) / sqrt(biased var + eps),
+    then the optional per-channel affine (§四.4; variant: see above)."""
+    x = _f64(x)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    y = (x - mu) / np.sqrt(var + eps)
+    if weight is not None:
+        y = y * _f64(weight)
+    if bias is not None:
+        y = y + _f64(bias)
+    return y
+
+
+def gelu(x):
+    """gelu(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2 (§四.4, exact form)."""
+    x = _f64(x)
+    return 0.5 * x * (1.0 + _erf(x / np.sqrt(2.0)))
+
+
+def ffn(X, W1, W2):
+    """FFN(X) = gelu(X W_1) W_2 (§四.4).  W_1: [d_model, d_ff], W_2: [d_ff, d_model]."""
+    return gelu(_f64(X) @ _f64(W1)) @ _f64(W2)
+
+
+def retnet_layer(X, msr_w, W1, W2, h, theta, flags, chunk, gn_eps, ln_eps,
+                 ln1=(None, None), ln2=(None, None)):
+    """One RetNet layer (§四.4): Y = MSR(LN(X)) + X;  X' = FFN(LN(Y)) + Y.
+
+    msr_w = (W_Q, W_K, W_V, W_G, W_O) as in msr_forward; ln1 / ln2 are the
+    (weight, bias) of the two LayerNorms (None = 1 and 0).  Returns X' of the
+    shape of X."""
+    X = _f64(X)
+    WQ, WK, WV, WG, WO = msr_w
+    Y = msr_forward(layer_norm(X, ln_eps, *ln1), WQ, WK, WV, WG, WO, h, theta, flags, chunk, gn_eps) + X
+    return ffn(layer_norm(Y, ln_eps, *ln2), W1, W2) + Y

@@ -435,11 +435,82 @@ def pin_pages_shape_example(m):
     assert list(np.transpose(o2, (0, 2, 1, 3)).reshape(b, L, dm).shape) == ex["printed_shape"]
 
 
+def pin_layer_norm(m):
+    """LayerNorm of the RetNet layer (§四.4): [1,2,3,4] has mean 2.5 and biased
+    variance 1.25, so it maps to [-3,-1,1,3]/sqrt(5); rows are independent; eps
+    enters under the square root; the affine is per channel; and LN(a x + c) =
+    LN(x) for a > 0."""
+    x = np.array([[1.0, 2.0, 3.0, 4.0], [10.0, 10.0, 10.0, 14.0]])
+    y = m.layer_norm(x, 0.0)
+    _close(y[0], np.array([-3, -1, 1, 3]) / np.sqrt(5.0), 1e-15, "LN row 0")
+    _close(y[1], np.array([-1, -1, -1, 3]) / np.sqrt(3.0), 1e-15, "LN row 1")
+    _close(m.layer_norm(np.array([1.0, -1.0]), 3.0), [0.5, -0.5], 1e-15, "LN eps")
+    w = np.arange(1, 5, dtype=np.float64)
+    bb = -np.arange(4, dtype=np.float64)
+    _close(m.layer_norm(x, 0.0, w, bb), y * w + bb, 1e-15, "LN affine")
+    r = _rand((3, 5, 16), 90)
+    _close(m.layer_norm(2.5 * r + 7.0, 0.0), m.layer_norm(r, 0.0), 1e-12, "LN invariance")
+
+
+def pin_gelu(m):
+    """gelu(x) = x Phi(x) with the standard normal CDF Phi: gelu(0) = 0,
+    gelu(1) = Phi(1) = 0.8413447460685429, gelu(-1) = -(1 - Phi(1)),
+    gelu(2) = 2 Phi(2) = 2 * 0.9772498680518208 (textbook values of Phi);
+    gelu(x) - gelu(-x) = x since Phi(x) + Phi(-x) = 1; gelu(40) = 40,
+    gelu(-40) = 0.  FFN with identity weights is gelu itself (§四.4)."""
+    g = m.gelu(np.array([0.0, 1.0, -1.0, 2.0, 40.0, -40.0]))
+    assert g[0] == 0.0
+    assert abs(g[1] - 0.8413447460685429) < 1e-15
+    assert abs(g[2] + 0.15865525393145707) < 1e-15
+    assert abs(g[3] - 1.9544997361036416) < 1e-14
+    assert abs(g[4] - 40.0) < 1e-12 and abs(g[5]) < 1e-300
+    x = _rand((1000,), 91, 3.0)
+    _close(m.gelu(x) - m.gelu(-x), x, 1e-13, "gelu odd part")
+    eye = np.eye(6)
+    xx = _rand((2, 7, 6), 92)
+    _close(m.ffn(xx, eye, eye), m.gelu(xx), 1e-15, "FFN identity")
+    # the second weight is applied after gelu, the first before it
+    W1 = np.diag(np.arange(1.0, 7.0))
+    W2 = 2.0 * eye
+    _close(m.ffn(xx, W1, W2), 2.0 * m.gelu(xx * np.arange(1.0, 7.0)), 1e-14, "FFN order")
+
+
+def pin_retnet_layer(m):
+    """One RetNet layer (§四.4), Y = MSR(LN(X)) + X, X' = FFN(LN(Y)) + Y:
+    zero W_O and W_2 give X' = X; with W_2 = 0, X' - X = MSR(LN(X)) is
+    unchanged by a positive rescaling of X (LN sits before MSR); with W_O = 0
+    the same holds for the FFN branch; X' - Y is linear in W_2; and token t
+    of X' depends on tokens <= t only."""
+    b, L, dm, h, dk, dv, dff = 1, 13, 8, 2, 4, 4, 12
+    r = np.random.default_rng(93)
+    X = r.standard_normal((b, L, dm)) + 0.5
+    WQ, WK = r.standard_normal((dm, h * dk)), r.standard_normal((dm, h * dk))
+    WV, WG = r.standard_normal((dm, h * dv)), r.standard_normal((dm, h * dv))
+    WO = r.standard_normal((h * dv, dm))
+    W1, W2 = r.standard_normal((dm, dff)), r.standard_normal((dff, dm))
+    th = _thetas(dk)
+    flags = XPOS | NORM_ALL
+    lay = lambda X_, WO_, W2_: m.retnet_layer(X_, (WQ, WK, WV, WG, WO_), W1, W2_, h, th, flags, 5, 0.0, 0.0)
+    _close(lay(X, 0 * WO, 0 * W2), X, 0.0, "identity")
+    y1 = lay(X, WO, 0 * W2) - X
+    y2 = lay(3.0 * X, WO, 0 * W2) - 3.0 * X
+    _close(y2, y1, 1e-11, "pre-norm MSR branch")
+    assert np.max(np.abs(y1)) > 1e-3
+    f1 = lay(X, 0 * WO, W2) - X
+    f2 = lay(3.0 * X, 0 * WO, W2) - 3.0 * X
+    _close(f2, f1, 1e-11, "pre-norm FFN branch")
+    Y = lay(X, WO, 0 * W2)
+    _close(lay(X, WO, 2.0 * W2) - Y, 2.0 * (lay(X, WO, W2) - Y), 1e-11, "linear in W_2")
+    full = lay(X, WO, W2)
+    X2 = X.copy(); X2[:, 9:] += 5.0
+    _close(lay(X2, WO, W2)[:, :9], full[:, :9], 1e-12, "causal")
+
+
 ALL_PINS = [pin_gamma_theta, pin_forms_agree, pin_onehot_decay, pin_xpos_closed_form,
             pin_drow_scale_closed_form, pin_score_clamp, pin_groupnorm_invariance,
             pin_groupnorm_values, pin_swish, pin_relative_position, pin_split_resume,
             pin_causality_linearity, pin_decode_zero_kv, pin_decode_vs_chunkwise, pin_block,
-            pin_pages_shape_example]
+            pin_pages_shape_example, pin_layer_norm, pin_gelu, pin_retnet_layer]
 
 
 def quick_forms(m):
