@@ -8,7 +8,9 @@ inputs are resident in HBM before timing; three input/output buffer sets are
 rotated so the 256 MB MALL cannot serve a repeated set.  Secondary lines in
 the same JSON record: the same workload at B = 64, the long workload (L =
 32768, 16 heads), the decode step (batch 128, 16 heads, 64 steps from
-position 8192) and the GroupNorm + gate epilogue at the block shape.
+position 8192), the GroupNorm + gate epilogue at the block shape, the gated
+MSR block (2 x 8192 tokens, d_model 4096) and one RetNet layer around it
+(LayerNorms, residuals and a 4 x d_model gelu FFN).
 
 Prints ONE JSON line.  Only N = 1 GPU is supported.
 """
@@ -133,7 +135,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true", help="time the primary workload only")
-    ap.add_argument("--secondary", default="medium_B64,long,decode,gate_norm,block,copy",
+    ap.add_argument("--secondary", default="medium_B64,long,decode,gate_norm,block,layer,copy",
                     help="comma list of secondary measurements to run (empty for none)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -272,6 +274,26 @@ def main():
                           "tflops": round((gflop + rflop) / (msb * 1e-3) / 1e12, 1),
                           "gemm_gflop": round(gflop / 1e9, 1), "retention_gflop": round(rflop / 1e9, 1)}
         del Xd, wq, wk, wv, wg, wo
+        torch.cuda.empty_cache()
+    if "layer" in todo:
+        # one RetNet layer around the block: LN, MSR + residual, LN, FFN (4 x d_model, gelu) + residual
+        lc = W.LAYER
+        msr_w, W1, W2, ln1, ln2 = W.layer_inputs(**lc)
+        dT = lambda w: dev(np.ascontiguousarray(w.T))
+        vec = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+        Xd, ws, w1, w2 = dev(msr_w[0]), tuple(dT(w) for w in msr_w[1:]), dT(W1), dT(W2)
+        l1, l2 = (vec(ln1[0]), vec(ln1[1])), (vec(ln2[0]), vec(ln2[1]))
+        del msr_w, W1, W2
+        lg, lth = W.gamma_vector(lc["h"]), W.theta_vector(lc["dk"])
+        msl = time_calls(lambda: R.retnet_layer_fwd(Xd, ws, w1, w2, lg, lth, lc["chunk"], lc["flags"], lc["eps"],
+                                                     lc["ln_eps"], l1, l2), 3, 1, torch)
+        M, dm, hdk, hdv, dff = lc["b"] * lc["L"], lc["d_model"], lc["h"] * lc["dk"], lc["h"] * lc["dv"], lc["d_ff"]
+        gflop = 2 * M * dm * (2 * hdk + 2 * hdv) + 2 * M * hdv * dm + 4 * M * dm * dff
+        rflop = chunk_flops(lc["b"], lc["h"], lc["L"], lc["dk"], lc["dv"], lc["chunk"])
+        extra["layer"] = {"ms": round(msl, 3), "tokens_per_s": M / (msl * 1e-3),
+                          "tflops": round((gflop + rflop) / (msl * 1e-3) / 1e12, 1), "d_ff": dff,
+                          "gemm_gflop": round(gflop / 1e9, 1), "retention_gflop": round(rflop / 1e9, 1)}
+        del Xd, ws, w1, w2
         torch.cuda.empty_cache()
     if "gate_norm" in todo:
         # GroupNorm + gate at the block shape (2 x 8192 tokens, 16 heads x 512)

@@ -172,6 +172,39 @@ int msr_gate_norm(const void* y, ret_strides sy, const void* g, void* out,
 int msr_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
              hipStream_t stream);
 
+/*
+ * msr_gemm_ex -- msr_gemm with an epilogue, for the RetNet layer ([notes]
+ * §四.4: Y = MSR(LN(X)) + X, X' = FFN(LN(Y)) + Y, FFN(X) = gelu(X W_1) W_2):
+ *   C = act(A . B^T) (+ residual)
+ *   epilogue   MSR_GEMM_GELU applies the exact gelu x Phi(x) = x (1 +
+ *              erf(x / sqrt 2)) / 2 to each fp32 output (FFN's first
+ *              projection); 0 applies none
+ *   residual   device [M][N] row-major of r_dt (f32, bf16 or f16, which
+ *              need not be c_dt) added in fp32 after act (the layer's
+ *              residual connections), or NULL (r_dt is then ignored); it may
+ *              be C itself when r_dt == c_dt (each element is read, then
+ *              written, by one thread) but must not overlap A or B
+ * Everything else as msr_gemm.  Supported: K a multiple of 32; 16-byte
+ * aligned pointers.
+ */
+#define MSR_GEMM_GELU 1u
+int msr_gemm_ex(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                const void* residual, ret_dtype r_dt, unsigned epilogue, hipStream_t stream);
+
+/*
+ * ret_layer_norm -- the LayerNorm of the RetNet layer ([notes] §四.4):
+ *   y = (x - mean) / sqrt(biased variance + eps) over each row, then the
+ *   optional per-channel affine
+ *   x  device [rows][d] row-major of x_dt (f32, bf16 or f16)
+ *   y  device [rows][d] row-major of y_dt; must not overlap x
+ *   weight, bias  device float32 [d] or NULL (= 1 and 0)
+ * The page names LN without its variant; this biased-variance form with eps
+ * under the square root is the reading taken.  Supported: d a multiple of 8,
+ * 8 <= d <= 8192; 16-byte aligned pointers.
+ */
+int ret_layer_norm(const void* x, void* y, int rows, int d, const float* weight, const float* bias, float eps,
+                   ret_dtype x_dt, ret_dtype y_dt, hipStream_t stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* retention_last_error(void);
 

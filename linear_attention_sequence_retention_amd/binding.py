@@ -49,6 +49,10 @@ def load_library(path=LIB_PATH):
     lib.msr_gate_norm.restype = i32
     lib.msr_gemm.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp]
     lib.msr_gemm.restype = i32
+    lib.msr_gemm_ex.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, u32, vp]
+    lib.msr_gemm_ex.restype = i32
+    lib.ret_layer_norm.argtypes = [vp, vp, i32, i32, vp, vp, f32, i32, i32, vp]
+    lib.ret_layer_norm.restype = i32
     lib.retention_last_error.argtypes = []
     lib.retention_last_error.restype = ctypes.c_char_p
     lib.retention_abi_version.argtypes = []
@@ -171,8 +175,10 @@ def gate_norm(y, g, eps, weight=None, bias=None, out=None, out_dtype=None, strea
     return out
 
 
-def gemm(a, b_nk, out=None, out_dtype=torch.bfloat16, stream=None):
-    """C = a . b_nk^T for a [M, K] (bf16 or fp16) and a bf16 weight b_nk [N, K]."""
+def gemm(a, b_nk, out=None, out_dtype=torch.bfloat16, residual=None, gelu=False, stream=None):
+    """C = act(a . b_nk^T) (+ residual) for a [M, K] (bf16 or fp16) and a bf16
+    weight b_nk [N, K]; act is the exact gelu when gelu is set, and residual
+    ([M, N], float32, bf16 or fp16, added in fp32) may be out itself."""
     if a.dtype not in (torch.bfloat16, torch.float16) or b_nk.dtype != torch.bfloat16:
         raise TypeError("gemm takes a bf16 or fp16 A and a bf16 weight")
     if not a.is_contiguous() or not b_nk.is_contiguous():
@@ -183,22 +189,52 @@ def gemm(a, b_nk, out=None, out_dtype=torch.bfloat16, stream=None):
         raise ValueError("inner dimensions differ")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    st = LIB.msr_gemm(_ptr(a), _dt(a), _ptr(b_nk), _ptr(out), _dt(out), M, N, K, _stream(stream))
-    _check(st, "msr_gemm")
+    if residual is None and not gelu:
+        st = LIB.msr_gemm(_ptr(a), _dt(a), _ptr(b_nk), _ptr(out), _dt(out), M, N, K, _stream(stream))
+        _check(st, "msr_gemm")
+        return out
+    if residual is not None:
+        if tuple(residual.shape) != (M, N) or not residual.is_contiguous():
+            raise ValueError("residual must be a contiguous [M, N] tensor")
+    st = LIB.msr_gemm_ex(_ptr(a), _dt(a), _ptr(b_nk), _ptr(out), _dt(out), M, N, K, _ptr(residual),
+                         _dt(out if residual is None else residual), 1 if gelu else 0, _stream(stream))
+    _check(st, "msr_gemm_ex")
+    return out
+
+
+def layer_norm(x, eps, weight=None, bias=None, out=None, out_dtype=None, stream=None):
+    """LayerNorm over the last axis (RetNet reading notes, §四.4): biased
+    variance, eps under the square root, optional float32 affine."""
+    if not x.is_contiguous():
+        raise ValueError("layer_norm needs a contiguous input")
+    d = x.shape[-1]
+    rows = x.numel() // d
+    if out is None:
+        out = torch.empty(x.shape, dtype=x.dtype if out_dtype is None else out_dtype, device=x.device)
+    if not out.is_contiguous() or out.numel() != x.numel():
+        raise ValueError("out must be contiguous and of x's size")
+    for t, name in ((weight, "weight"), (bias, "bias")):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != d or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 vector of {d}")
+    st = LIB.ret_layer_norm(_ptr(x), _ptr(out), rows, d, _ptr(weight), _ptr(bias), float(eps), _dt(x), _dt(out),
+                            _stream(stream))
+    _check(st, "ret_layer_norm")
     return out
 
 
 def msr_block_fwd(x, wq_t, wk_t, wv_t, wg_t, wo_t, gamma, theta, chunk, flags, eps, out_dtype=torch.bfloat16,
-                  stream=None):
+                  residual=None, stream=None):
     """Gated multi-scale retention block forward (RetNet reading notes, §三.2):
     MSR(X) = (swish(X W_G) (.) GroupNorm_h(Retention heads)) W_O.
 
-    x: [b, L, d_model] bf16; w*_t: weights as [out_features, in_features] bf16;
+    x: [b, L, d_model] bf16 or fp16; w*_t: weights as [out_features,
+    in_features] bf16;
     gamma: the h per-head decays (host float64).
     Every step runs in the library's kernels: four projections, the
     chunkwise retention over [b, h, L, d] views of the projections, the
-    GroupNorm + swish gate, and the output projection.  Intermediates (the
-    projections, the head outputs and the gated heads) are stored as fp16.
+    GroupNorm + swish gate, and the output projection, whose epilogue adds
+    residual ([b*L, d_model] of out_dtype) when one is given.  Intermediates
+    (the projections, the head outputs and the gated heads) are stored as fp16.
     """
     b, L, dm = x.shape
     h = len(gamma)
@@ -217,5 +253,32 @@ def msr_block_fwd(x, wq_t, wk_t, wv_t, wg_t, wo_t, gamma, theta, chunk, flags, e
     yv = Y.view(b, L, h, dv).transpose(1, 2)
     chunkwise_fwd(qv, kv, vv, gamma, theta, chunk, flags, out=yv, stream=stream)
     Z = gate_norm(yv, G.view(b, L, h * dv), eps, stream=stream)
-    out = gemm(Z.view(b * L, h * dv), wo_t, out_dtype=out_dtype, stream=stream)
+    out = gemm(Z.view(b * L, h * dv), wo_t, out_dtype=out_dtype, residual=residual, stream=stream)
     return out.view(b, L, -1)
+
+
+def retnet_layer_fwd(x, msr_w_t, w1_t, w2_t, gamma, theta, chunk, flags, gn_eps, ln_eps, ln1=(None, None),
+                     ln2=(None, None), stream=None):
+    """One RetNet layer forward (reading notes §四.4):
+        Y = MSR(LN(X)) + X,   X' = FFN(LN(Y)) + Y,   FFN(Y) = gelu(Y W_1) W_2.
+
+    x: [b, L, d_model] float32 or bf16; the result has x's dtype;
+    msr_w_t: (W_Q, W_K, W_V, W_G, W_O) as [out_features, in_features] bf16;
+    w1_t: [d_ff, d_model] and w2_t: [d_model, d_ff] bf16; ln1 / ln2: the two
+    LayerNorms' float32 (weight, bias), None for 1 and 0.  Every step runs in
+    the library: the LayerNorms (stored as fp16, the GEMMs' activation
+    operand), the MSR block whose output projection adds X in its epilogue
+    and keeps Y in float32, the first FFN projection with gelu in its
+    epilogue (hidden stored as fp16) and the second with Y added.
+    """
+    if x.dtype not in (torch.float32, torch.bfloat16) or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 or bf16 tensor")
+    b, L, dm = x.shape
+    x2 = x.view(b * L, dm)
+    xn = layer_norm(x2, ln_eps, *ln1, out_dtype=torch.float16, stream=stream)
+    Y = msr_block_fwd(xn.view(b, L, dm), *msr_w_t, gamma, theta, chunk, flags, gn_eps, out_dtype=torch.float32,
+                      residual=x2, stream=stream).view(b * L, dm)
+    yn = layer_norm(Y, ln_eps, *ln2, out_dtype=torch.float16, stream=stream)
+    H = gemm(yn, w1_t, out_dtype=torch.float16, gelu=True, stream=stream)
+    out = gemm(H, w2_t, out_dtype=x.dtype, residual=Y, stream=stream)
+    return out.view(b, L, dm)

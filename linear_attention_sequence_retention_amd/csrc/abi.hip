@@ -188,16 +188,41 @@ int msr_gate_norm(const void* y, ret_strides sy, const void* g, void* out,
   return hip_status(ret::launch_gate_norm(a, stream), "msr_gate_norm launch");
 }
 
-int msr_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
-             hipStream_t stream) {
+int msr_gemm_ex(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                const void* residual, ret_dtype r_dt, unsigned epilogue, hipStream_t stream) {
   if (M <= 0 || N <= 0 || K <= 0) return fail(RET_E_INVAL, "sizes must be positive (M=%d N=%d K=%d)", M, N, K);
   if (K % 32) return fail(RET_E_UNSUPPORTED, "K must be a multiple of 32 (got %d)", K);
-  if (!valid_dt(c_dt) || !valid_dt(a_dt)) return fail(RET_E_INVAL, "unknown dtype");
+  if (!valid_dt(c_dt) || !valid_dt(a_dt) || (residual && !valid_dt(r_dt))) return fail(RET_E_INVAL, "unknown dtype");
   if (a_dt == RET_F32) return fail(RET_E_UNSUPPORTED, "A must be bf16 or f16");
+  if (epilogue & ~(unsigned)MSR_GEMM_GELU) return fail(RET_E_INVAL, "unknown epilogue bits 0x%x", epilogue);
   if (!A || !B || !C) return fail(RET_E_INVAL, "A, B and C must be non-NULL");
-  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16)) return fail(RET_E_ALIGN, "A, B and C must be 16-byte aligned");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || (residual && !aligned(residual, 16)))
+    return fail(RET_E_ALIGN, "A, B, C and residual must be 16-byte aligned");
   if (C == A || C == B) return fail(RET_E_INVAL, "C must not alias A or B");
-  return hip_status(ret::launch_gemm(A, a_dt, B, C, c_dt, M, N, K, stream), "msr_gemm launch");
+  if (residual && (residual == A || residual == B)) return fail(RET_E_INVAL, "residual must not alias A or B");
+  if (residual == C && r_dt != c_dt) return fail(RET_E_INVAL, "a residual that is C must have C's dtype");
+  return hip_status(ret::launch_gemm(A, a_dt, B, C, c_dt, M, N, K, residual, r_dt, (epilogue & MSR_GEMM_GELU) ? 1 : 0,
+                                     stream),
+                    "msr_gemm launch");
+}
+
+int msr_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+             hipStream_t stream) {
+  return msr_gemm_ex(A, a_dt, B, C, c_dt, M, N, K, nullptr, c_dt, 0u, stream);
+}
+
+int ret_layer_norm(const void* x, void* y, int rows, int d, const float* weight, const float* bias, float eps,
+                   ret_dtype x_dt, ret_dtype y_dt, hipStream_t stream) {
+  if (rows <= 0 || d <= 0) return fail(RET_E_INVAL, "sizes must be positive (rows=%d d=%d)", rows, d);
+  if (d % 8 || d > 8192) return fail(RET_E_UNSUPPORTED, "d must be a multiple of 8 and <= 8192 (got %d)", d);
+  if (!valid_dt(x_dt) || !valid_dt(y_dt)) return fail(RET_E_INVAL, "unknown dtype");
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(RET_E_INVAL, "eps must be finite and >= 0");
+  if (!x || !y) return fail(RET_E_INVAL, "x and y must be non-NULL");
+  if (!aligned(x, 16) || !aligned(y, 16) || (weight && !aligned(weight, 16)) || (bias && !aligned(bias, 16)))
+    return fail(RET_E_ALIGN, "x, y, weight and bias must be 16-byte aligned");
+  if (x == y) return fail(RET_E_INVAL, "y must not alias x");
+  return hip_status(ret::launch_layer_norm(x, y, rows, d, weight, bias, eps, x_dt, y_dt, stream),
+                    "ret_layer_norm launch");
 }
 
 }  // extern "C"

@@ -136,6 +136,97 @@ static hipError_t launch_gn_g(const GateArgs& a, hipStream_t st) {
   if (a.g_dt == RET_F16) return launch_gn_o<TY, half>(a, st);
   return launch_gn_o<TY, float>(a, st);
 }
+// ---------------------------------------------------------------- LayerNorm
+// The two LayerNorms of the RetNet layer (reading notes §四.4: Y = MSR(LN(X))
+// + X, X' = FFN(LN(Y)) + Y): each row of d values (one token) is normalised by
+// its mean and biased variance (eps added to the variance), then the optional
+// per-channel affine.  One wave per row, the row in registers (8 values per
+// lane per 512-wide slab); HBM-bound: x read once, y written once.
+template <typename TX, typename TY, int NI>
+__global__ void __launch_bounds__(256)
+layer_norm_kernel(const TX* __restrict__ x, TY* __restrict__ y, int rows, int d, const float* __restrict__ w,
+                  const float* __restrict__ bias, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const TX* xp = x + row * d;
+  float v[NI][8];
+  float sum = 0.f;
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int e = 8 * lane + 512 * it;
+    if (e < d) {
+      Vec8<TX>::ld(xp + e, v[it]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum += v[it][j];
+    }
+  }
+  const float inv_n = 1.f / (float)d;
+  const float mean = wave_sum(sum) * inv_n;
+  float sq = 0.f;
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int e = 8 * lane + 512 * it;
+    if (e < d) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float t = v[it][j] - mean;
+        sq += t * t;
+      }
+    }
+  }
+  const float rstd = rsqrtf(wave_sum(sq) * inv_n + eps);
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int e = 8 * lane + 512 * it;
+    if (e < d) {
+      float r[8], wv[8], bv[8];
+      if (w) Vec8<float>::ld(w + e, wv);
+      if (bias) Vec8<float>::ld(bias + e, bv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float t = (v[it][j] - mean) * rstd;
+        if (w) t *= wv[j];
+        if (bias) t += bv[j];
+        r[j] = t;
+      }
+      Vec8<TY>::st(y + row * d + e, r);
+    }
+  }
+}
+
+template <typename TX, typename TY>
+static hipError_t launch_ln_t(const void* x, void* y, int rows, int d, const float* w, const float* bias, float eps,
+                              hipStream_t st) {
+  dim3 grid((unsigned)((rows + 3) / 4));
+  const int ni = (d + 511) / 512;
+#define RET_LN(NI)                                                                                         \
+  hipLaunchKernelGGL((layer_norm_kernel<TX, TY, NI>), grid, dim3(256), 0, st, (const TX*)x, (TY*)y, rows, d, \
+                     w, bias, eps)
+  if (ni <= 1) RET_LN(1);
+  else if (ni <= 2) RET_LN(2);
+  else if (ni <= 4) RET_LN(4);
+  else if (ni <= 8) RET_LN(8);
+  else RET_LN(16);
+#undef RET_LN
+  return hipGetLastError();
+}
+
+template <typename TX>
+static hipError_t launch_ln_o(const void* x, void* y, int rows, int d, const float* w, const float* bias, float eps,
+                              ret_dtype y_dt, hipStream_t st) {
+  if (y_dt == RET_BF16) return launch_ln_t<TX, bf16>(x, y, rows, d, w, bias, eps, st);
+  if (y_dt == RET_F16) return launch_ln_t<TX, half>(x, y, rows, d, w, bias, eps, st);
+  return launch_ln_t<TX, float>(x, y, rows, d, w, bias, eps, st);
+}
+
+hipError_t launch_layer_norm(const void* x, void* y, int rows, int d, const float* w, const float* bias, float eps,
+                             ret_dtype x_dt, ret_dtype y_dt, hipStream_t st) {
+  if (x_dt == RET_BF16) return launch_ln_o<bf16>(x, y, rows, d, w, bias, eps, y_dt, st);
+  if (x_dt == RET_F16) return launch_ln_o<half>(x, y, rows, d, w, bias, eps, y_dt, st);
+  return launch_ln_o<float>(x, y, rows, d, w, bias, eps, y_dt, st);
+}
+
 hipError_t launch_gate_norm(const GateArgs& a, hipStream_t st) {
   if (a.y_dt == RET_BF16) return launch_gn_g<bf16>(a, st);
   if (a.y_dt == RET_F16) return launch_gn_g<half>(a, st);

@@ -13,6 +13,12 @@
 // one barrier per slab), and within a slab the fragments of step s + 1 are
 // read while step s multiplies.  Rows and columns beyond M / N are clamped on
 // load and skipped on store; K must be a multiple of 32.
+//
+// Epilogue options (the RetNet layer, reading notes §四.4): the exact gelu
+// x Phi(x) of each output (FFN's first projection), then the addition of a
+// residual (the layer's two residual connections) stored as fp32, bf16 or
+// fp16 independently of the output, so that an fp32 residual stream can feed
+// a bf16 result and the reverse.
 #include "internal.h"
 
 namespace ret {
@@ -59,10 +65,20 @@ template <> struct GemmOp<half> {
   __device__ __forceinline__ static u32x4 cvt_b(u32x4 u) { return bf16x8_to_f16x8(u); }
 };
 
+__device__ __forceinline__ float gelu_exact(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
+
+// residual element as fp32; r_dt is uniform over the launch
+__device__ __forceinline__ float ld_residual(const void* R, int r_dt, size_t i) {
+  if (r_dt == RET_F32) return static_cast<const float*>(R)[i];
+  if (r_dt == RET_BF16) return Elem<bf16>::ld(static_cast<const bf16*>(R) + i);
+  return Elem<half>::ld(static_cast<const half*>(R) + i);
+}
+
+// C may be the residual itself (each element is read, then written, by one thread)
 template <typename TA, typename TO, int BK>
 __global__ void __launch_bounds__(GT, 1)
-gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, TO* __restrict__ C,
-               int M, int N, int K, int tiles_n) {
+gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, TO* C,
+               int M, int N, int K, int tiles_n, const void* R, int r_dt, int act) {
   typedef GemmOp<TA> G;
   constexpr int LP = GemmSmem<BK>::LP;
   constexpr int A_LD = BM * BK / 8 / GT;   // 16-byte loads per thread per slab
@@ -160,43 +176,51 @@ gemm_nt_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, T
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm + i * 32 + acc_row(r, lane);
-          if (row < M) C[(size_t)row * N + col] = Store<TO>::cvt(acc[i][j][r]);
+          if (row < M) {
+            float v = acc[i][j][r];
+            if (act) v = gelu_exact(v);
+            if (R) v += ld_residual(R, r_dt, (size_t)row * N + col);
+            C[(size_t)row * N + col] = Store<TO>::cvt(v);
+          }
         }
       }
     }
 }
 
 template <typename TA, typename TO, int BK>
-static hipError_t launch_gemm_k(const void* A, const void* B, void* C, int M, int N, int K, hipStream_t st) {
+static hipError_t launch_gemm_k(const void* A, const void* B, void* C, int M, int N, int K, const void* R,
+                                int r_dt, int act, hipStream_t st) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const size_t sh = sizeof(GemmSmem<BK>);
   auto kern = gemm_nt_kernel<TA, TO, BK>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(GT), sh, st, (const uint16_t*)A, (const uint16_t*)B,
-                     (TO*)C, M, N, K, tiles_n);
+                     (TO*)C, M, N, K, tiles_n, R, r_dt, act);
   return hipGetLastError();
 }
 
 template <typename TA, typename TO>
-static hipError_t launch_gemm_t(const void* A, const void* B, void* C, int M, int N, int K, hipStream_t st) {
-  return K % 64 == 0 ? launch_gemm_k<TA, TO, 64>(A, B, C, M, N, K, st) : launch_gemm_k<TA, TO, 32>(A, B, C, M, N, K, st);
+static hipError_t launch_gemm_t(const void* A, const void* B, void* C, int M, int N, int K, const void* R,
+                                int r_dt, int act, hipStream_t st) {
+  return K % 64 == 0 ? launch_gemm_k<TA, TO, 64>(A, B, C, M, N, K, R, r_dt, act, st)
+                     : launch_gemm_k<TA, TO, 32>(A, B, C, M, N, K, R, r_dt, act, st);
 }
 
 template <typename TA>
 static hipError_t launch_gemm_a(const void* A, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
-                                hipStream_t st) {
-  if (c_dt == RET_BF16) return launch_gemm_t<TA, bf16>(A, B, C, M, N, K, st);
-  if (c_dt == RET_F16) return launch_gemm_t<TA, half>(A, B, C, M, N, K, st);
-  return launch_gemm_t<TA, float>(A, B, C, M, N, K, st);
+                                const void* R, int r_dt, int act, hipStream_t st) {
+  if (c_dt == RET_BF16) return launch_gemm_t<TA, bf16>(A, B, C, M, N, K, R, r_dt, act, st);
+  if (c_dt == RET_F16) return launch_gemm_t<TA, half>(A, B, C, M, N, K, R, r_dt, act, st);
+  return launch_gemm_t<TA, float>(A, B, C, M, N, K, R, r_dt, act, st);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
-                       hipStream_t st) {
-  return a_dt == RET_F16 ? launch_gemm_a<half>(A, B, C, c_dt, M, N, K, st)
-                         : launch_gemm_a<bf16>(A, B, C, c_dt, M, N, K, st);
+                       const void* R, ret_dtype r_dt, int act, hipStream_t st) {
+  return a_dt == RET_F16 ? launch_gemm_a<half>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, st)
+                         : launch_gemm_a<bf16>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, st);
 }
 
 }  // namespace ret

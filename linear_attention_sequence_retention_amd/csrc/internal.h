@@ -79,7 +79,10 @@ bool three_phase_applies(ret_dtype in_dt, int dk, int dv, int B);
 size_t three_phase_workspace(int b, int h, int L, int B);
 hipError_t launch_three_phase(const ChunkArgs& a, hipStream_t st);
 
+// R: optional residual [M][N] of c_dt added after the optional exact gelu (act != 0)
 hipError_t launch_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
-                       hipStream_t st);
+                       const void* R, ret_dtype r_dt, int act, hipStream_t st);
+hipError_t launch_layer_norm(const void* x, void* y, int rows, int d, const float* w, const float* bias, float eps,
+                             ret_dtype x_dt, ret_dtype y_dt, hipStream_t st);
 
 }  // namespace ret

@@ -91,6 +91,11 @@ DECODE = dict(b=128, h=16, dk=256, dv=512, s0_sigma=0.1, sigma=1.0 / 16,
 BLOCK = dict(b=2, L=8192, d_model=4096, h=16, dk=256, dv=512, x_sigma=1.0,
              w_sigma=0.02, chunk=512, flags=XPOS | NORM_ALL, eps=1e-5)
 
+# One RetNet layer (reading notes §四.4) around the block workload: the FFN
+# width is not stated there; the one width the pages print is the hotelren.com
+# article's example model (§5.1: hidden 768, FFN 3072), i.e. 4 x d_model.
+LAYER = dict(BLOCK, d_ff=4 * BLOCK['d_model'], ln_eps=1e-5, ln_sigma=0.1)
+
 
 def workload_name(cfg, chunk=None):
     s = f"b{cfg['b']}_h{cfg['h']}_L{cfg['L']}_dk{cfg['dk']}_dv{cfg['dv']}_{cfg['dtype']}"
@@ -128,3 +133,18 @@ def block_inputs(b, L, d_model, h, dk, dv, x_sigma, w_sigma, seed=0, **_):
     WG = draw(rng, (d_model, h * dv), w_sigma, 'bf16')
     WO = draw(rng, (h * dv, d_model), w_sigma, 'bf16')
     return X, WQ, WK, WV, WG, WO
+
+
+def layer_inputs(b, L, d_model, h, dk, dv, d_ff, x_sigma, w_sigma, ln_sigma, seed=0, **_):
+    """The block's X, W_Q, W_K, W_V, W_G, W_O, then W_1 [d_model, d_ff] and
+    W_2 [d_ff, d_model] (bf16, N(0, w_sigma)), then the two LayerNorms'
+    float32 (weight, bias): weight 1 + N(0, ln_sigma), bias N(0, ln_sigma)."""
+    X, WQ, WK, WV, WG, WO = block_inputs(b, L, d_model, h, dk, dv, x_sigma, w_sigma, seed=seed)
+    rng = np.random.default_rng([seed, 1])
+    W1 = draw(rng, (d_model, d_ff), w_sigma, 'bf16')
+    W2 = draw(rng, (d_ff, d_model), w_sigma, 'bf16')
+    ln = []
+    for _i in range(2):
+        w = (1.0 + draw(rng, (d_model,), ln_sigma, 'f32')).astype(np.float32)
+        ln.append((w, draw(rng, (d_model,), ln_sigma, 'f32')))
+    return (X, WQ, WK, WV, WG, WO), W1, W2, ln[0], ln[1]

@@ -1,0 +1,153 @@
+"""Parity of the RetNet layer pieces (reading notes §四.4) with the fp64
+oracle: the LayerNorm kernel, the GEMM's gelu / residual epilogue, and the
+whole layer Y = MSR(LN(X)) + X, X' = FFN(LN(Y)) + Y composed from library
+calls."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, announce, check, check_bf16_out, dev, f64, host64
+from linear_attention_sequence_retention_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def R():
+    from linear_attention_sequence_retention_amd import binding
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return binding
+
+
+def _vec(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+@pytest.mark.parametrize("rows,d", [(1, 8), (37, 520), (300, 4096), (5, 8192), (129, 1000)])
+@pytest.mark.parametrize("affine", [False, True])
+def test_layer_norm(R, rows, d, affine):
+    rng = np.random.default_rng(rows * 7 + d)
+    x = W.draw(rng, (rows, d), 2.0, "bf16")
+    # a row offset, so that the mean matters
+    x32 = (W.as_f32(x, "bf16") + np.float32(3.0)).astype(np.float32)
+    w = (1.0 + W.draw(rng, (d,), 0.2, "f32")).astype(np.float32) if affine else None
+    bias = W.draw(rng, (d,), 0.2, "f32") if affine else None
+    wd = None if w is None else _vec(w)
+    bd = None if bias is None else _vec(bias)
+    ref = oracle.layer_norm(x32.astype(np.float64), 1e-5, w, bias)
+    announce(f"layer_norm rows{rows} d{d} affine{affine}")
+    y32 = R.layer_norm(dev(x32, "f32"), 1e-5, wd, bd)
+    ybf = R.layer_norm(dev(x32, "f32"), 1e-5, wd, bd, out_dtype=torch.bfloat16)
+    y_from_bf = R.layer_norm(dev(x, "bf16"), 1e-5, wd, bd, out_dtype=torch.float32)
+    y16 = R.layer_norm(dev(x32, "f32"), 1e-5, wd, bd, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    # fp16 output (the layer's GEMM operand): within half an fp16 ulp of the
+    # exact value, plus the fp32 bar
+    g16 = host64(y16)
+    ulp_half = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -14))) - 11)
+    excess = np.max(np.maximum(np.abs(g16 - ref) - ulp_half, 0.0)) / np.sqrt(np.mean(ref ** 2))
+    print(f"[parity] layer_norm {rows}x{d} f32->f16: beyond output rounding = {excess:.3e}", flush=True)
+    assert excess <= TOL["f32"]
+    check(f"layer_norm {rows}x{d} f32->f32", host64(y32), ref, TOL["f32"])
+    check_bf16_out(f"layer_norm {rows}x{d} f32->bf16", host64(ybf), ref, TOL["bf16"])
+    ref_bf = oracle.layer_norm(f64(x, "bf16"), 1e-5, w, bias)
+    check(f"layer_norm {rows}x{d} bf16->f32", host64(y_from_bf), ref_bf, TOL["f32"])
+
+
+def test_layer_norm_rejects(R):
+    x = torch.zeros((4, 12), dtype=torch.float32, device="cuda")
+    with pytest.raises(RuntimeError):
+        R.layer_norm(x, 1e-5)                      # d not a multiple of 8
+    x = torch.zeros((4, 16), dtype=torch.float32, device="cuda")
+    with pytest.raises(RuntimeError):
+        R.layer_norm(x, -1.0)                      # negative eps
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 256), (1, 1000, 96), (513, 257, 4096)])
+def test_gemm_epilogue(R, M, N, K):
+    rng = np.random.default_rng(M * 3 + N + K)
+    a = W.draw(rng, (M, K), 1.0, "bf16")
+    b = W.draw(rng, (N, K), 1.0 / np.sqrt(K), "bf16")
+    r = W.draw(rng, (M, N), 1.0, "f32")
+    z = f64(a, "bf16") @ f64(b, "bf16").T
+    announce(f"gemm epilogue M{M} N{N} K{K}")
+    ad, bd = dev(a, "bf16"), dev(b, "bf16")
+    g32 = R.gemm(ad, bd, out_dtype=torch.float32, gelu=True)
+    res32 = R.gemm(ad, bd, out_dtype=torch.float32, residual=dev(r, "f32"))
+    both = R.gemm(ad, bd, out_dtype=torch.float32, gelu=True, residual=dev(r, "f32"))
+    inplace = dev(r, "f32")
+    R.gemm(ad, bd, out=inplace, gelu=True, residual=inplace)
+    rbf = W.f32_to_bf16_bits(r)
+    gbf = R.gemm(ad, bd, out_dtype=torch.bfloat16, gelu=True, residual=dev(rbf, "bf16"))
+    # residual dtype other than the output's: fp32 stream into bf16, bf16 and fp16 into fp32
+    bf_from32 = R.gemm(ad, bd, out_dtype=torch.bfloat16, residual=dev(r, "f32"))
+    f32_from_bf = R.gemm(ad, bd, out_dtype=torch.float32, gelu=True, residual=dev(rbf, "bf16"))
+    r16 = r.astype(np.float16)
+    f32_from_16 = R.gemm(ad, bd, out_dtype=torch.float32, residual=torch.from_numpy(r16).cuda())
+    torch.cuda.synchronize()
+    check(f"gemm gelu {M}x{N}x{K}", host64(g32), oracle.gelu(z), TOL["f32"])
+    check(f"gemm residual {M}x{N}x{K}", host64(res32), z + r, TOL["f32"])
+    check(f"gemm gelu+residual {M}x{N}x{K}", host64(both), oracle.gelu(z) + r, TOL["f32"])
+    check(f"gemm gelu+residual in place {M}x{N}x{K}", host64(inplace), oracle.gelu(z) + r, TOL["f32"])
+    check_bf16_out(f"gemm gelu+residual bf16 {M}x{N}x{K}", host64(gbf), oracle.gelu(z) + f64(rbf, "bf16"),
+                   TOL["bf16"])
+    check_bf16_out(f"gemm f32 residual into bf16 {M}x{N}x{K}", host64(bf_from32), z + r, TOL["bf16"])
+    check(f"gemm gelu + bf16 residual into f32 {M}x{N}x{K}", host64(f32_from_bf), oracle.gelu(z) + f64(rbf, "bf16"),
+          TOL["f32"])
+    check(f"gemm f16 residual into f32 {M}x{N}x{K}", host64(f32_from_16), z + r16.astype(np.float64), TOL["f32"])
+
+
+def test_gemm_epilogue_rejects(R):
+    a = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((64, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(RuntimeError):       # C as its own residual under another dtype is refused
+        R._check(R.LIB.msr_gemm_ex(R._ptr(a), R._dt(a), R._ptr(b), R._ptr(c), R._dt(c), 64, 64, 64, R._ptr(c),
+                                   R._dt(a), 0, None), "msr_gemm_ex")
+    with pytest.raises(RuntimeError):       # unknown epilogue bits
+        R._check(R.LIB.msr_gemm_ex(R._ptr(a), R._dt(a), R._ptr(b), R._ptr(c), R._dt(c), 64, 64, 64, None,
+                                   R._dt(c), 6, None), "msr_gemm_ex")
+
+
+def _layer_case(R, cfg, seed, x_dtype, check_tokens=None):
+    msr_w, W1, W2, ln1, ln2 = W.layer_inputs(**cfg, seed=seed)
+    X = msr_w[0]
+    h, dk = cfg["h"], cfg["dk"]
+    th = W.theta_vector(dk)
+    flags = cfg.get("flags", W.XPOS | W.NORM_ALL)
+    eps, ln_eps, chunk = cfg.get("eps", 1e-5), cfg["ln_eps"], cfg["chunk"]
+    dT = lambda w: dev(np.ascontiguousarray(w.T), "bf16")     # [out, in] on the device
+    lnd = lambda p: (_vec(p[0]), _vec(p[1]))
+    xd = dev(X, "bf16") if x_dtype == "bf16" else dev(W.as_f32(X, "bf16"), "f32")
+    announce(f"retnet layer b{cfg['b']} L{cfg['L']} dm{cfg['d_model']} dff{cfg['d_ff']} x {x_dtype}")
+    out = R.retnet_layer_fwd(xd, tuple(dT(w) for w in msr_w[1:]), dT(W1), dT(W2), W.gamma_vector(h), th, chunk,
+                             flags, eps, ln_eps, lnd(ln1), lnd(ln2))
+    torch.cuda.synchronize()
+    nt = cfg["L"] if check_tokens is None else check_tokens
+    ref = oracle.retnet_layer(f64(X[:1, :nt], "bf16"), tuple(f64(w, "bf16") for w in msr_w[1:]),
+                              f64(W1, "bf16"), f64(W2, "bf16"), h, th, flags, chunk, eps, ln_eps,
+                              ln1=ln1, ln2=ln2)
+    got = host64(out)[:1, :nt]
+    name = f"retnet layer b{cfg['b']} L{cfg['L']} x {x_dtype} (batch 0, {nt} tokens)"
+    if x_dtype == "bf16":
+        check_bf16_out(name, got, ref, TOL["bf16"])
+    else:
+        check(name, got, ref, TOL["bf16"])
+
+
+SMALL = dict(b=2, L=300, d_model=256, h=2, dk=128, dv=256, d_ff=1024, x_sigma=1.0, w_sigma=0.05,
+             ln_sigma=0.1, ln_eps=1e-5, chunk=64)
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_layer_small(R, x_dtype):
+    _layer_case(R, SMALL, seed=3, x_dtype=x_dtype)
+
+
+def test_layer_full_shape_prefix(R):
+    """The layer around the full block workload (batch 2, 8192 tokens,
+    d_model 4096, 16 heads of 256 / 512, FFN 16384, chunk 512); the oracle
+    recomputes batch 0's first 512 tokens, which by causality depend on
+    nothing later."""
+    _layer_case(R, W.LAYER, seed=0, x_dtype="bf16", check_tokens=512)
