@@ -7,4 +7,5 @@ from .retention import (XPOS, SCALE_QK, NORM_DROW, NORM_SCORE, NORM_ALL,  # noqa
                         gammas, thetas, xpos_rotate, retention_recurrent,
                         retention_parallel, retention_chunkwise, recurrent_step,
                         swish, group_norm_heads, gate_norm, split_heads, msr_forward,
-                        layer_norm, gelu, ffn, retnet_layer)
+                        layer_norm, gelu, ffn, retnet_layer, retnet_stack, msr_step,
+                        retnet_decode_step, zero_states)

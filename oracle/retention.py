@@ -16,7 +16,7 @@ next to the code.  Sources (page title, section):
   §2.1 architecture motivation (the complex-phase derivation),
   §2.2 recurrent mode, §2.3 parallel mode, §2.4 chunkwise recurrent mode,
   §三.2 MSR module, §三.3 normalisation, §四.4 single-layer structure
-  (LN, residuals and the gelu FFN around the MSR module).
+  (LN, residuals and the gelu FFN around the MSR module; layers stacked).
 * zyxy.net lecture ("RetNet（Retentive Network）：多尺度指数衰减…"), §5
   multi-scale grouping: the head split of d_model into contiguous column
   blocks, shape (batch, heads, seq, d_head).
@@ -303,23 +303,28 @@ def split_heads(x, h):
     return np.transpose(x.reshape(b, L, h, hd // h), (0, 2, 1, 3))
 
 
-def msr_forward(X, WQ, WK, WV, WG, WO, h, theta, flags, chunk, eps):
+def msr_forward(X, WQ, WK, WV, WG, WO, h, theta, flags, chunk, eps, pos0=0, n_prev=0, state=None,
+                return_state=False):
     """Gated multi-scale retention block forward (reading notes §三.2).
 
       Q = X W_Q, K = X W_K, V = X W_V  (§2.1), heads split as contiguous columns
       head_i = Retention(X, gamma_i)   (chunkwise form, per-head gamma_i)
       Y = GroupNorm_h(Concat(heads));  MSR(X) = (swish(X W_G) (.) Y) W_O
     X: [b, L, d_model]; W_Q, W_K: [d_model, h*dk]; W_V, W_G: [d_model, h*dv];
-    W_O: [h*dv, d_model].  Returns [b, L, d_model].
+    W_O: [h*dv, d_model].  Returns [b, L, d_model], and with return_state the
+    heads' final (S, z) as well.  state = (S, z) continues a sequence whose
+    first n_prev tokens (phases from pos0 - n_prev) are in it.
     """
     X = _f64(X)
     Q = split_heads(X @ _f64(WQ), h)
     K = split_heads(X @ _f64(WK), h)
     V = split_heads(X @ _f64(WV), h)
     G = X @ _f64(WG)
-    Y, _, _ = retention_chunkwise(Q, K, V, gammas(h), theta, flags, chunk)
-    Z = gate_norm(Y, G, eps)
-    return Z @ _f64(WO)
+    S0, z0 = (None, None) if state is None else state
+    Y, S, z = retention_chunkwise(Q, K, V, gammas(h), theta, flags, chunk, pos0=pos0, n_prev=n_prev,
+                                  state_in=S0, z_in=z0)
+    out = gate_norm(Y, G, eps) @ _f64(WO)
+    return (out, (S, z)) if return_state else out
 
 
 # ---------------------------------------------------------------------------
@@ -366,13 +371,75 @@ def ffn(X, W1, W2):
 
 
 def retnet_layer(X, msr_w, W1, W2, h, theta, flags, chunk, gn_eps, ln_eps,
-                 ln1=(None, None), ln2=(None, None)):
+                 ln1=(None, None), ln2=(None, None), pos0=0, n_prev=0, state=None, return_state=False):
     """One RetNet layer (§四.4): Y = MSR(LN(X)) + X;  X' = FFN(LN(Y)) + Y.
 
     msr_w = (W_Q, W_K, W_V, W_G, W_O) as in msr_forward; ln1 / ln2 are the
     (weight, bias) of the two LayerNorms (None = 1 and 0).  Returns X' of the
-    shape of X."""
+    shape of X (and the retention state, as msr_forward, with return_state)."""
     X = _f64(X)
     WQ, WK, WV, WG, WO = msr_w
-    Y = msr_forward(layer_norm(X, ln_eps, *ln1), WQ, WK, WV, WG, WO, h, theta, flags, chunk, gn_eps) + X
-    return ffn(layer_norm(Y, ln_eps, *ln2), W1, W2) + Y
+    m, st = msr_forward(layer_norm(X, ln_eps, *ln1), WQ, WK, WV, WG, WO, h, theta, flags, chunk, gn_eps,
+                        pos0=pos0, n_prev=n_prev, state=state, return_state=True)
+    Y = m + X
+    out = ffn(layer_norm(Y, ln_eps, *ln2), W1, W2) + Y
+    return (out, st) if return_state else out
+
+
+# ---------------------------------------------------------------------------
+# A stack of layers and its token-by-token decode.  The model stacks identical
+# layers (§四.4); decoding runs each layer's MSR in the recurrent form (§2.2),
+# one token at a time, each layer carrying its own heads' state (S, z):
+# [b,h,dk,dv] and [b,h,dk].  A layer's parameters are the tuple
+# (msr_w, W1, W2, ln1, ln2) of retnet_layer.
+# ---------------------------------------------------------------------------
+
+def retnet_stack(X, layers, h, theta, flags, chunk, gn_eps, ln_eps, pos0=0, n_prev=0, states=None,
+                 return_states=False):
+    """The layers applied in order (chunkwise MSR).  states: one (S, z) per
+    layer to continue from, or None; with return_states the layers' final
+    states are returned too."""
+    X = _f64(X)
+    out_states = []
+    for i, (msr_w, W1, W2, ln1, ln2) in enumerate(layers):
+        X, st = retnet_layer(X, msr_w, W1, W2, h, theta, flags, chunk, gn_eps, ln_eps, ln1, ln2, pos0=pos0,
+                             n_prev=n_prev, state=None if states is None else states[i], return_state=True)
+        out_states.append(st)
+    return (X, out_states) if return_states else X
+
+
+def msr_step(x, WQ, WK, WV, WG, WO, h, theta, flags, eps, state, pos, n_tokens):
+    """One token of the MSR module in the recurrent form (§三.2 with §2.2).
+
+    x: [b, d_model]; state = (S, z) of the h heads.  The projections are split
+    into heads like split_heads (head i takes columns [i*d, (i+1)*d)); each
+    head takes one recurrent_step; GroupNorm and the gate act on the one
+    token.  Returns ([b, d_model], (S_new, z_new))."""
+    x = _f64(x)
+    b = x.shape[0]
+    Q, K, V = x @ _f64(WQ), x @ _f64(WK), x @ _f64(WV)
+    dk, dv = Q.shape[1] // h, V.shape[1] // h
+    S, z = state
+    o, S, z = recurrent_step(Q.reshape(b, h, dk), K.reshape(b, h, dk), V.reshape(b, h, dv), S, gammas(h), theta,
+                             flags, pos, n_tokens, z)
+    Z = gate_norm(o[:, :, None, :], (x @ _f64(WG))[:, None, :], eps)[:, 0]
+    return Z @ _f64(WO), (S, z)
+
+
+def retnet_decode_step(x, layers, h, theta, flags, gn_eps, ln_eps, states, pos, n_tokens):
+    """One token through the stack: for each layer Y = MSR_step(LN(x)) + x,
+    x <- FFN(LN(Y)) + Y.  x: [b, d_model]; states: one (S, z) per layer.
+    Returns (x', new states)."""
+    x = _f64(x)
+    new_states = []
+    for (msr_w, W1, W2, ln1, ln2), st in zip(layers, states):
+        m, st = msr_step(layer_norm(x, ln_eps, *ln1), *msr_w, h, theta, flags, gn_eps, st, pos, n_tokens)
+        y = m + x
+        x = ffn(layer_norm(y, ln_eps, *ln2), W1, W2) + y
+        new_states.append(st)
+    return x, new_states
+
+
+def zero_states(n_layers, b, h, dk, dv):
+    """Empty per-layer states (S, z) for a fresh sequence."""
+    return [(np.zeros((b, h, dk, dv)), np.zeros((b, h, dk))) for _ in range(n_layers)]

@@ -506,11 +506,60 @@ def pin_retnet_layer(m):
     _close(lay(X2, WO, W2)[:, :9], full[:, :9], 1e-12, "causal")
 
 
+def _stack_params(r, n_layers, dm, h, dk, dv, dff):
+    layers = []
+    for _ in range(n_layers):
+        msr_w = (0.5 * r.standard_normal((dm, h * dk)), 0.5 * r.standard_normal((dm, h * dk)),
+                 0.5 * r.standard_normal((dm, h * dv)), 0.5 * r.standard_normal((dm, h * dv)),
+                 0.3 * r.standard_normal((h * dv, dm)))
+        W1, W2 = 0.4 * r.standard_normal((dm, dff)), 0.3 * r.standard_normal((dff, dm))
+        ln1 = (1.0 + 0.2 * r.standard_normal(dm), 0.2 * r.standard_normal(dm))
+        ln2 = (1.0 + 0.2 * r.standard_normal(dm), 0.2 * r.standard_normal(dm))
+        layers.append((msr_w, W1, W2, ln1, ln2))
+    return layers
+
+
+def pin_stack_decode(m):
+    """A stack of layers (§四.4) decoded token by token in the recurrent form
+    (§2.2, each layer carrying its own (S, z)) equals the chunkwise forward
+    of the stack at every position; a chunkwise prefill handing each layer's
+    state to the decode continues the same sequence; the final states agree.
+    The two paths share only LN, FFN and the gate; the retention, the head
+    split and the state hand-over differ."""
+    b, T, dm, h, dk, dv, dff, n_layers = 2, 9, 8, 2, 4, 4, 12, 2
+    r = np.random.default_rng(107)
+    layers = _stack_params(r, n_layers, dm, h, dk, dv, dff)
+    X = r.standard_normal((b, T, dm))
+    th = _thetas(dk)
+    for flags in (XPOS | NORM_ALL, XPOS, NORM_SCORE):
+        full, fst = m.retnet_stack(X, layers, h, th, flags, 4, 1e-5, 1e-5, return_states=True)
+        states = m.zero_states(n_layers, b, h, dk, dv)
+        for t in range(T):
+            y, states = m.retnet_decode_step(X[:, t], layers, h, th, flags, 1e-5, 1e-5, states, t, t + 1)
+            _close(y, full[:, t], 1e-10, f"decode token {t} flags {flags}")
+        for (S, z), (S2, z2) in zip(states, fst):
+            _close(S, S2, 1e-10, "final state S")
+            _close(z, z2, 1e-10, "final key-sum z")
+        P = 5
+        _, pst = m.retnet_stack(X[:, :P], layers, h, th, flags, 3, 1e-5, 1e-5, return_states=True)
+        for t in range(P, T):
+            y, pst = m.retnet_decode_step(X[:, t], layers, h, th, flags, 1e-5, 1e-5, pst, t, t + 1)
+            _close(y, full[:, t], 1e-10, f"prefill {P} then decode token {t}")
+        # a prefilled prefix continued chunkwise is the same sequence too
+        _, pst = m.retnet_stack(X[:, :P], layers, h, th, flags, 3, 1e-5, 1e-5, return_states=True)
+        rest = m.retnet_stack(X[:, P:], layers, h, th, flags, 2, 1e-5, 1e-5, pos0=P, n_prev=P, states=pst)
+        _close(rest, full[:, P:], 1e-10, "prefill then chunkwise continuation")
+    # the stack is not trivially the identity, and layer 2 depends on layer 1
+    assert np.max(np.abs(full - X)) > 1e-2
+    one = m.retnet_stack(X, layers[1:], h, th, XPOS, 4, 1e-5, 1e-5)
+    assert np.max(np.abs(one - full)) > 1e-3
+
+
 ALL_PINS = [pin_gamma_theta, pin_forms_agree, pin_onehot_decay, pin_xpos_closed_form,
             pin_drow_scale_closed_form, pin_score_clamp, pin_groupnorm_invariance,
             pin_groupnorm_values, pin_swish, pin_relative_position, pin_split_resume,
             pin_causality_linearity, pin_decode_zero_kv, pin_decode_vs_chunkwise, pin_block,
-            pin_pages_shape_example, pin_layer_norm, pin_gelu, pin_retnet_layer]
+            pin_pages_shape_example, pin_layer_norm, pin_gelu, pin_retnet_layer, pin_stack_decode]
 
 
 def quick_forms(m):

@@ -38,17 +38,24 @@ MUTANTS = [
      "        num = np.einsum('bhd,bhde->bhe', qp, S - kp[:, :, :, None] * v[:, :, p, None, :])\n"),
     ("heads interleaved", "np.transpose(x.reshape(b, L, h, hd // h), (0, 2, 1, 3))",
      "np.transpose(x.reshape(b, L, hd // h, h), (0, 3, 1, 2))"),
-    ("gate after W_O", "Z = gate_norm(Y, G, eps)\n    return Z @ _f64(WO)",
-     "Z = group_norm_heads(Y, eps)\n    return (Z @ _f64(WO)) * swish(G[..., :WO.shape[1]])"),
+    ("gate after W_O", "out = gate_norm(Y, G, eps) @ _f64(WO)",
+     "out = (group_norm_heads(Y, eps) @ _f64(WO)) * swish(G[..., :WO.shape[1]])"),
     ("unbiased LN variance", "var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)",
      "var = ((x - mu) ** 2).sum(axis=-1, keepdims=True) / (x.shape[-1] - 1)"),
     ("gelu tanh approximation", "return 0.5 * x * (1.0 + _erf(x / np.sqrt(2.0)))",
      "return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))"),
     ("FFN without gelu", "return gelu(_f64(X) @ _f64(W1)) @ _f64(W2)", "return (_f64(X) @ _f64(W1)) @ _f64(W2)"),
-    ("layer without the first LN", "Y = msr_forward(layer_norm(X, ln_eps, *ln1),", "Y = msr_forward(X,"),
-    ("layer drops the MSR residual", "WG, WO, h, theta, flags, chunk, gn_eps) + X", "WG, WO, h, theta, flags, chunk, gn_eps)"),
-    ("layer drops the FFN residual", "return ffn(layer_norm(Y, ln_eps, *ln2), W1, W2) + Y",
-     "return ffn(layer_norm(Y, ln_eps, *ln2), W1, W2) + X"),
+    ("layer without the first LN", "m, st = msr_forward(layer_norm(X, ln_eps, *ln1),", "m, st = msr_forward(X,"),
+    ("layer drops the MSR residual", "    Y = m + X\n", "    Y = m\n"),
+    ("layer drops the FFN residual", "out = ffn(layer_norm(Y, ln_eps, *ln2), W1, W2) + Y",
+     "out = ffn(layer_norm(Y, ln_eps, *ln2), W1, W2) + X"),
+    ("decode heads transposed", "Q.reshape(b, h, dk), K.reshape(b, h, dk)",
+     "Q.reshape(b, dk, h).transpose(0, 2, 1), K.reshape(b, dk, h).transpose(0, 2, 1)"),
+    ("decode second LN on the layer input", "x = ffn(layer_norm(y, ln_eps, *ln2), W1, W2) + y",
+     "x = ffn(layer_norm(x, ln_eps, *ln2), W1, W2) + y"),
+    ("decode shares one state across layers", "zip(layers, states)", "zip(layers, [states[0]] * len(states))"),
+    ("stack drops the carried state", "n_prev=n_prev, state=None if states is None else states[i]",
+     "n_prev=n_prev, state=None"),
 ]
 
 
