@@ -9,8 +9,9 @@ rotated so the 256 MB MALL cannot serve a repeated set.  Secondary lines in
 the same JSON record: the same workload at B = 64, the long workload (L =
 32768, 16 heads), the decode step (batch 128, 16 heads, 64 steps from
 position 8192), the GroupNorm + gate epilogue at the block shape, the gated
-MSR block (2 x 8192 tokens, d_model 4096) and one RetNet layer around it
-(LayerNorms, residuals and a 4 x d_model gelu FFN).
+MSR block (2 x 8192 tokens, d_model 4096), one RetNet layer around it
+(LayerNorms, residuals and a 4 x d_model gelu FFN), and that layer decoding
+one token for 128 sequences.
 
 Prints ONE JSON line.  Only N = 1 GPU is supported.
 """
@@ -135,7 +136,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true", help="time the primary workload only")
-    ap.add_argument("--secondary", default="medium_B64,long,decode,gate_norm,block,layer,copy",
+    ap.add_argument("--secondary", default="medium_B64,long,decode,gate_norm,block,layer,decode_layer,copy",
                     help="comma list of secondary measurements to run (empty for none)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -294,6 +295,29 @@ def main():
                           "tflops": round((gflop + rflop) / (msl * 1e-3) / 1e12, 1), "d_ff": dff,
                           "gemm_gflop": round(gflop / 1e9, 1), "retention_gflop": round(rflop / 1e9, 1)}
         del Xd, ws, w1, w2
+        torch.cuda.empty_cache()
+    if "decode_layer" in todo:
+        # one RetNet layer decoding one token for 128 sequences (d_model 4096, 16 heads, FFN 16384)
+        dc = dict(W.LAYER, b=128, L=1)
+        msr_w, W1, W2, ln1, ln2 = W.layer_inputs(**dc)
+        dT = lambda w: dev(np.ascontiguousarray(w.T))
+        vec = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+        lay = [(tuple(dT(w) for w in msr_w[1:]), dT(W1), dT(W2), (vec(ln1[0]), vec(ln1[1])),
+                (vec(ln2[0]), vec(ln2[1])))]
+        del msr_w, W1, W2
+        db, dh, ddk, ddv, ddm, dff = dc["b"], dc["h"], dc["dk"], dc["dv"], dc["d_model"], dc["d_ff"]
+        st = R.new_states(1, db, dh, ddk, ddv)
+        xd = torch.randn((db, ddm), device="cuda")
+        dg, dth = W.gamma_vector(dh), W.theta_vector(ddk)
+        msd = time_calls(lambda: R.retnet_decode_step(xd, lay, st, dg, dth, 8192, 8193, dc["flags"], dc["eps"],
+                                                       dc["ln_eps"]), 10, 2, torch)
+        wbytes = 2 * (ddm * (2 * dh * ddk + 2 * dh * ddv) + dh * ddv * ddm + 2 * ddm * dff)
+        sbytes = 2 * 4 * db * dh * ddk * ddv
+        extra["decode_layer"] = {"ms": round(msd, 4), "tokens_per_s": db / (msd * 1e-3),
+                                 "weight_mb": round(wbytes / 1e6, 1), "state_mb": round(sbytes / 1e6, 1),
+                                 "gbs": round((wbytes + sbytes) / (msd * 1e-3) / 1e9, 1),
+                                 "hbm_frac": round((wbytes + sbytes) / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del lay, st
         torch.cuda.empty_cache()
     if "gate_norm" in todo:
         # GroupNorm + gate at the block shape (2 x 8192 tokens, 16 heads x 512)

@@ -223,7 +223,7 @@ def layer_norm(x, eps, weight=None, bias=None, out=None, out_dtype=None, stream=
 
 
 def msr_block_fwd(x, wq_t, wk_t, wv_t, wg_t, wo_t, gamma, theta, chunk, flags, eps, out_dtype=torch.bfloat16,
-                  residual=None, stream=None):
+                  residual=None, pos0=0, n_prev=0, state=None, state_out=None, stream=None):
     """Gated multi-scale retention block forward (RetNet reading notes, §三.2):
     MSR(X) = (swish(X W_G) (.) GroupNorm_h(Retention heads)) W_O.
 
@@ -233,8 +233,11 @@ def msr_block_fwd(x, wq_t, wk_t, wv_t, wg_t, wo_t, gamma, theta, chunk, flags, e
     Every step runs in the library's kernels: four projections, the
     chunkwise retention over [b, h, L, d] views of the projections, the
     GroupNorm + swish gate, and the output projection, whose epilogue adds
-    residual ([b*L, d_model] of out_dtype) when one is given.  Intermediates
-    (the projections, the head outputs and the gated heads) are stored as fp16.
+    residual ([b*L, d_model]) when one is given.  Intermediates (the
+    projections, the head outputs and the gated heads) are stored as fp16.
+    state = (S, z) continues a sequence of n_prev tokens (phases from pos0);
+    state_out = (S, z) receives the heads' final state (float32
+    [b,h,d_k,d_v], [b,h,d_k]).
     """
     b, L, dm = x.shape
     h = len(gamma)
@@ -251,25 +254,29 @@ def msr_block_fwd(x, wq_t, wk_t, wv_t, wg_t, wo_t, gamma, theta, chunk, flags, e
     vv = V.view(b, L, h, dv).transpose(1, 2)
     Y = torch.empty((b, L, h * dv), dtype=f16, device=x.device)
     yv = Y.view(b, L, h, dv).transpose(1, 2)
-    chunkwise_fwd(qv, kv, vv, gamma, theta, chunk, flags, out=yv, stream=stream)
+    S0, z0 = (None, None) if state is None else state
+    S1, z1 = (None, None) if state_out is None else state_out
+    chunkwise_fwd(qv, kv, vv, gamma, theta, chunk, flags, pos0=pos0, n_prev=n_prev, state_in=S0, z_in=z0,
+                  state_out=S1, z_out=z1, out=yv, stream=stream)
     Z = gate_norm(yv, G.view(b, L, h * dv), eps, stream=stream)
     out = gemm(Z.view(b * L, h * dv), wo_t, out_dtype=out_dtype, residual=residual, stream=stream)
     return out.view(b, L, -1)
 
 
 def retnet_layer_fwd(x, msr_w_t, w1_t, w2_t, gamma, theta, chunk, flags, gn_eps, ln_eps, ln1=(None, None),
-                     ln2=(None, None), stream=None):
+                     ln2=(None, None), pos0=0, n_prev=0, state=None, state_out=None, out_dtype=None, stream=None):
     """One RetNet layer forward (reading notes §四.4):
         Y = MSR(LN(X)) + X,   X' = FFN(LN(Y)) + Y,   FFN(Y) = gelu(Y W_1) W_2.
 
-    x: [b, L, d_model] float32 or bf16; the result has x's dtype;
+    x: [b, L, d_model] float32 or bf16; the result has x's dtype (or out_dtype);
     msr_w_t: (W_Q, W_K, W_V, W_G, W_O) as [out_features, in_features] bf16;
     w1_t: [d_ff, d_model] and w2_t: [d_model, d_ff] bf16; ln1 / ln2: the two
     LayerNorms' float32 (weight, bias), None for 1 and 0.  Every step runs in
     the library: the LayerNorms (stored as fp16, the GEMMs' activation
     operand), the MSR block whose output projection adds X in its epilogue
     and keeps Y in float32, the first FFN projection with gelu in its
-    epilogue (hidden stored as fp16) and the second with Y added.
+    epilogue (hidden stored as fp16) and the second with Y added.  state /
+    state_out: the MSR heads' (S, z), as in msr_block_fwd.
     """
     if x.dtype not in (torch.float32, torch.bfloat16) or not x.is_contiguous():
         raise TypeError("x must be a contiguous float32 or bf16 tensor")
@@ -277,8 +284,69 @@ def retnet_layer_fwd(x, msr_w_t, w1_t, w2_t, gamma, theta, chunk, flags, gn_eps,
     x2 = x.view(b * L, dm)
     xn = layer_norm(x2, ln_eps, *ln1, out_dtype=torch.float16, stream=stream)
     Y = msr_block_fwd(xn.view(b, L, dm), *msr_w_t, gamma, theta, chunk, flags, gn_eps, out_dtype=torch.float32,
-                      residual=x2, stream=stream).view(b * L, dm)
+                      residual=x2, pos0=pos0, n_prev=n_prev, state=state, state_out=state_out,
+                      stream=stream).view(b * L, dm)
     yn = layer_norm(Y, ln_eps, *ln2, out_dtype=torch.float16, stream=stream)
     H = gemm(yn, w1_t, out_dtype=torch.float16, gelu=True, stream=stream)
-    out = gemm(H, w2_t, out_dtype=x.dtype, residual=Y, stream=stream)
+    out = gemm(H, w2_t, out_dtype=x.dtype if out_dtype is None else out_dtype, residual=Y, stream=stream)
     return out.view(b, L, dm)
+
+
+def new_states(n_layers, b, h, d_k, d_v, device="cuda"):
+    """Zeroed per-layer retention states (S, z) for a fresh sequence."""
+    return [(torch.zeros((b, h, d_k, d_v), dtype=torch.float32, device=device),
+             torch.zeros((b, h, d_k), dtype=torch.float32, device=device)) for _ in range(n_layers)]
+
+
+def retnet_stack_fwd(x, layers, gamma, theta, chunk, flags, gn_eps, ln_eps, pos0=0, n_prev=0, states=None,
+                     states_out=None, stream=None):
+    """A stack of RetNet layers (reading notes §四.4) over a sequence, the MSR
+    heads in the chunkwise form.  layers: (msr_w_t, w1_t, w2_t, ln1, ln2) per
+    layer as in retnet_layer_fwd; states: per-layer (S, z) to continue from;
+    states_out: per-layer (S, z) buffers receiving the final states (a
+    prefill for retnet_decode_step).  Between layers the activations stay
+    float32; the result has x's dtype."""
+    final_dtype = x.dtype
+    for i, (msr_w_t, w1_t, w2_t, ln1, ln2) in enumerate(layers):
+        last = i == len(layers) - 1
+        x = retnet_layer_fwd(x, msr_w_t, w1_t, w2_t, gamma, theta, chunk, flags, gn_eps, ln_eps, ln1, ln2,
+                             pos0=pos0, n_prev=n_prev, state=None if states is None else states[i],
+                             state_out=None if states_out is None else states_out[i],
+                             out_dtype=final_dtype if last else torch.float32, stream=stream)
+    return x
+
+
+def retnet_decode_step(x, layers, states, gamma, theta, pos, n_tokens, flags, gn_eps, ln_eps, stream=None):
+    """One token per sequence through a stack of RetNet layers, each layer's
+    MSR in the recurrent form (reading notes §2.2, §四.4).
+
+    x: [b, d_model] float32 or bf16 (the result has its dtype); states: the
+    layers' (S, z), updated in place; pos: the token's position (xPos phase);
+    n_tokens: tokens seen including this one.  Per layer: LayerNorm (fp16),
+    four projections, retention_recurrent_step on the [b, h, d] views,
+    GroupNorm + gate on the one token, W_O with x added (Y in float32),
+    LayerNorm, the gelu FFN with Y added -- all in the library's kernels.
+    Between layers the activations stay float32."""
+    if x.dtype not in (torch.float32, torch.bfloat16) or not x.is_contiguous() or x.dim() != 2:
+        raise TypeError("x must be a contiguous [b, d_model] float32 or bf16 tensor")
+    b, dm = x.shape
+    h = len(gamma)
+    f16 = torch.float16
+    final_dtype = x.dtype
+    for li, ((wq, wk, wv, wg, wo), w1, w2, ln1, ln2) in enumerate(layers):
+        S, z = states[li]
+        dk, dv = wq.shape[0] // h, wv.shape[0] // h
+        xn = layer_norm(x, ln_eps, *ln1, out_dtype=f16, stream=stream)
+        Q = gemm(xn, wq, out_dtype=f16, stream=stream)
+        K = gemm(xn, wk, out_dtype=f16, stream=stream)
+        V = gemm(xn, wv, out_dtype=f16, stream=stream)
+        G = gemm(xn, wg, out_dtype=f16, stream=stream)
+        o = recurrent_step(Q.view(b, h, dk), K.view(b, h, dk), V.view(b, h, dv), S, gamma, theta, pos, n_tokens,
+                           flags, z=z, out_dtype=torch.float32, stream=stream)
+        Z = gate_norm(o.view(b, h, 1, dv), G.view(b, 1, h * dv), gn_eps, stream=stream)
+        Y = gemm(Z.view(b, h * dv), wo, out_dtype=torch.float32, residual=x, stream=stream)
+        yn = layer_norm(Y, ln_eps, *ln2, out_dtype=f16, stream=stream)
+        H = gemm(yn, w1, out_dtype=f16, gelu=True, stream=stream)
+        x = gemm(H, w2, out_dtype=final_dtype if li == len(layers) - 1 else torch.float32, residual=Y,
+                 stream=stream)
+    return x

@@ -136,11 +136,17 @@ static hipError_t launch_step_t(const StepArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename TI>
+static hipError_t launch_step_i(const StepArgs& a, hipStream_t st) {
+  if (a.out_dt == RET_BF16) return launch_step_t<TI, bf16>(a, st);
+  if (a.out_dt == RET_F16) return launch_step_t<TI, half>(a, st);
+  return launch_step_t<TI, float>(a, st);
+}
+
 hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t st) {
-  if (a.in_dt == RET_BF16) {
-    return a.out_dt == RET_BF16 ? launch_step_t<bf16, bf16>(a, st) : launch_step_t<bf16, float>(a, st);
-  }
-  return a.out_dt == RET_BF16 ? launch_step_t<float, bf16>(a, st) : launch_step_t<float, float>(a, st);
+  if (a.in_dt == RET_BF16) return launch_step_i<bf16>(a, st);
+  if (a.in_dt == RET_F16) return launch_step_i<half>(a, st);
+  return launch_step_i<float>(a, st);
 }
 
 }  // namespace ret

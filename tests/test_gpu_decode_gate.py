@@ -18,16 +18,24 @@ def R():
     return binding
 
 
-def _decode(R, b, h, dk, dv, steps, flags, use_z, seed, sample=None, out_dtype=torch.float32):
+def _decode(R, b, h, dk, dv, steps, flags, use_z, seed, sample=None, out_dtype=torch.float32, in_f16=False):
     S0, qs, ks, vs = W.decode_inputs(b, h, dk, dv, 0.1, 1 / np.sqrt(dk), steps, seed=seed)
+    if in_f16:
+        # fp16 inputs: the bf16 draws rounded to fp16; both sides see those values
+        qs, ks, vs = (f64(a, "bf16").astype(np.float16) for a in (qs, ks, vs))
+        ind = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        inf = lambda a: a.astype(np.float64)
+    else:
+        ind = lambda a: dev(a, "bf16")
+        inf = lambda a: f64(a, "bf16")
     g, th = W.gamma_vector(h), W.theta_vector(dk)
     pos0 = 8192
-    announce(f"decode b{b} h{h} dk{dk} dv{dv} steps{steps} flags{flags} z={use_z}")
+    announce(f"decode b{b} h{h} dk{dk} dv{dv} steps{steps} flags{flags} z={use_z} f16 in={in_f16} out={out_dtype}")
     S = torch.from_numpy(S0).cuda()
     z = torch.zeros((b, h, dk), dtype=torch.float32, device="cuda") if use_z else None
     outs = []
     for t in range(steps):
-        o = R.recurrent_step(dev(qs[t], "bf16"), dev(ks[t], "bf16"), dev(vs[t], "bf16"), S, g, th, pos0 + t,
+        o = R.recurrent_step(ind(qs[t]), ind(ks[t]), ind(vs[t]), S, g, th, pos0 + t,
                              pos0 + t + 1, flags, z=z, out_dtype=out_dtype)
         outs.append(o)
     torch.cuda.synchronize()
@@ -40,14 +48,22 @@ def _decode(R, b, h, dk, dv, steps, flags, use_z, seed, sample=None, out_dtype=t
     gs = g[hi]
     o_ref, o_got = [], []
     for t in range(steps):
-        o_t, S_ref, z_ref = oracle.recurrent_step(f64(qs[t][bi, hi], "bf16")[None], f64(ks[t][bi, hi], "bf16")[None],
-                                                  f64(vs[t][bi, hi], "bf16")[None], S_ref, gs, th, flags,
+        o_t, S_ref, z_ref = oracle.recurrent_step(inf(qs[t][bi, hi])[None], inf(ks[t][bi, hi])[None],
+                                                  inf(vs[t][bi, hi])[None], S_ref, gs, th, flags,
                                                   pos0 + t, pos0 + t + 1, z=z_ref)
         o_ref.append(o_t[0])
         o_got.append(host64(outs[t])[bi, hi])
     name = f"decode b{b}h{h} steps{steps} f{flags}"
-    chk = check_bf16_out if out_dtype == torch.bfloat16 else check
-    chk(name + " o (all steps)", np.stack(o_got), np.stack(o_ref), TOL["bf16"])
+    if out_dtype == torch.float16:
+        # fp16 output: half an fp16 ulp of the exact value on top of the fp32 bar
+        got, ref = np.stack(o_got), np.stack(o_ref)
+        half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -14))) - 11)
+        ex = np.max(np.maximum(np.abs(got - ref) - half_ulp, 0.0)) / np.sqrt(np.mean(ref ** 2))
+        print(f"[parity] {name} o f16: beyond output rounding = {ex:.3e}", flush=True)
+        assert ex <= TOL["f32"]
+    else:
+        chk = check_bf16_out if out_dtype == torch.bfloat16 else check
+        chk(name + " o (all steps)", np.stack(o_got), np.stack(o_ref), TOL["bf16"])
     S_got = host64(S)[bi, hi]
     check(name + " final S", S_got, S_ref[0], TOL["f32"])
     if use_z:
@@ -65,6 +81,11 @@ def test_decode_all_norms(R):
 @pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128), (128, 1024), (6, 12)])
 def test_decode_shapes(R, dk, dv):
     _decode(R, 2, 3, dk, dv, 3, W.XPOS | W.NORM_ALL, True, seed=3, out_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.float32])
+def test_decode_f16_inputs(R, out_dtype):
+    _decode(R, 2, 4, 128, 256, 5, W.XPOS | W.NORM_ALL, True, seed=4, out_dtype=out_dtype, in_f16=True)
 
 
 def test_decode_full_sampled(R):
