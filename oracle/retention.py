@@ -233,6 +233,58 @@ def retention_chunkwise(q, k, v, gamma, theta, flags, chunk, pos0=0, n_prev=0,
     return o, R, z
 
 
+def retention_parallel_bwd(q, k, v, do, gamma, theta, flags, pos0=0):
+    """Gradients dL/dq, dL/dk, dL/dv of the normalised retention of a fresh
+    sequence, given dL/dO (the chunkwise backward's definition: the training
+    path of §四 differentiates the forward of §2.3 with §三.3's normalisers).
+
+    Written out on the parallel form: with q', k' the rotated inputs,
+      A_pm   = (q'_p . k'_m) gamma^(p-m)  for m <= p         (unscaled scores)
+      num_p  = sum_m A_pm v_m,   den_p = sum_m A_pm
+      o_p    = s_p num_p / n_p,  n_p = max(|s_p den_p|, 1) with NORM_SCORE, else 1
+    the chain rule gives
+      dL/dnum_p = s_p g_p / n_p
+      dL/dden_p = -s_p^2 sign(den_p) (g_p . num_p) / n_p^2  where |s_p den_p| > 1, else 0
+      dL/dA_pm  = dL/dnum_p . v_m + dL/dden_p
+      dq'_p = sum_m dL/dA_pm gamma^(p-m) k'_m,  dk'_m = sum_p dL/dA_pm gamma^(p-m) q'_p
+      dv_m  = sum_p A_pm dL/dnum_p
+    and dq, dk rotate dq', dk' back by -p theta (the rotation is orthogonal).
+    Reading: nothing is detached (the pages leave it open); on the clamp's
+    boundary |s den| = 1 the constant branch is taken.  Returns (dq, dk, dv).
+    """
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(do)
+    gamma = _f64(gamma)
+    b, h, L, dk = q.shape
+    pos = pos0 + np.arange(L)
+    if flags & XPOS:
+        q = xpos_rotate(q, pos, theta)
+        k = xpos_rotate(k, pos, theta)
+    n = np.arange(L)
+    diff = n[:, None] - n[None, :]
+    D = np.where(diff[None] >= 0, gamma[:, None, None] ** np.maximum(diff, 0)[None], 0.0)    # [h,L,L]
+    A = (q @ np.swapaxes(k, -1, -2)) * D[None]
+    num = A @ v
+    den = A.sum(axis=-1)
+    s = _row_scale(flags, gamma, dk, n + 1)[None]                                         # [1,h,L]
+    if flags & NORM_SCORE:
+        nrm = np.maximum(np.abs(s * den), 1.0)
+        active = np.abs(s * den) > 1.0
+        gden = np.where(active, -(s ** 2) * np.sign(den) * np.einsum('bhpe,bhpe->bhp', g, num) / nrm ** 2, 0.0)
+    else:
+        nrm = np.ones_like(den)
+        gden = np.zeros_like(den)
+    gnum = (s / nrm)[..., None] * g
+    dA = gnum @ np.swapaxes(v, -1, -2) + gden[..., None]
+    dS = dA * D[None]
+    dqr = dS @ k
+    dkr = np.swapaxes(dS, -1, -2) @ q
+    dv = np.swapaxes(A, -1, -2) @ gnum
+    if flags & XPOS:
+        dqr = xpos_rotate(dqr, -pos, theta)
+        dkr = xpos_rotate(dkr, -pos, theta)
+    return dqr, dkr, dv
+
+
 def recurrent_step(q, k, v, S, gamma, theta, flags, pos, n_tokens, z=None):
     """One decode step of the recurrent form (reading notes §2.2).
 

@@ -555,11 +555,72 @@ def pin_stack_decode(m):
     assert np.max(np.abs(one - full)) > 1e-3
 
 
+def pin_backward(m):
+    """The chunkwise backward's definition (gradients of the normalised
+    retention): equal to central finite differences of the recurrent form
+    (the definition, a different code path) for four flag sets, two of them
+    with the score clamp active on some rows and inactive on others; and
+    Euler's identity for homogeneous functions -- without the score
+    normalisation O is of degree 1 in each of q, k and v, so
+    sum(dq . q) = sum(dk . k) = sum(dv . v) = sum(dO . O); with the clamp
+    active on every row O is of degree 0 in q and in k."""
+    r = np.random.default_rng(211)
+    b, h, L, dk, dv = 1, 2, 7, 4, 3
+    th = _thetas(dk)
+    g = m.gammas(h)
+    eps = 1e-6
+    for flags, qscale in ((0, 1.0), (XPOS, 1.0), (XPOS | NORM_ALL, 2.0), (XPOS | NORM_SCORE, 1.0)):
+        q = r.standard_normal((b, h, L, dk)) * qscale
+        k, v = r.standard_normal((b, h, L, dk)), r.standard_normal((b, h, L, dv))
+        do = r.standard_normal((b, h, L, dv))
+        if flags & NORM_SCORE:
+            # keep every row away from the clamp's kink, and both branches in use
+            pr = m.retention_parallel(q, k, np.ones((b, h, L, 1)), g, th, flags & ~NORM_SCORE, pos0=3)[..., 0]
+            assert np.min(np.abs(np.abs(pr) - 1.0)) > 1e-3
+            assert np.any(np.abs(pr) > 1.0) and np.any(np.abs(pr) < 1.0)
+        loss = lambda q_, k_, v_: float(np.sum(do * m.retention_recurrent(q_, k_, v_, g, th, flags, pos0=3)[0]))
+        grads = m.retention_parallel_bwd(q, k, v, do, g, th, flags, pos0=3)
+        for which, x in enumerate((q, k, v)):
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                args = [q, k, v]
+                xp = x.copy(); xp[idx] += eps
+                xm = x.copy(); xm[idx] -= eps
+                args[which] = xp; fp = loss(*args)
+                args[which] = xm; fm = loss(*args)
+                fd[idx] = (fp - fm) / (2 * eps)
+            _close(grads[which], fd, 1e-7, f"finite differences, input {which}, flags {flags}")
+    # Euler's identity at a larger size
+    b, h, L, dk, dv = 2, 3, 40, 8, 6
+    th = _thetas(dk)
+    g = m.gammas(h)
+    q, k = r.standard_normal((b, h, L, dk)), r.standard_normal((b, h, L, dk))
+    v, do = r.standard_normal((b, h, L, dv)), r.standard_normal((b, h, L, dv))
+    for flags in (XPOS, XPOS | SCALE_QK | NORM_DROW):
+        o = m.retention_parallel(q, k, v, g, th, flags)
+        dq, dk_, dv_ = m.retention_parallel_bwd(q, k, v, do, g, th, flags)
+        ref = np.sum(do * o)
+        for x, dx in ((q, dq), (k, dk_), (v, dv_)):
+            assert abs(np.sum(dx * x) - ref) <= 1e-10 * max(1.0, abs(ref)), "degree-1 homogeneity"
+    # positive q, k (no rotation) make every score row sum large: the clamp
+    # is active on every row
+    flags = SCALE_QK | NORM_SCORE
+    qb, kb = 50.0 * np.abs(q), np.abs(k)
+    pr = m.retention_parallel(qb, kb, np.ones((b, h, L, 1)), g, th, SCALE_QK)[..., 0]
+    assert np.all(np.abs(pr) > 1.0)
+    o = m.retention_parallel(qb, kb, v, g, th, flags)
+    dq, dk_, dv_ = m.retention_parallel_bwd(qb, kb, v, do, g, th, flags)
+    assert abs(np.sum(dq * qb)) <= 1e-10 * np.sqrt(np.sum(dq * dq) * np.sum(qb * qb)), "degree-0 in q"
+    assert abs(np.sum(dk_ * kb)) <= 1e-10 * np.sqrt(np.sum(dk_ * dk_) * np.sum(kb * kb)), "degree-0 in k"
+    assert np.max(np.abs(dq)) > 1e-6
+    assert abs(np.sum(dv_ * v) - np.sum(do * o)) <= 1e-10 * max(1.0, abs(np.sum(do * o))), "degree-1 in v"
+
+
 ALL_PINS = [pin_gamma_theta, pin_forms_agree, pin_onehot_decay, pin_xpos_closed_form,
             pin_drow_scale_closed_form, pin_score_clamp, pin_groupnorm_invariance,
             pin_groupnorm_values, pin_swish, pin_relative_position, pin_split_resume,
             pin_causality_linearity, pin_decode_zero_kv, pin_decode_vs_chunkwise, pin_block,
-            pin_pages_shape_example, pin_layer_norm, pin_gelu, pin_retnet_layer, pin_stack_decode]
+            pin_pages_shape_example, pin_layer_norm, pin_gelu, pin_retnet_layer, pin_stack_decode, pin_backward]
 
 
 def quick_forms(m):

@@ -54,6 +54,11 @@ MUTANTS = [
     ("decode second LN on the layer input", "x = ffn(layer_norm(y, ln_eps, *ln2), W1, W2) + y",
      "x = ffn(layer_norm(x, ln_eps, *ln2), W1, W2) + y"),
     ("decode shares one state across layers", "zip(layers, states)", "zip(layers, [states[0]] * len(states))"),
+    ("backward clamp gradient sign", "gden = np.where(active, -(s ** 2)", "gden = np.where(active, (s ** 2)"),
+    ("backward clamp gradient missing a scale", "gden = np.where(active, -(s ** 2)", "gden = np.where(active, -(s ** 1)"),
+    ("backward dk from the untransposed scores", "dkr = np.swapaxes(dS, -1, -2) @ q", "dkr = dS @ q"),
+    ("backward without the inverse rotation", "dkr = xpos_rotate(dkr, -pos, theta)", "dkr = xpos_rotate(dkr, pos, theta)"),
+    ("backward dv ignores the normaliser", "gnum = (s / nrm)[..., None] * g", "gnum = s[..., None] * g"),
     ("stack drops the carried state", "n_prev=n_prev, state=None if states is None else states[i]",
      "n_prev=n_prev, state=None"),
 ]
