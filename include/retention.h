@@ -118,6 +118,42 @@ size_t retention_chunkwise_workspace_bytes(int b, int h, int L, int d_k, int d_v
                                            unsigned flags);
 
 /*
+ * retention_chunkwise_bwd -- gradients of retention_chunkwise_fwd for a fresh
+ * sequence (the training path of [notes] §四, chunkwise as in §2.4):
+ * given g = dL/dO, writes dq = dL/dq, dk = dL/dk, dv = dL/dv of
+ *   o_p = s_p num_p / n_p,  num_p = sum_{m<=p} A_pm v_m,
+ *   A_pm = (q'_p . k'_m) gamma^(p-m),  n_p = max(|s_p sum_m A_pm|, 1)
+ * (n_p = 1 without RET_NORM_SCORE; q', k' rotated as in the forward).  The
+ * normalisers are differentiated, not detached; where |s_p den_p| = 1 the
+ * clamp's constant branch is used.
+ *   q, k, v, dout   [b,h,L,d] views of in_dt (bf16 or f16), as in the forward
+ *   dq, dk          [b,h,L,d_k] views of grad_dt (f32 or bf16); dv [b,h,L,d_v]
+ *                   (written, not accumulated; must not overlap the inputs)
+ *   chunk_B         the backward's own chunk size, a multiple of 64 (any
+ *                   value gives the same result up to rounding)
+ *   gamma, theta, pos0, flags  as in the forward (n_prev = 0, no state_in)
+ *   workspace       device scratch of retention_chunkwise_bwd_workspace_bytes()
+ *                   bytes, 256-byte aligned
+ * Products are fp16 MFMA with fp32 accumulation.  g is scaled per (batch,
+ * head) by a power of two that brings its largest magnitude near 1 (undone
+ * exactly on the results), so g has no range precondition; q, k, v have the
+ * forward's (|q|, |k| < 2^15, |v| < 2^16, s_p |q'_p . k'_m| < 2^16), and
+ * |a_p (g_p . v_m) + c_p| < 2^15 must hold for the scaled g (a_p = s_p / n_p,
+ * c_p the clamp term).  Supported (d_k, d_v): (64,64), (128,128), (128,256),
+ * (256,512).
+ */
+int retention_chunkwise_bwd(const void* q, ret_strides sq, const void* k, ret_strides sk,
+                            const void* v, ret_strides sv, const void* dout, ret_strides sdo,
+                            void* dq, ret_strides sdq, void* dk, ret_strides sdk, void* dv, ret_strides sdv,
+                            int b, int h, int L, int d_k, int d_v, int chunk_B,
+                            const double* gamma, const double* theta, int64_t pos0, unsigned flags,
+                            ret_dtype in_dt, ret_dtype grad_dt,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace retention_chunkwise_bwd needs for this problem. */
+size_t retention_chunkwise_bwd_workspace_bytes(int b, int h, int L, int d_k, int d_v, int chunk_B);
+
+/*
  * retention_recurrent_step -- one decode step of the recurrent form
  * ([notes] §2.2): S <- gamma S + k'^T v, o = q' S, the current token included.
  *

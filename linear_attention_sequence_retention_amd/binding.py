@@ -49,6 +49,12 @@ def load_library(path=LIB_PATH):
     lib.msr_gate_norm.restype = i32
     lib.msr_gemm.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp]
     lib.msr_gemm.restype = i32
+    lib.retention_chunkwise_bwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides,
+                                            vp, Strides, vp, Strides, vp, Strides,
+                                            i32, i32, i32, i32, i32, i32, dp, dp, i64, u32, i32, i32, vp, sz, vp]
+    lib.retention_chunkwise_bwd.restype = i32
+    lib.retention_chunkwise_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.retention_chunkwise_bwd_workspace_bytes.restype = sz
     lib.msr_gemm_ex.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, u32, vp]
     lib.msr_gemm_ex.restype = i32
     lib.ret_layer_norm.argtypes = [vp, vp, i32, i32, vp, vp, f32, i32, i32, vp]
@@ -141,6 +147,39 @@ def chunkwise_fwd(q, k, v, gamma, theta, chunk, flags, pos0=0, n_prev=0, state_i
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
     _check(st, "retention_chunkwise_fwd")
     return out
+
+
+def chunkwise_bwd_workspace_bytes(b, h, L, dk, dv, chunk):
+    return LIB.retention_chunkwise_bwd_workspace_bytes(b, h, L, dk, dv, chunk)
+
+
+def chunkwise_bwd(q, k, v, dout, gamma, theta, chunk, flags, pos0=0, dq=None, dk=None, dv=None,
+                  grad_dtype=torch.float32, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of chunkwise_fwd for a fresh sequence given
+    dout = dL/dO ([b,h,L,d] views of one bf16 or fp16 dtype).  chunk is the
+    backward's own chunk size (a multiple of 64)."""
+    b, h, L, d_k = q.shape
+    d_v = v.shape[-1]
+    in_dt = _dt(q)
+    if _dt(k) != in_dt or _dt(v) != in_dt or _dt(dout) != in_dt:
+        raise TypeError("q, k, v and dout must share one dtype")
+    dq = torch.empty((b, h, L, d_k), dtype=grad_dtype, device=q.device) if dq is None else dq
+    dk = torch.empty((b, h, L, d_k), dtype=grad_dtype, device=q.device) if dk is None else dk
+    dv = torch.empty((b, h, L, d_v), dtype=grad_dtype, device=q.device) if dv is None else dv
+    if _dt(dk) != _dt(dq) or _dt(dv) != _dt(dq):
+        raise TypeError("dq, dk and dv must share one dtype")
+    g, gp = _f64(gamma, h, "gamma")
+    th, tp = (None, None) if theta is None else _f64(theta, d_k // 2, "theta")
+    need = chunkwise_bwd_workspace_bytes(b, h, L, d_k, d_v, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = LIB.retention_chunkwise_bwd(
+        _ptr(q), _strides4(q, "q"), _ptr(k), _strides4(k, "k"), _ptr(v), _strides4(v, "v"),
+        _ptr(dout), _strides4(dout, "dout"), _ptr(dq), _strides4(dq, "dq"), _ptr(dk), _strides4(dk, "dk"),
+        _ptr(dv), _strides4(dv, "dv"), b, h, L, d_k, d_v, chunk, gp, tp, pos0, flags, in_dt, _dt(dq),
+        _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "retention_chunkwise_bwd")
+    return dq, dk, dv
 
 
 def recurrent_step(q, k, v, S, gamma, theta, pos, n_tokens, flags, z=None, out=None,

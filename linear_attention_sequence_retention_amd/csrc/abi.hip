@@ -136,6 +136,63 @@ int retention_chunkwise_fwd(const void* q, ret_strides sq, const void* k, ret_st
   return hip_status(e, "retention_chunkwise_fwd launch");
 }
 
+size_t retention_chunkwise_bwd_workspace_bytes(int b, int h, int L, int d_k, int d_v, int chunk_B) {
+  if (b <= 0 || h <= 0 || L <= 0 || d_k <= 0 || d_v <= 0 || chunk_B <= 0) return 0;
+  return ret::chunkwise_bwd_workspace(b, h, L, d_k, d_v, chunk_B);
+}
+
+int retention_chunkwise_bwd(const void* q, ret_strides sq, const void* k, ret_strides sk,
+                            const void* v, ret_strides sv, const void* dout, ret_strides sdo,
+                            void* dq, ret_strides sdq, void* dk, ret_strides sdk, void* dv, ret_strides sdv,
+                            int b, int h, int L, int d_k, int d_v, int chunk_B,
+                            const double* gamma, const double* theta, int64_t pos0, unsigned flags,
+                            ret_dtype in_dt, ret_dtype grad_dt,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (b <= 0 || h <= 0 || L <= 0 || d_k <= 0 || d_v <= 0)
+    return fail(RET_E_INVAL, "sizes must be positive (b=%d h=%d L=%d d_k=%d d_v=%d)", b, h, L, d_k, d_v);
+  if (h > ret::kMaxHeads) return fail(RET_E_UNSUPPORTED, "h = %d exceeds %d heads", h, ret::kMaxHeads);
+  if (chunk_B < 64 || chunk_B % 64) return fail(RET_E_UNSUPPORTED, "chunk_B must be a multiple of 64 (got %d)", chunk_B);
+  if (pos0 < 0) return fail(RET_E_INVAL, "pos0 must be >= 0");
+  if (flags & ~15u) return fail(RET_E_INVAL, "unknown flag bits 0x%x", flags & ~15u);
+  if (!valid_dt(in_dt) || !valid_dt(grad_dt)) return fail(RET_E_INVAL, "unknown dtype");
+  if (in_dt == RET_F32) return fail(RET_E_UNSUPPORTED, "the backward takes bf16 or f16 inputs");
+  if (grad_dt == RET_F16) return fail(RET_E_UNSUPPORTED, "gradients are written as f32 or bf16");
+  if (!ret::chunkwise_bwd_supported(d_k, d_v))
+    return fail(RET_E_UNSUPPORTED, "no backward kernel for d_k=%d d_v=%d", d_k, d_v);
+  int r;
+  if ((r = check_gamma(gamma, h))) return r;
+  if ((r = check_theta(theta, d_k, flags))) return r;
+  const size_t ie = dt_size(in_dt), ge = dt_size(grad_dt);
+  if ((r = check_view("q", q, sq, ie))) return r;
+  if ((r = check_view("k", k, sk, ie))) return r;
+  if ((r = check_view("v", v, sv, ie))) return r;
+  if ((r = check_view("dout", dout, sdo, ie))) return r;
+  if ((r = check_view("dq", dq, sdq, ge))) return r;
+  if ((r = check_view("dk", dk, sdk, ge))) return r;
+  if ((r = check_view("dv", dv, sdv, ge))) return r;
+  const void* ins[4] = {q, k, v, dout};
+  const void* outs[3] = {dq, dk, dv};
+  for (const void* o : outs)
+    for (const void* i : ins)
+      if (o == i) return fail(RET_E_INVAL, "gradient buffers must not alias the inputs");
+  if (dq == dk || dq == dv || dk == dv) return fail(RET_E_INVAL, "dq, dk and dv must be distinct");
+  const size_t need = ret::chunkwise_bwd_workspace(b, h, L, d_k, d_v, chunk_B);
+  if (!workspace || workspace_bytes < need)
+    return fail(RET_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : 0);
+  if (!aligned(workspace, 256)) return fail(RET_E_ALIGN, "workspace must be 256-byte aligned");
+
+  ret::HeadParams hp;
+  fill_params(hp, gamma, h, theta, d_k, flags);
+  ret::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.dout = dout;
+  a.gq = dq; a.gk = dk; a.gv = dv;
+  a.sq = sq; a.sk = sk; a.sv = sv; a.sdo = sdo; a.sgq = sdq; a.sgk = sdk; a.sgv = sdv;
+  a.b = b; a.h = h; a.L = L; a.d_k = d_k; a.d_v = d_v; a.B = chunk_B;
+  a.pos0 = pos0; a.flags = flags; a.in_dt = in_dt; a.grad_dt = grad_dt;
+  a.ws = workspace; a.hp = &hp;
+  return hip_status(ret::launch_chunkwise_bwd(a, stream), "retention_chunkwise_bwd launch");
+}
+
 int retention_recurrent_step(const void* q, const void* k, const void* v, float* S, float* z,
                              void* o, int b, int h, int d_k, int d_v,
                              const double* gamma, const double* theta,

@@ -1,0 +1,1001 @@
+// Chunkwise backward of the normalised retention (RetNet reading notes §2.4,
+// with the xPos rotation of §2.3 and the normalisations of §三.3): dq, dk and
+// dv of a fresh sequence from dL/dO.  Nothing is detached; on the clamp's
+// boundary |s den| = 1 its constant branch is taken.
+//
+// With q', k' the rotated inputs, g_p = dL/do_p and, for m <= p,
+//   A_pm = (q'_p . k'_m) gamma^(p-m),  num_p = sum_m A_pm v_m,  den_p = sum_m A_pm,
+//   o_p  = s_p num_p / n_p,  n_p = max(|s_p den_p|, 1) (1 without the score normalisation),
+// the chain rule reads
+//   a_p  = s_p / n_p,  c_p = -s_p^2 sign(den_p) (g_p . num_p) / n_p^2 where |s_p den_p| > 1, else 0,
+//   E_pm = gamma^(p-m) (a_p g_p . v_m + c_p)                (dL / d(q'_p . k'_m)),
+//   dq'_p = sum_m E_pm k'_m,  dk'_m = sum_p E_pm q'_p,  dv_m = sum_p a_p A_pm g_p.
+// Chunk c covers rows [c0, c1).  Terms reaching into earlier chunks go
+// through the forward state R_c = sum_{m<c0} gamma^(c0-1-m) k'_m v_m^T (and
+// the key-sum z_c); terms reaching into later chunks through the reverse
+// state U_c = sum_{p>=c1} gamma^(p-c1) q'_p (a_p g_p)^T (and u_c, weighted by c_p):
+//   dq'_p += gamma^(p-c0+1) (a_p R_c g_p + c_p z_c)
+//   dk'_m += gamma^(c1-m) (U_c v_m + u_c),   dv_m += gamma^(c1-m) U_c^T k'_m
+//   den_p += gamma^(p-c0+1) q'_p . z_c,      g_p . num_p += gamma^(p-c0+1) (q'_p R_c) . g_p
+// and dq, dk are dq', dk' rotated back by -p theta.
+//
+// Kernels, in order: prep (rotated q', k' and bf16 copies of v, dO, once),
+// fstate (R_c, z_c: a scan over the chunks), stats (a_p, c_p; only with the
+// score normalisation), rstate (U_c, u_c: a scan over the chunks from the
+// end), then dq, dk and dv, one 64-row tile per workgroup.  Every product is
+// an fp16 v_mfma_f32_32x32x16 with fp32 accumulation on 64-row tiles staged in
+// LDS (fp16's 11-bit significand: bf16 operands would make the roundings of
+// q', k' and of the E / a A tiles 8x larger).  Range: every gradient is linear
+// in dO, so dO is scaled per (batch, head) by a power of two that brings its
+// largest magnitude into [1/2, 1) (gmax + prep) and the results are scaled
+// back exactly; each 64 x 64 slab of a state copied to fp16 gets its own
+// power of two, undone when its product is added to the fp32 accumulator.
+// The remaining preconditions are the forward's (|q|, |k| < 2^15, |v| < 2^16,
+// s_p |q'_p . k'_m| < 2^16) and |a_p (g_p . v_m) + c_p| < 2^15 for the scaled dO.
+// A workgroup is 4 waves; wave w owns the 32 x 32 block (w / 2, w % 2) of
+// each 64 x 64 output tile.
+#include "internal.h"
+
+namespace ret {
+
+namespace {
+
+constexpr int BT = 256;        // threads per workgroup
+constexpr int TL = 64;         // rows per tile
+constexpr int SP = TL + 8;     // pitch (elements) of a 64-column LDS slab
+
+typedef short s16x4 __attribute__((__vector_size__(8)));
+typedef short s16x8 __attribute__((__vector_size__(16)));
+
+struct BwdP {
+  const void *q, *k, *v, *dout;
+  void *dq, *dk, *dv;
+  ret_strides sq, sk, sv, sdo, sdq, sdk, sdv;
+  int h, L, B, nc, nt;           // nt: 64-row tiles of the sequence
+  int64_t pos0;
+  unsigned flags;
+  uint16_t *Qr, *Kr, *Vb, *Gb;   // fp16 [bh][L][d]: q', k', v, 2^-e dO
+  float *tmax, *gsc;             // [bh][nt] tile maxima of |dO|; [bh] the 2^e of each head
+  float *Rin, *zin, *Ust, *ust;  // [bh][nc][DK][DV] and [bh][nc][DK]
+  float *ra, *rc;                // [bh][L]: a_p and c_p (with the score normalisation)
+};
+
+// ------------------------------------------------------------ fp16 packing
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  f16x2 v;
+  v.x = (half)lo;
+  v.y = (half)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float h_lo(uint32_t u) { return (float)__builtin_bit_cast(f16x2, u).x; }
+__device__ __forceinline__ float h_hi(uint32_t u) { return (float)__builtin_bit_cast(f16x2, u).y; }
+__device__ __forceinline__ float h2f(uint16_t u) { return (float)__builtin_bit_cast(half, u); }
+__device__ __forceinline__ uint16_t f2h(float x) { return __builtin_bit_cast(uint16_t, (half)x); }
+
+// ------------------------------------------------------------ fragments
+// A/B operand of v_mfma_f32_32x32x16_f16: lane l supplies row (A) or column
+// (B) l % 32 and the 8 consecutive k values 8 (l / 32) .. 8 (l / 32) + 7.
+// "nt": the LDS tile is stored [x][k] (k contiguous): one 16-byte read.
+__device__ __forceinline__ f16x8 fr_nt(const uint16_t* t, int pitch, int x0, int k0, int lane) {
+  return *reinterpret_cast<const f16x8*>(t + (x0 + (lane & 31)) * pitch + k0 + 8 * (lane >> 5));
+}
+// "tr": the LDS tile is stored [k][x].  ds_read_b64_tr_b16: within each group
+// of 16 lanes, lane i returns element (i & 3) of the 8-byte rows addressed by
+// lanes (i >> 2) + 4t, t = 0..3.  Lane j of group g addresses row
+// k0 + 8 (g / 2) + (j >> 2) at column x0 + 16 (g % 2) + 4 (j & 3), so lane i
+// receives rows k .. k + 3 at column x0 + 16 (g % 2) + i = x0 + l % 32; a
+// second read 4 rows further gives k + 4 .. k + 7.
+__device__ __forceinline__ f16x8 fr_tr(const uint16_t* t, int pitch, int x0, int k0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const uint16_t* p = t + (k0 + 8 * (g >> 1) + (j >> 2)) * pitch + x0 + 16 * (g & 1) + 4 * (j & 3);
+  s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 4 * pitch));
+  s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// acc += A B^T over a 64-deep k range: A rows xa .. xa + 31, B columns
+// xb .. xb + 31; ATR / BTR select the stored orientation of each operand
+template <bool ATR, bool BTR>
+__device__ __forceinline__ void mm64(f32x16& acc, const uint16_t* A, int pa, int xa, const uint16_t* B, int pb,
+                                     int xb, int lane) {
+#pragma unroll
+  for (int k0 = 0; k0 < 64; k0 += 16) {
+    const f16x8 a = ATR ? fr_tr(A, pa, xa, k0, lane) : fr_nt(A, pa, xa, k0, lane);
+    const f16x8 b = BTR ? fr_tr(B, pb, xb, k0, lane) : fr_nt(B, pb, xb, k0, lane);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+  }
+}
+
+// ------------------------------------------------------------ staging
+// rows [0, 64) x columns [0, NC) of an fp16 array (row length ld) -> LDS
+// [64][pitch]; rows >= nvalid are zero; scale (LDS, per row) multiplies a row
+template <int NC>
+__device__ __forceinline__ void stage(uint16_t* dst, int pitch, const uint16_t* src, int ld, int nvalid,
+                                      const float* scale) {
+  constexpr int PR = NC / 8;
+  for (int i = threadIdx.x; i < TL * PR; i += BT) {
+    const int r = i / PR, c8 = i - r * PR;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < nvalid) v = *reinterpret_cast<const u32x4*>(src + (int64_t)r * ld + 8 * c8);
+    if (scale) {
+      const float f = scale[r];
+      v.x = pack_h2(h_lo(v.x) * f, h_hi(v.x) * f);
+      v.y = pack_h2(h_lo(v.y) * f, h_hi(v.y) * f);
+      v.z = pack_h2(h_lo(v.z) * f, h_hi(v.z) * f);
+      v.w = pack_h2(h_lo(v.w) * f, h_hi(v.w) * f);
+    }
+    *reinterpret_cast<u32x4*>(dst + r * pitch + 8 * c8) = v;
+  }
+}
+
+// a 64 x 64 block of an fp32 matrix (row length ld) -> fp16 LDS [64][SP],
+// scaled by the power of two 2^-e that puts its largest magnitude in
+// [2^14, 2^15); returns 2^e.  red: 4 floats of LDS.  The whole workgroup
+// calls it (it synchronises once).
+__device__ __forceinline__ float stage_f32(uint16_t* dst, const float* src, int ld, float* red) {
+  constexpr int NP = TL * 16 / BT;
+  f32x4 v[NP];
+  float m = 0.f;
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int i = threadIdx.x + u * BT, r = i >> 4, c4 = i & 15;
+    v[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)r * ld + 4 * c4);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int ex = 0;
+  if (m > 0.f && m < 3.0e38f) {
+    frexpf(m, &ex);
+    ex = min(max(ex - 15, -120), 120);
+  }
+  const float down = ldexpf(1.f, -ex);
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int i = threadIdx.x + u * BT, r = i >> 4, c4 = i & 15;
+    uint2 w;
+    w.x = pack_h2(v[u][0] * down, v[u][1] * down);
+    w.y = pack_h2(v[u][2] * down, v[u][3] * down);
+    *reinterpret_cast<uint2*>(dst + r * SP + 4 * c4) = w;
+  }
+  return ldexpf(1.f, ex);
+}
+
+// NR rows x 64 columns of an fp32 matrix -> fp16 LDS [NR][SP] with one power
+// of two for the whole block (two passes over the source: the largest
+// magnitude, then the scaled copy); returns 2^e.  The whole workgroup calls
+// it (it synchronises once).
+template <int NR>
+__device__ __forceinline__ float stage_f32_rows(uint16_t* dst, const float* src, int ld, float* red) {
+  float m = 0.f;
+  for (int i = threadIdx.x; i < NR * 16; i += BT) {
+    const int r = i >> 4, c4 = i & 15;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (int64_t)r * ld + 4 * c4);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int ex = 0;
+  if (m > 0.f && m < 3.0e38f) {
+    frexpf(m, &ex);
+    ex = min(max(ex - 15, -120), 120);
+  }
+  const float down = ldexpf(1.f, -ex);
+  for (int i = threadIdx.x; i < NR * 16; i += BT) {
+    const int r = i >> 4, c4 = i & 15;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (int64_t)r * ld + 4 * c4);
+    uint2 w;
+    w.x = pack_h2(v[0] * down, v[1] * down);
+    w.y = pack_h2(v[2] * down, v[3] * down);
+    *reinterpret_cast<uint2*>(dst + r * SP + 4 * c4) = w;
+  }
+  return ldexpf(1.f, ex);
+}
+
+// the positive row scale s_p of a row that has seen n tokens (§三.3, first two factors)
+__device__ __forceinline__ float row_scale(const Decay& dec, unsigned flags, float qk, int64_t n) {
+  float s = qk;
+  if (flags & RET_NORM_DROW) s *= dec.drow((float)n);
+  return s;
+}
+
+// a_p and c_p of row p (p < L)
+__device__ __forceinline__ void row_ac(const BwdP& p, const Decay& dec, float qk, int bh, int row, float& a,
+                                       float& c) {
+  if (p.flags & RET_NORM_SCORE) {
+    a = p.ra[(int64_t)bh * p.L + row];
+    c = p.rc[(int64_t)bh * p.L + row];
+  } else {
+    a = row_scale(dec, p.flags, qk, row + 1);
+    c = 0.f;
+  }
+}
+
+template <typename TG> struct Out2;
+template <> struct Out2<float> {
+  __device__ __forceinline__ static void st(float* p, float a, float b) {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+  }
+};
+template <> struct Out2<bf16> {
+  __device__ __forceinline__ static void st(bf16* p, float a, float b) {
+    *reinterpret_cast<uint32_t*>(p) = pack_bf2(a, b);
+  }
+};
+
+// ------------------------------------------------------------ gmax
+// the largest |dO| of each 64-row tile
+template <typename T, int DV>
+__global__ void __launch_bounds__(BT) bwd_gmax_kernel(BwdP p) {
+  const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
+  const int bb = bh / p.h, hh = bh % p.h;
+  const int r0 = tile * TL, nv = min(TL, p.L - r0);
+  const T* g = reinterpret_cast<const T*>(p.dout) + bb * p.sdo.b + hh * p.sdo.h + r0 * p.sdo.l;
+  constexpr int VP = DV / 2;
+  float m = 0.f;
+  for (int i = threadIdx.x; i < nv * VP; i += BT) {
+    const int r = i / VP, cp = i - r * VP;
+    const float2 y = Elem<T>::ld2(g + (int64_t)r * p.sdo.l + 2 * cp);
+    m = fmaxf(m, fmaxf(fabsf(y.x), fabsf(y.y)));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  __shared__ float red[BT / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) p.tmax[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// ------------------------------------------------------------ prep
+// q', k' (rotated), v and 2^-e dO as contiguous fp16 rows, and 2^e of the head
+template <typename T, int DK, int DV>
+__global__ void __launch_bounds__(BT) bwd_prep_kernel(BwdP p, HeadParams hp) {
+  const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
+  const int bb = bh / p.h, hh = bh % p.h;
+  const int r0 = tile * TL, nv = min(TL, p.L - r0);
+  const T* q = reinterpret_cast<const T*>(p.q) + bb * p.sq.b + hh * p.sq.h + r0 * p.sq.l;
+  const T* k = reinterpret_cast<const T*>(p.k) + bb * p.sk.b + hh * p.sk.h + r0 * p.sk.l;
+  const T* v = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + hh * p.sv.h + r0 * p.sv.l;
+  const T* g = reinterpret_cast<const T*>(p.dout) + bb * p.sdo.b + hh * p.sdo.h + r0 * p.sdo.l;
+  const int64_t ro = (int64_t)bh * p.L + r0;
+  constexpr int PAIRS = DK / 2, RPP = BT / PAIRS;
+  const int j = threadIdx.x % PAIRS, i0 = threadIdx.x / PAIRS;
+  const bool xpos = (p.flags & RET_XPOS) != 0;
+  float c = 1.f, s = 0.f, c1 = 1.f, s1 = 0.f;
+  if (xpos) {
+    phase(p.pos0 + r0 + i0, hp.theta[j], c, s);
+    phase(RPP, hp.theta[j], c1, s1);
+  }
+  for (int i = i0; i < nv; i += RPP) {
+    float2 x = Elem<T>::ld2(q + (int64_t)i * p.sq.l + 2 * j);
+    float2 y = Elem<T>::ld2(k + (int64_t)i * p.sk.l + 2 * j);
+    if (xpos) {
+      rot(x.x, x.y, c, s);
+      rot(y.x, y.y, c, s);
+      advance(c, s, c1, s1);
+    }
+    *reinterpret_cast<uint32_t*>(p.Qr + (ro + i) * DK + 2 * j) = pack_h2(x.x, x.y);
+    *reinterpret_cast<uint32_t*>(p.Kr + (ro + i) * DK + 2 * j) = pack_h2(y.x, y.y);
+  }
+  // the head's power of two: 2^-e puts max |dO| in [1/2, 1)
+  __shared__ float red[BT / 64];
+  float m = 0.f;
+  for (int t = threadIdx.x; t < p.nt; t += BT) m = fmaxf(m, p.tmax[(int64_t)bh * p.nt + t]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int ex = 0;
+  if (m > 0.f && m < 3.0e38f) {
+    frexpf(m, &ex);
+    ex = min(max(ex, -120), 120);
+  }
+  const float down = ldexpf(1.f, -ex);
+  if (tile == 0 && threadIdx.x == 0) p.gsc[bh] = ldexpf(1.f, ex);
+  constexpr int VP = DV / 2;
+  for (int i = threadIdx.x; i < nv * VP; i += BT) {
+    const int r = i / VP, cp = i - r * VP;
+    const float2 x = Elem<T>::ld2(v + (int64_t)r * p.sv.l + 2 * cp);
+    const float2 y = Elem<T>::ld2(g + (int64_t)r * p.sdo.l + 2 * cp);
+    *reinterpret_cast<uint32_t*>(p.Vb + (ro + r) * DV + 2 * cp) = pack_h2(x.x, x.y);
+    *reinterpret_cast<uint32_t*>(p.Gb + (ro + r) * DV + 2 * cp) = pack_h2(y.x * down, y.y * down);
+  }
+}
+
+// ------------------------------------------------------------ state scans
+// REV = false: R_c, z_c for every chunk (R <- gamma^(B_c) R + K'^T (zeta V),
+// zeta_m = gamma^(c1-1-m)), walking the chunks forwards.
+// REV = true: U_c, u_c (U <- gamma^(B_c) U + Q'^T (w G), w_p = gamma^(p-c0) a_p,
+// and c_p in place of a_p for u), walking backwards.  The value stored for
+// chunk c is the state before that chunk is folded in.  A workgroup owns rows
+// [64 db, 64 db + 64) and columns [DVB eb, DVB eb + DVB) of the state.
+template <int DK, int DV, int DVB, bool REV>
+struct StateSmem {
+  uint16_t As[TL * SP];            // weighted k' (q') rows [row][d of the block]
+  uint16_t Bs[TL * (DVB + 8)];     // v (dO) rows [row][e of the block]
+  float w[TL];                     // row weights of As
+  float zw[TL];                    // row weights of the key-sum
+};
+
+template <int DK, int DV, int DVB, bool REV>
+__global__ void __launch_bounds__(BT) bwd_state_kernel(BwdP p, HeadParams hp) {
+  typedef StateSmem<DK, DV, DVB, REV> SM;
+  __shared__ SM sm;
+  constexpr int NDB = DK / 64, NEB = DV / DVB, NB = DVB / 64;   // NB column blocks of 32 per wave
+  constexpr int BP = DVB + 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bi = wave >> 1, bj = wave & 1;
+  const int eb = blockIdx.x % NEB;
+  const int db = (blockIdx.x / NEB) % NDB;
+  const int bh = blockIdx.x / (NEB * NDB);
+  const int head = bh % p.h;
+  Decay dec;
+  dec.init(hp.gamma[head]);
+  const float qk = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
+  const uint16_t* X = (REV ? p.Qr : p.Kr) + (int64_t)bh * p.L * DK + 64 * db;
+  const uint16_t* Y = (REV ? p.Gb : p.Vb) + (int64_t)bh * p.L * DV + DVB * eb;
+  float* dst = (REV ? p.Ust : p.Rin) + (int64_t)bh * p.nc * DK * DV;
+  float* zdst = (REV ? p.ust : p.zin) + (int64_t)bh * p.nc * DK;
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) acc[n] = f32x16{};
+  float zreg = 0.f;                         // z / u at d = 64 db + tid (tid < 64, eb == 0)
+
+  for (int step = 0; step < p.nc; ++step) {
+    const int c = REV ? p.nc - 1 - step : step;
+    const int c0 = c * p.B, Bc = min(p.B, p.L - c0), c1 = c0 + Bc;
+    // store the state entering chunk c
+    {
+      float* Sd = dst + (int64_t)c * DK * DV;
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int d = 64 * db + 32 * bi + acc_row(r, lane);
+          const int e = DVB * eb + 64 * n + 32 * bj + (lane & 31);
+          Sd[(int64_t)d * DV + e] = acc[n][r];
+        }
+      if (eb == 0 && tid < 64) zdst[(int64_t)c * DK + 64 * db + tid] = zreg;
+    }
+    const float gB = dec.pow((float)Bc);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] *= gB;
+    zreg *= gB;
+    for (int m0 = c0; m0 < c1; m0 += TL) {
+      const int nv = min(TL, c1 - m0);
+      __syncthreads();
+      if (tid < TL) {
+        const int row = m0 + tid;
+        float w = 0.f, zw = 0.f;
+        if (tid < nv) {
+          if (REV) {
+            float a, cc;
+            row_ac(p, dec, qk, bh, row, a, cc);
+            const float gp = dec.pow((float)(row - c0));
+            w = gp * a;
+            zw = gp * cc;
+          } else {
+            w = dec.pow((float)(c1 - 1 - row));
+            zw = w;
+          }
+        }
+        sm.w[tid] = w;
+        sm.zw[tid] = zw;
+      }
+      __syncthreads();
+      stage<64>(sm.As, SP, X + (int64_t)m0 * DK, DK, nv, sm.w);
+      stage<DVB>(sm.Bs, BP, Y + (int64_t)m0 * DV, DV, nv, nullptr);
+      __syncthreads();
+      if (eb == 0 && tid < 64) {
+        const uint16_t* xp = X + (int64_t)m0 * DK + tid;
+        for (int i = 0; i < nv; ++i) zreg += sm.zw[i] * h2f(xp[(int64_t)i * DK]);
+      }
+      // acc[d][e] += sum_row As[row][d] Bs[row][e]: both operands read transposed
+#pragma unroll
+      for (int n = 0; n < NB; ++n) mm64<true, true>(acc[n], sm.As, SP, 32 * bi, sm.Bs, BP, 64 * n + 32 * bj, lane);
+    }
+  }
+}
+
+// ------------------------------------------------------------ row statistics
+// a_p and c_p of one 64-row query tile (only with the score normalisation)
+template <int DK, int DV>
+struct StatsSmem {
+  uint16_t Qs[TL * (DK + 8)];
+  uint16_t Gs[TL * (DV + 8)];
+  uint16_t Sl[TL * SP];
+  float red[2][2][TL];             // [den / gnum][column half][row]
+  float qz[TL];                    // q'_p . z_c
+  float mx[4];
+};
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(BT) bwd_stats_kernel(BwdP p, HeadParams hp) {
+  typedef StatsSmem<DK, DV> SM;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  constexpr int QP = DK + 8, GP = DV + 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
+  const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
+  const int head = bh % p.h;
+  const int r0 = tile * TL, nq = min(TL, p.L - r0);
+  const int c = r0 / p.B, c0 = c * p.B;
+  Decay dec;
+  dec.init(hp.gamma[head]);
+  const float qk = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
+  const uint16_t* Qr = p.Qr + (int64_t)bh * p.L * DK;
+  const uint16_t* Kr = p.Kr + (int64_t)bh * p.L * DK;
+  const uint16_t* Vb = p.Vb + (int64_t)bh * p.L * DV;
+  const uint16_t* Gb = p.Gb + (int64_t)bh * p.L * DV;
+
+  stage<DK>(sm.Qs, QP, Qr + (int64_t)r0 * DK, DK, nq, nullptr);
+  stage<DV>(sm.Gs, GP, Gb + (int64_t)r0 * DV, DV, nq, nullptr);
+  float dsum[16], gsum[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dsum[r] = gsum[r] = 0.f;
+
+  // intra-chunk key tiles up to the diagonal
+  for (int m0 = c0; m0 <= r0; m0 += TL) {
+    const int nk = min(TL, p.L - m0);
+    f32x16 S = {}, T = {};
+    for (int ds = 0; ds < DK / 64; ++ds) {
+      __syncthreads();
+      stage<64>(sm.Sl, SP, Kr + (int64_t)m0 * DK + 64 * ds, DK, nk, nullptr);
+      __syncthreads();
+      mm64<false, false>(S, sm.Qs + 64 * ds, QP, 32 * bi, sm.Sl, SP, 32 * bj, lane);
+    }
+    for (int es = 0; es < DV / 64; ++es) {
+      __syncthreads();
+      stage<64>(sm.Sl, SP, Vb + (int64_t)m0 * DV + 64 * es, DV, nk, nullptr);
+      __syncthreads();
+      mm64<false, false>(T, sm.Gs + 64 * es, GP, 32 * bi, sm.Sl, SP, 32 * bj, lane);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = r0 + 32 * bi + acc_row(r, lane), col = m0 + 32 * bj + l32;
+      const bool ok = col <= row && col < p.L && row < p.L;
+      const float A = ok ? S[r] * dec.pow((float)(row - col)) : 0.f;
+      dsum[r] += A;
+      gsum[r] += A * T[r];
+    }
+  }
+  // cross part of g . num: xi_p (q'_p R_c) . g_p, column block by column block
+  if (c > 0) {
+    const float* R = p.Rin + ((int64_t)bh * p.nc + c) * DK * DV;
+    for (int es = 0; es < DV / 64; ++es) {
+      f32x16 X = {};
+      for (int ds = 0; ds < DK / 64; ++ds) {
+        __syncthreads();
+        const float up = stage_f32(sm.Sl, R + (int64_t)(64 * ds) * DV + 64 * es, DV, sm.mx);
+        __syncthreads();
+        // X[p][e] += sum_d Q'[p][d] R[d][e]; R staged [d][e] (k = d): transposed B
+        f32x16 t = {};
+        mm64<false, true>(t, sm.Qs + 64 * ds, QP, 32 * bi, sm.Sl, SP, 32 * bj, lane);
+        X += up * t;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pl = 32 * bi + acc_row(r, lane);
+        const float xi = dec.pow((float)(r0 + pl - c0 + 1));
+        const float gv = h2f(sm.Gs[pl * GP + 64 * es + 32 * bj + l32]);
+        gsum[r] += xi * X[r] * gv;
+      }
+    }
+    // q'_p . z_c: 4 threads per row
+    const float* z = p.zin + ((int64_t)bh * p.nc + c) * DK;
+    const int row = tid >> 2, part = tid & 3;
+    float acc = 0.f;
+    for (int d = part * (DK / 4); d < (part + 1) * (DK / 4); ++d) acc += h2f(sm.Qs[row * QP + d]) * z[d];
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    if (part == 0) sm.qz[row] = acc * dec.pow((float)(r0 + row - c0 + 1));
+  } else if (tid < TL) {
+    sm.qz[tid] = 0.f;
+  }
+  // row sums over the 32 columns of each half-wave, then over the two column blocks
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float d = dsum[r], g = gsum[r];
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+      d += __shfl_xor(d, o, 64);
+      g += __shfl_xor(g, o, 64);
+    }
+    if (l32 == 0) {
+      const int pl = 32 * bi + acc_row(r, lane);
+      sm.red[0][bj][pl] = d;
+      sm.red[1][bj][pl] = g;
+    }
+  }
+  __syncthreads();
+  if (tid < nq) {
+    const int row = r0 + tid;
+    const float den = sm.red[0][0][tid] + sm.red[0][1][tid] + sm.qz[tid];
+    const float gn = sm.red[1][0][tid] + sm.red[1][1][tid];
+    const float s = row_scale(dec, p.flags, qk, row + 1);
+    const float sd = fabsf(s * den);
+    const float n = fmaxf(sd, 1.f);
+    float cc = 0.f;
+    if (sd > 1.f) cc = -(s * s) * (den > 0.f ? 1.f : -1.f) * gn / (n * n);
+    p.ra[(int64_t)bh * p.L + row] = s / n;
+    p.rc[(int64_t)bh * p.L + row] = cc;
+  }
+}
+
+// ------------------------------------------------------------ epilogue
+// an fp32 tile [64][DK + 4] in LDS -> rows of dq / dk, times gs (the 2^e of
+// the head's dO) and rotated back by -p theta
+template <typename TG, int DK>
+__device__ __forceinline__ void store_rotated(const float* t, TG* out, const ret_strides& so, int bb, int hh, int r0,
+                                              int nrows, const BwdP& p, const HeadParams& hp, float gs) {
+  constexpr int PAIRS = DK / 2, RPP = BT / PAIRS, TP = DK + 4;
+  const int j = threadIdx.x % PAIRS, i0 = threadIdx.x / PAIRS;
+  const bool xpos = (p.flags & RET_XPOS) != 0;
+  float c = 1.f, s = 0.f, c1 = 1.f, s1 = 0.f;
+  if (xpos) {
+    phase(p.pos0 + r0 + i0, hp.theta[j], c, s);
+    phase(RPP, hp.theta[j], c1, s1);
+  }
+  TG* o = out + bb * so.b + hh * so.h;
+  for (int i = i0; i < nrows; i += RPP) {
+    float x0 = gs * t[i * TP + 2 * j], x1 = gs * t[i * TP + 2 * j + 1];
+    if (xpos) {
+      rot(x0, x1, c, -s);
+      advance(c, s, c1, s1);
+    }
+    Out2<TG>::st(o + (int64_t)(r0 + i) * so.l + 2 * j, x0, x1);
+  }
+}
+
+// ------------------------------------------------------------ dq
+template <int DK, int DV>
+struct DqSmem {
+  union {
+    struct {
+      uint16_t Gs[TL * (DV + 8)];
+      uint16_t Es[TL * SP];
+      uint16_t Sl[TL * SP];
+    } w;
+    float out[TL * (DK + 4)];
+  } u;
+  float ra[TL], rc[TL], xi[TL];
+  float mx[4];
+};
+
+template <typename TG, int DK, int DV>
+__global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
+  typedef DqSmem<DK, DV> SM;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  constexpr int GP = DV + 8, ND = DK / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
+  const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
+  const int bb = bh / p.h, head = bh % p.h;
+  const int r0 = tile * TL, nq = min(TL, p.L - r0);
+  const int c = r0 / p.B, c0 = c * p.B;
+  Decay dec;
+  dec.init(hp.gamma[head]);
+  const float qk = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
+  const uint16_t* Kr = p.Kr + (int64_t)bh * p.L * DK;
+  const uint16_t* Vb = p.Vb + (int64_t)bh * p.L * DV;
+  const uint16_t* Gb = p.Gb + (int64_t)bh * p.L * DV;
+
+  if (tid < TL) {
+    float a = 0.f, cc = 0.f;
+    if (tid < nq) row_ac(p, dec, qk, bh, r0 + tid, a, cc);
+    sm.ra[tid] = a;
+    sm.rc[tid] = cc;
+    sm.xi[tid] = dec.pow((float)(r0 + tid - c0 + 1));
+  }
+  stage<DV>(sm.u.w.Gs, GP, Gb + (int64_t)r0 * DV, DV, nq, nullptr);
+  f32x16 acc[ND];
+#pragma unroll
+  for (int n = 0; n < ND; ++n) acc[n] = f32x16{};
+
+  // cross: xi_p (a_p (G R_c^T)_pd + c_p z_c[d])
+  if (c > 0) {
+    const float* R = p.Rin + ((int64_t)bh * p.nc + c) * DK * DV;
+    const float* z = p.zin + ((int64_t)bh * p.nc + c) * DK;
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds)
+      for (int es = 0; es < DV / 64; ++es) {
+        __syncthreads();
+        const float up = stage_f32(sm.u.w.Sl, R + (int64_t)(64 * ds) * DV + 64 * es, DV, sm.mx);
+        __syncthreads();
+        // B[n = d][k = e] = R[d][e], staged [d][e]: "nt"
+        f32x16 t = {};
+        mm64<false, false>(t, sm.u.w.Gs + 64 * es, GP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
+        acc[ds] += up * t;
+      }
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds) {
+      const float zd = z[64 * ds + 32 * bj + l32];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pl = 32 * bi + acc_row(r, lane);
+        acc[ds][r] = sm.xi[pl] * (sm.ra[pl] * acc[ds][r] + sm.rc[pl] * zd);
+      }
+    }
+  }
+  // intra-chunk key tiles up to the diagonal
+  for (int m0 = c0; m0 <= r0; m0 += TL) {
+    const int nk = min(TL, p.L - m0);
+    f32x16 T = {};
+    for (int es = 0; es < DV / 64; ++es) {
+      __syncthreads();
+      stage<64>(sm.u.w.Sl, SP, Vb + (int64_t)m0 * DV + 64 * es, DV, nk, nullptr);
+      __syncthreads();
+      mm64<false, false>(T, sm.u.w.Gs + 64 * es, GP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
+    }
+    // E[p][m] -> LDS (row p, column m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int pl = 32 * bi + acc_row(r, lane), ml = 32 * bj + l32;
+      const int row = r0 + pl, col = m0 + ml;
+      const bool ok = col <= row && col < p.L && row < p.L;
+      const float e = ok ? dec.pow((float)(row - col)) * (sm.ra[pl] * T[r] + sm.rc[pl]) : 0.f;
+      sm.u.w.Es[pl * SP + ml] = f2h(e);
+    }
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds) {
+      __syncthreads();
+      stage<64>(sm.u.w.Sl, SP, Kr + (int64_t)m0 * DK + 64 * ds, DK, nk, nullptr);
+      __syncthreads();
+      // dq'[p][d] += sum_m E[p][m] K'[m][d]; K' staged [m][d] (k = m): transposed B
+      mm64<false, true>(acc[ds], sm.u.w.Es, SP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ds = 0; ds < ND; ++ds)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      sm.u.out[(32 * bi + acc_row(r, lane)) * (DK + 4) + 64 * ds + 32 * bj + l32] = acc[ds][r];
+  __syncthreads();
+  store_rotated<TG, DK>(sm.u.out, reinterpret_cast<TG*>(p.dq), p.sdq, bb, head, r0, nq, p, hp, p.gsc[bh]);
+}
+
+// ------------------------------------------------------------ dk
+template <int DK, int DV>
+struct DkSmem {
+  union {
+    struct {
+      uint16_t Vs[TL * (DV + 8)];
+      uint16_t Es[TL * SP];        // E^T [m][p]
+      uint16_t Sl[TL * SP];
+    } w;
+    float out[TL * (DK + 4)];
+  } u;
+  float pa[TL], pc[TL];
+  float mx[4];
+};
+
+template <typename TG, int DK, int DV>
+__global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
+  typedef DkSmem<DK, DV> SM;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  constexpr int VP = DV + 8, ND = DK / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
+  const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
+  const int bb = bh / p.h, head = bh % p.h;
+  const int m0 = tile * TL, nk = min(TL, p.L - m0);
+  const int c = m0 / p.B, c0 = c * p.B, c1 = min(c0 + p.B, p.L);
+  Decay dec;
+  dec.init(hp.gamma[head]);
+  const float qk = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
+  const uint16_t* Qr = p.Qr + (int64_t)bh * p.L * DK;
+  const uint16_t* Vb = p.Vb + (int64_t)bh * p.L * DV;
+  const uint16_t* Gb = p.Gb + (int64_t)bh * p.L * DV;
+
+  stage<DV>(sm.u.w.Vs, VP, Vb + (int64_t)m0 * DV, DV, nk, nullptr);
+  f32x16 acc[ND];
+#pragma unroll
+  for (int n = 0; n < ND; ++n) acc[n] = f32x16{};
+
+  // cross: gamma^(c1-m) ((V U_c^T)[m][d] + u_c[d])
+  if (c + 1 < p.nc) {
+    const float* U = p.Ust + ((int64_t)bh * p.nc + c) * DK * DV;
+    const float* u = p.ust + ((int64_t)bh * p.nc + c) * DK;
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds)
+      for (int es = 0; es < DV / 64; ++es) {
+        __syncthreads();
+        const float up = stage_f32(sm.u.w.Sl, U + (int64_t)(64 * ds) * DV + 64 * es, DV, sm.mx);
+        __syncthreads();
+        f32x16 t = {};
+        mm64<false, false>(t, sm.u.w.Vs + 64 * es, VP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
+        acc[ds] += up * t;
+      }
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds) {
+      const float ud = u[64 * ds + 32 * bj + l32];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + 32 * bi + acc_row(r, lane);
+        acc[ds][r] = dec.pow((float)(c1 - row)) * (acc[ds][r] + ud);
+      }
+    }
+  }
+  // intra-chunk query tiles from the diagonal to the chunk end
+  for (int q0 = m0; q0 < c1; q0 += TL) {
+    const int nq = min(TL, p.L - q0);
+    __syncthreads();
+    if (tid < TL) {
+      float a = 0.f, cc = 0.f;
+      if (tid < nq) row_ac(p, dec, qk, bh, q0 + tid, a, cc);
+      sm.pa[tid] = a;
+      sm.pc[tid] = cc;
+    }
+    f32x16 T = {};
+    for (int es = 0; es < DV / 64; ++es) {
+      __syncthreads();
+      stage<64>(sm.u.w.Sl, SP, Gb + (int64_t)q0 * DV + 64 * es, DV, nq, nullptr);
+      __syncthreads();
+      // T^T[m][p] = sum_e V[m][e] G[p][e]
+      mm64<false, false>(T, sm.u.w.Vs + 64 * es, VP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ml = 32 * bi + acc_row(r, lane), pl = 32 * bj + l32;
+      const int row = q0 + pl, col = m0 + ml;
+      const bool ok = col <= row && col < p.L && row < p.L;
+      const float e = ok ? dec.pow((float)(row - col)) * (sm.pa[pl] * T[r] + sm.pc[pl]) : 0.f;
+      sm.u.w.Es[ml * SP + pl] = f2h(e);
+    }
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds) {
+      __syncthreads();
+      stage<64>(sm.u.w.Sl, SP, Qr + (int64_t)q0 * DK + 64 * ds, DK, nq, nullptr);
+      __syncthreads();
+      // dk'[m][d] += sum_p E^T[m][p] Q'[p][d]; Q' staged [p][d] (k = p): transposed B
+      mm64<false, true>(acc[ds], sm.u.w.Es, SP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ds = 0; ds < ND; ++ds)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      sm.u.out[(32 * bi + acc_row(r, lane)) * (DK + 4) + 64 * ds + 32 * bj + l32] = acc[ds][r];
+  __syncthreads();
+  store_rotated<TG, DK>(sm.u.out, reinterpret_cast<TG*>(p.dk), p.sdk, bb, head, m0, nk, p, hp, p.gsc[bh]);
+}
+
+// ------------------------------------------------------------ dv
+template <int DK, int DV>
+struct DvSmem {
+  uint16_t Ks[TL * (DK + 8)];
+  uint16_t As[TL * SP];            // a_p A^T [m][p]
+  uint16_t Sl[TL * SP];
+  uint16_t Ub[DK * SP];            // one 64-column block of U_c, all d rows
+  float pa[TL];
+  float mx[4];
+};
+
+template <typename TG, int DK, int DV>
+__global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
+  typedef DvSmem<DK, DV> SM;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  constexpr int KP = DK + 8, NE = DV / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
+  const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
+  const int bb = bh / p.h, head = bh % p.h;
+  const int m0 = tile * TL, nk = min(TL, p.L - m0);
+  const int c = m0 / p.B, c0 = c * p.B, c1 = min(c0 + p.B, p.L);
+  Decay dec;
+  dec.init(hp.gamma[head]);
+  const float qk = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
+  const uint16_t* Qr = p.Qr + (int64_t)bh * p.L * DK;
+  const uint16_t* Kr = p.Kr + (int64_t)bh * p.L * DK;
+  const uint16_t* Gb = p.Gb + (int64_t)bh * p.L * DV;
+
+  stage<DK>(sm.Ks, KP, Kr + (int64_t)m0 * DK, DK, nk, nullptr);
+  f32x16 acc[NE];
+#pragma unroll
+  for (int n = 0; n < NE; ++n) acc[n] = f32x16{};
+
+  // cross: gamma^(c1-m) (K' U_c)[m][e]
+  if (c + 1 < p.nc) {
+    const float* U = p.Ust + ((int64_t)bh * p.nc + c) * DK * DV;
+#pragma unroll
+    for (int es = 0; es < NE; ++es) {
+      __syncthreads();
+      const float up = stage_f32_rows<DK>(sm.Ub, U + 64 * es, DV, sm.mx);
+      __syncthreads();
+      // B[n = e][k = d] = U[d][e], staged [d][e]: transposed B; acc[es] starts at zero
+#pragma unroll
+      for (int ds = 0; ds < DK / 64; ++ds)
+        mm64<false, true>(acc[es], sm.Ks + 64 * ds, KP, 32 * bi, sm.Ub + 64 * ds * SP, SP, 32 * bj, lane);
+      acc[es] *= up;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float f = dec.pow((float)(c1 - (m0 + 32 * bi + acc_row(r, lane))));
+#pragma unroll
+      for (int es = 0; es < NE; ++es) acc[es][r] *= f;
+    }
+  }
+  for (int q0 = m0; q0 < c1; q0 += TL) {
+    const int nq = min(TL, p.L - q0);
+    __syncthreads();
+    if (tid < TL) {
+      float a = 0.f, cc = 0.f;
+      if (tid < nq) row_ac(p, dec, qk, bh, q0 + tid, a, cc);
+      sm.pa[tid] = a;
+    }
+    f32x16 S = {};
+    for (int ds = 0; ds < DK / 64; ++ds) {
+      __syncthreads();
+      stage<64>(sm.Sl, SP, Qr + (int64_t)q0 * DK + 64 * ds, DK, nq, nullptr);
+      __syncthreads();
+      // S^T[m][p] = sum_d K'[m][d] Q'[p][d]
+      mm64<false, false>(S, sm.Ks + 64 * ds, KP, 32 * bi, sm.Sl, SP, 32 * bj, lane);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ml = 32 * bi + acc_row(r, lane), pl = 32 * bj + l32;
+      const int row = q0 + pl, col = m0 + ml;
+      const bool ok = col <= row && col < p.L && row < p.L;
+      const float x = ok ? sm.pa[pl] * dec.pow((float)(row - col)) * S[r] : 0.f;
+      sm.As[ml * SP + pl] = f2h(x);
+    }
+#pragma unroll
+    for (int es = 0; es < NE; ++es) {
+      __syncthreads();
+      stage<64>(sm.Sl, SP, Gb + (int64_t)q0 * DV + 64 * es, DV, nq, nullptr);
+      __syncthreads();
+      // dv[m][e] += sum_p (a A^T)[m][p] G[p][e]; G staged [p][e] (k = p): transposed B
+      mm64<false, true>(acc[es], sm.As, SP, 32 * bi, sm.Sl, SP, 32 * bj, lane);
+    }
+  }
+  TG* o = reinterpret_cast<TG*>(p.dv) + bb * p.sdv.b + head * p.sdv.h;
+  const float gs = p.gsc[bh];
+#pragma unroll
+  for (int es = 0; es < NE; ++es)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ml = 32 * bi + acc_row(r, lane);
+      if (ml < nk) o[(int64_t)(m0 + ml) * p.sdv.l + 64 * es + 32 * bj + l32] = Store<TG>::cvt(gs * acc[es][r]);
+    }
+}
+
+// ------------------------------------------------------------ host side
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Carve {
+  size_t qr, kr, vb, gb, rin, zin, ust, us, ra, rc, tmax, gsc, total;
+};
+
+Carve carve_bwd(int b, int h, int L, int dk, int dv, int B) {
+  const size_t bh = (size_t)b * h, nc = (size_t)((L + B - 1) / B);
+  Carve c;
+  size_t o = 0;
+  c.qr = o; o += al256(bh * L * dk * 2);
+  c.kr = o; o += al256(bh * L * dk * 2);
+  c.vb = o; o += al256(bh * L * dv * 2);
+  c.gb = o; o += al256(bh * L * dv * 2);
+  c.rin = o; o += al256(bh * nc * dk * dv * 4);
+  c.zin = o; o += al256(bh * nc * dk * 4);
+  c.ust = o; o += al256(bh * nc * dk * dv * 4);
+  c.us = o; o += al256(bh * nc * dk * 4);
+  c.ra = o; o += al256(bh * L * 4);
+  c.rc = o; o += al256(bh * L * 4);
+  c.tmax = o; o += al256(bh * (size_t)((L + TL - 1) / TL) * 4);
+  c.gsc = o; o += al256(bh * 4);
+  c.total = o;
+  return c;
+}
+
+template <typename K>
+hipError_t set_smem(K k, size_t bytes) {
+  return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <typename T, typename TG, int DK, int DV>
+hipError_t run_bwd(const BwdArgs& a, hipStream_t st) {
+  BwdP p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout;
+  p.dq = a.gq; p.dk = a.gk; p.dv = a.gv;
+  p.sq = a.sq; p.sk = a.sk; p.sv = a.sv; p.sdo = a.sdo; p.sdq = a.sgq; p.sdk = a.sgk; p.sdv = a.sgv;
+  p.h = a.h; p.L = a.L; p.B = a.B;
+  p.nc = (a.L + a.B - 1) / a.B;
+  p.nt = (a.L + TL - 1) / TL;
+  p.pos0 = a.pos0; p.flags = a.flags;
+  const Carve cv = carve_bwd(a.b, a.h, a.L, DK, DV, a.B);
+  unsigned char* w = static_cast<unsigned char*>(a.ws);
+  p.Qr = reinterpret_cast<uint16_t*>(w + cv.qr);
+  p.Kr = reinterpret_cast<uint16_t*>(w + cv.kr);
+  p.Vb = reinterpret_cast<uint16_t*>(w + cv.vb);
+  p.Gb = reinterpret_cast<uint16_t*>(w + cv.gb);
+  p.Rin = reinterpret_cast<float*>(w + cv.rin);
+  p.zin = reinterpret_cast<float*>(w + cv.zin);
+  p.Ust = reinterpret_cast<float*>(w + cv.ust);
+  p.ust = reinterpret_cast<float*>(w + cv.us);
+  p.ra = reinterpret_cast<float*>(w + cv.ra);
+  p.rc = reinterpret_cast<float*>(w + cv.rc);
+  p.tmax = reinterpret_cast<float*>(w + cv.tmax);
+  p.gsc = reinterpret_cast<float*>(w + cv.gsc);
+  const int bh = a.b * a.h;
+  const HeadParams& hp = *a.hp;
+  constexpr int DVB = DV < 256 ? DV : 256;
+  const dim3 tiles(bh * p.nt), sgrid(bh * (DK / 64) * (DV / DVB)), blk(BT);
+  hipError_t e;
+  hipLaunchKernelGGL((bwd_gmax_kernel<T, DV>), tiles, blk, 0, st, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_prep_kernel<T, DK, DV>), tiles, blk, 0, st, p, hp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_state_kernel<DK, DV, DVB, false>), sgrid, blk, 0, st, p, hp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.flags & RET_NORM_SCORE) {
+    auto k = bwd_stats_kernel<DK, DV>;
+    if ((e = set_smem(k, sizeof(StatsSmem<DK, DV>))) != hipSuccess) return e;
+    hipLaunchKernelGGL(k, tiles, blk, sizeof(StatsSmem<DK, DV>), st, p, hp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((bwd_state_kernel<DK, DV, DVB, true>), sgrid, blk, 0, st, p, hp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    auto k = bwd_dq_kernel<TG, DK, DV>;
+    if ((e = set_smem(k, sizeof(DqSmem<DK, DV>))) != hipSuccess) return e;
+    hipLaunchKernelGGL(k, tiles, blk, sizeof(DqSmem<DK, DV>), st, p, hp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    auto k = bwd_dk_kernel<TG, DK, DV>;
+    if ((e = set_smem(k, sizeof(DkSmem<DK, DV>))) != hipSuccess) return e;
+    hipLaunchKernelGGL(k, tiles, blk, sizeof(DkSmem<DK, DV>), st, p, hp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    auto k = bwd_dv_kernel<TG, DK, DV>;
+    if ((e = set_smem(k, sizeof(DvSmem<DK, DV>))) != hipSuccess) return e;
+    hipLaunchKernelGGL(k, tiles, blk, sizeof(DvSmem<DK, DV>), st, p, hp);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int DK, int DV>
+hipError_t run_bwd_g(const BwdArgs& a, hipStream_t st) {
+  return a.grad_dt == RET_BF16 ? run_bwd<T, bf16, DK, DV>(a, st) : run_bwd<T, float, DK, DV>(a, st);
+}
+
+#define RET_BWD_SHAPES(X) X(64, 64) X(128, 128) X(128, 256) X(256, 512)
+
+}  // namespace
+
+bool chunkwise_bwd_supported(int dk, int dv) {
+#define X(DK, DV) if (dk == DK && dv == DV) return true;
+  RET_BWD_SHAPES(X)
+#undef X
+  return false;
+}
+
+size_t chunkwise_bwd_workspace(int b, int h, int L, int dk, int dv, int B) {
+  return carve_bwd(b, h, L, dk, dv, B).total;
+}
+
+hipError_t launch_chunkwise_bwd(const BwdArgs& a, hipStream_t st) {
+#define X(DK, DV)                                                                                   \
+  if (a.d_k == DK && a.d_v == DV)                                                                   \
+    return a.in_dt == RET_F16 ? run_bwd_g<half, DK, DV>(a, st) : run_bwd_g<bf16, DK, DV>(a, st);
+  RET_BWD_SHAPES(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ret

@@ -79,6 +79,22 @@ bool three_phase_applies(ret_dtype in_dt, int dk, int dv, int B);
 size_t three_phase_workspace(int b, int h, int L, int B);
 hipError_t launch_three_phase(const ChunkArgs& a, hipStream_t st);
 
+// chunkwise backward of a fresh sequence: dq, dk, dv (gq, gk, gv) from dO
+struct BwdArgs {
+  const void *q, *k, *v, *dout;
+  void *gq, *gk, *gv;
+  ret_strides sq, sk, sv, sdo, sgq, sgk, sgv;
+  int b, h, L, d_k, d_v, B;
+  int64_t pos0;
+  unsigned flags;
+  ret_dtype in_dt, grad_dt;
+  void* ws;
+  const HeadParams* hp;
+};
+bool chunkwise_bwd_supported(int dk, int dv);
+size_t chunkwise_bwd_workspace(int b, int h, int L, int dk, int dv, int B);
+hipError_t launch_chunkwise_bwd(const BwdArgs& a, hipStream_t st);
+
 // R: optional residual [M][N] of c_dt added after the optional exact gelu (act != 0)
 hipError_t launch_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
                        const void* R, ret_dtype r_dt, int act, hipStream_t st);

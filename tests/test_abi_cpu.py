@@ -139,3 +139,66 @@ def test_gemm_validation(B):
 def test_workspace_query(B):
     assert B.LIB.retention_chunkwise_workspace_bytes(1, 2, 128, 32, 32, 64, 15) == 0
     assert B.LIB.retention_chunkwise_workspace_bytes(0, 2, 128, 32, 32, 64, 15) == 0
+
+
+def _bwd(B, **kw):
+    g = np.array([0.9, 0.99])
+    st = B.Strides(2 * 128 * 64, 128 * 64, 64)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, do=FAKE, dq=ctypes.c_void_p(0x200000), dk=ctypes.c_void_p(0x300000),
+             dv=ctypes.c_void_p(0x400000), b=1, h=2, L=128, dk_=64, dv_=64, chunk=64, gamma=g,
+             theta=np.ones(32), pos0=0, flags=15, in_dt=1, g_dt=0, ws=ctypes.c_void_p(0x10000000), wsb=1 << 30)
+    a.update(kw)
+    gp = None if a["gamma"] is None else _dptr(a["gamma"])
+    tp = None if a["theta"] is None else _dptr(a["theta"])
+    r = B.LIB.retention_chunkwise_bwd(a["q"], st, a["k"], st, a["v"], st, a["do"], st, a["dq"], st, a["dk"], st,
+                                      a["dv"], st, a["b"], a["h"], a["L"], a["dk_"], a["dv_"], a["chunk"], gp, tp,
+                                      a["pos0"], a["flags"], a["in_dt"], a["g_dt"], a["ws"], a["wsb"], None)
+    return r, B.LIB.retention_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(chunk=100), 2, "multiple of 64"),
+    (dict(chunk=0), 2, "multiple of 64"),
+    (dict(in_dt=0), 2, "bf16 or f16"),
+    (dict(g_dt=2), 2, "f32 or bf16"),
+    (dict(dk_=32, dv_=32, theta=np.ones(16)), 2, "no backward kernel"),
+    (dict(do=None), 1, "dout is NULL"),
+    (dict(dq=FAKE), 1, "alias"),
+    (dict(dk=ctypes.c_void_p(0x200000)), 1, "distinct"),
+    (dict(wsb=16), 4, "workspace"),
+    (dict(ws=ctypes.c_void_p(0x10000010)), 3, "256-byte"),
+    (dict(theta=None), 1, "theta"),
+    (dict(gamma=np.array([0.9, 1.5])), 1, "gamma[1]"),
+    (dict(pos0=-1), 1, "pos0"),
+    (dict(dv=FAKE_MIS), 3, "aligned"),
+])
+def test_bwd_validation(B, kw, code, msg):
+    r, err = _bwd(B, **kw)
+    assert r == code, (r, err)
+    assert msg in err
+
+
+def test_bwd_workspace_query(B):
+    n = B.LIB.retention_chunkwise_bwd_workspace_bytes(2, 3, 300, 128, 256, 128)
+    # q', k', v, dO (fp16), two state sets of 3 chunks (fp32), two row vectors
+    bh, nc = 6, 3
+    # and the per-tile maxima of |dO| and the per-head scale
+    least = (bh * 300 * (2 * 128 + 2 * 256) * 2 + 2 * bh * nc * (128 * 256 + 128) * 4 + 2 * bh * 300 * 4
+             + bh * 5 * 4 + bh * 4)
+    assert least <= n <= least + 12 * 256
+    assert B.LIB.retention_chunkwise_bwd_workspace_bytes(0, 3, 300, 128, 256, 128) == 0
+
+
+def test_layer_norm_and_gemm_ex_validation(B):
+    L = B.LIB
+    x, y = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    assert L.ret_layer_norm(x, y, 4, 12, None, None, 1e-5, 0, 0, None) == 2       # d % 8
+    assert L.ret_layer_norm(x, y, 4, 16, None, None, -1.0, 0, 0, None) == 1       # eps
+    assert L.ret_layer_norm(x, x, 4, 16, None, None, 1e-5, 0, 0, None) == 1       # alias
+    assert L.ret_layer_norm(FAKE_MIS, y, 4, 16, None, None, 1e-5, 0, 0, None) == 3
+    assert L.ret_layer_norm(x, y, 4, 16384, None, None, 1e-5, 0, 0, None) == 2    # d > 8192
+    A, Bm, C = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    assert L.msr_gemm_ex(A, 1, Bm, C, 0, 16, 16, 64, None, 0, 4, None) == 1      # unknown epilogue bit
+    assert L.msr_gemm_ex(A, 1, Bm, C, 0, 16, 16, 64, C, 1, 0, None) == 1         # residual C with another dtype
+    assert L.msr_gemm_ex(A, 1, Bm, C, 0, 16, 16, 64, A, 1, 0, None) == 1         # residual aliases A
+    assert L.msr_gemm_ex(A, 1, Bm, C, 0, 16, 16, 64, FAKE_MIS, 0, 0, None) == 3
