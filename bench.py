@@ -7,7 +7,8 @@ three normalisations, bf16 output): value = tokens/s = b*L / step time.  The
 inputs are resident in HBM before timing; three input/output buffer sets are
 rotated so the 256 MB MALL cannot serve a repeated set.  Secondary lines in
 the same JSON record: the same workload at B = 64, the long workload (L =
-32768, 16 heads), the decode step (batch 128, 16 heads, 64 steps from
+32768, 16 heads), the chunkwise backward on the medium workload, the decode
+step (batch 128, 16 heads, 64 steps from
 position 8192), the GroupNorm + gate epilogue at the block shape, the gated
 MSR block (2 x 8192 tokens, d_model 4096), one RetNet layer around it
 (LayerNorms, residuals and a 4 x d_model gelu FFN), and that layer decoding
@@ -70,6 +71,23 @@ def chunk_flops(b, h, L, dk, dv, B, with_state_out=False):
     cross = (nc - 1) * 2 * B * dk * dv
     state = (nc - 1 + (1 if with_state_out else 0)) * 2 * B * dk * dv
     return b * h * (intra + cross + state)
+
+
+def bwd_flops(b, h, L, dk, dv, B, score_norm):
+    """Algorithmic flops of the chunkwise backward, each product counted once:
+    the causal half of the intra-chunk products Q'K'^T and dO V^T, E K',
+    E^T Q' and (a A)^T dO; the cross terms dO R^T (chunks >= 1), V U^T and
+    K' U (chunks before the last), q' R . dO for the clamp statistics (with
+    the score normalisation); and the two state scans K'^T (zeta V) and
+    Q'^T (w dO)."""
+    nc = (L + B - 1) // B
+    pairs = sum(min(B, L - c * B) * (min(B, L - c * B) + 1) // 2 for c in range(nc))
+    intra = 2 * pairs * ((dk + dv) + (2 * dk + dv))
+    rows_after_first = max(L - B, 0)
+    rows_before_last = L - min(B, L - (nc - 1) * B)
+    cross = 2 * dk * dv * (rows_after_first * (2 if score_norm else 1) + 2 * rows_before_last)
+    states = 2 * 2 * L * dk * dv
+    return b * h * (intra + cross + states)
 
 
 def chunk_bytes(b, h, L, dk, dv, in_bytes=2, out_bytes=2):
@@ -136,7 +154,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true", help="time the primary workload only")
-    ap.add_argument("--secondary", default="medium_B64,long,decode,gate_norm,block,layer,decode_layer,copy",
+    ap.add_argument("--secondary", default="medium_B64,backward,long,decode,gate_norm,block,layer,decode_layer,copy",
                     help="comma list of secondary measurements to run (empty for none)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -206,6 +224,27 @@ def main():
                                "tflops": round(f64_ / (ms64 * 1e-3) / 1e12, 1),
                                "mfma_frac": round(f64_ / (ms64 * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
                                "gbs": round(nbytes / (ms64 * 1e-3) / 1e9, 1)}
+    if "backward" in todo:
+        # chunkwise backward on the medium workload (dq, dk, dv in fp32 from a bf16 dO)
+        qd, kd, vd, _ = sets[0]
+        rng = np.random.default_rng(77)
+        dod = dev(W.draw(rng, (b, h, L, dv), 1.0, "bf16"))
+        grads = [torch.empty((b, h, L, dk), device="cuda"), torch.empty((b, h, L, dk), device="cuda"),
+                 torch.empty((b, h, L, dv), device="cuda")]
+        best = None
+        for Bb in (256, 512):
+            wsb = torch.empty(R.chunkwise_bwd_workspace_bytes(b, h, L, dk, dv, Bb), dtype=torch.uint8, device="cuda")
+            msb = time_calls(lambda: R.chunkwise_bwd(qd, kd, vd, dod, g, th, Bb, flags, dq=grads[0], dk=grads[1],
+                                                     dv=grads[2], workspace=wsb), max(5, args.steps // 2), 2, torch)
+            fl = bwd_flops(b, h, L, dk, dv, Bb, True)
+            ent = {"ms": round(msb, 4), "chunk": Bb, "tokens_per_s": tokens / (msb * 1e-3),
+                   "tflops": round(fl / (msb * 1e-3) / 1e12, 1),
+                   "mfma_frac": round(fl / (msb * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4), "alg_gflop": round(fl / 1e9, 2)}
+            if best is None or msb < best["ms"]:
+                best = ent
+            del wsb
+        extra["backward"] = best
+        del dod, grads
     del sets[:]
     torch.cuda.empty_cache()
     if "long" in todo:
