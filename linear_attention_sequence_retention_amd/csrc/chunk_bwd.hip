@@ -56,6 +56,7 @@ struct BwdP {
   unsigned flags;
   uint16_t *Qr, *Kr, *Vb, *Gb;   // fp16 [bh][L][d]: q', k', v, 2^-e dO
   float *tmax, *gsc;             // [bh][nt] tile maxima of |dO|; [bh] the 2^e of each head
+  float *rmax, *umax;            // [bh][nc][partial maxima] of |R_c| and |U_c|
   float *Rin, *zin, *Ust, *ust;  // [bh][nc][DK][DV] and [bh][nc][DK]
   float *ra, *rc;                // [bh][L]: a_p and c_p (with the score normalisation)
 };
@@ -109,94 +110,37 @@ __device__ __forceinline__ void mm64(f32x16& acc, const uint16_t* A, int pa, int
 
 // ------------------------------------------------------------ staging
 // rows [0, 64) x columns [0, NC) of an fp16 array (row length ld) -> LDS
-// [64][pitch]; rows >= nvalid are zero; scale (LDS, per row) multiplies a row
+// [64][pitch]; rows >= nvalid are zero; scale (LDS, per row) multiplies a
+// row.  The loads are issued in batches of up to 8 per thread before their
+// stores, unconditionally (rows clamped, then selected), so they overlap.
 template <int NC>
 __device__ __forceinline__ void stage(uint16_t* dst, int pitch, const uint16_t* src, int ld, int nvalid,
                                       const float* scale) {
-  constexpr int PR = NC / 8;
-  for (int i = threadIdx.x; i < TL * PR; i += BT) {
-    const int r = i / PR, c8 = i - r * PR;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < nvalid) v = *reinterpret_cast<const u32x4*>(src + (int64_t)r * ld + 8 * c8);
-    if (scale) {
-      const float f = scale[r];
-      v.x = pack_h2(h_lo(v.x) * f, h_hi(v.x) * f);
-      v.y = pack_h2(h_lo(v.y) * f, h_hi(v.y) * f);
-      v.z = pack_h2(h_lo(v.z) * f, h_hi(v.z) * f);
-      v.w = pack_h2(h_lo(v.w) * f, h_hi(v.w) * f);
+  constexpr int PR = NC / 8, NPC = TL * PR / BT, NBAT = NPC < 8 ? NPC : 8;
+  static_assert(NPC % NBAT == 0, "pieces per thread");
+#pragma unroll
+  for (int b0 = 0; b0 < NPC; b0 += NBAT) {
+    u32x4 v[NBAT];
+#pragma unroll
+    for (int u = 0; u < NBAT; ++u) {
+      const int i = threadIdx.x + (b0 + u) * BT, r = i / PR, c8 = i - r * PR;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)min(r, nvalid - 1) * ld + 8 * c8);
+      v[u] = r < nvalid ? x : u32x4{0u, 0u, 0u, 0u};
     }
-    *reinterpret_cast<u32x4*>(dst + r * pitch + 8 * c8) = v;
-  }
-}
-
-// a 64 x 64 block of an fp32 matrix (row length ld) -> fp16 LDS [64][SP],
-// scaled by the power of two 2^-e that puts its largest magnitude in
-// [2^14, 2^15); returns 2^e.  red: 4 floats of LDS.  The whole workgroup
-// calls it (it synchronises once).
-__device__ __forceinline__ float stage_f32(uint16_t* dst, const float* src, int ld, float* red) {
-  constexpr int NP = TL * 16 / BT;
-  f32x4 v[NP];
-  float m = 0.f;
 #pragma unroll
-  for (int u = 0; u < NP; ++u) {
-    const int i = threadIdx.x + u * BT, r = i >> 4, c4 = i & 15;
-    v[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)r * ld + 4 * c4);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
+    for (int u = 0; u < NBAT; ++u) {
+      const int i = threadIdx.x + (b0 + u) * BT, r = i / PR, c8 = i - r * PR;
+      u32x4 x = v[u];
+      if (scale) {
+        const float f = scale[r];
+        x.x = pack_h2(h_lo(x.x) * f, h_hi(x.x) * f);
+        x.y = pack_h2(h_lo(x.y) * f, h_hi(x.y) * f);
+        x.z = pack_h2(h_lo(x.z) * f, h_hi(x.z) * f);
+        x.w = pack_h2(h_lo(x.w) * f, h_hi(x.w) * f);
+      }
+      *reinterpret_cast<u32x4*>(dst + r * pitch + 8 * c8) = x;
+    }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  int ex = 0;
-  if (m > 0.f && m < 3.0e38f) {
-    frexpf(m, &ex);
-    ex = min(max(ex - 15, -120), 120);
-  }
-  const float down = ldexpf(1.f, -ex);
-#pragma unroll
-  for (int u = 0; u < NP; ++u) {
-    const int i = threadIdx.x + u * BT, r = i >> 4, c4 = i & 15;
-    uint2 w;
-    w.x = pack_h2(v[u][0] * down, v[u][1] * down);
-    w.y = pack_h2(v[u][2] * down, v[u][3] * down);
-    *reinterpret_cast<uint2*>(dst + r * SP + 4 * c4) = w;
-  }
-  return ldexpf(1.f, ex);
-}
-
-// NR rows x 64 columns of an fp32 matrix -> fp16 LDS [NR][SP] with one power
-// of two for the whole block (two passes over the source: the largest
-// magnitude, then the scaled copy); returns 2^e.  The whole workgroup calls
-// it (it synchronises once).
-template <int NR>
-__device__ __forceinline__ float stage_f32_rows(uint16_t* dst, const float* src, int ld, float* red) {
-  float m = 0.f;
-  for (int i = threadIdx.x; i < NR * 16; i += BT) {
-    const int r = i >> 4, c4 = i & 15;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (int64_t)r * ld + 4 * c4);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  int ex = 0;
-  if (m > 0.f && m < 3.0e38f) {
-    frexpf(m, &ex);
-    ex = min(max(ex - 15, -120), 120);
-  }
-  const float down = ldexpf(1.f, -ex);
-  for (int i = threadIdx.x; i < NR * 16; i += BT) {
-    const int r = i >> 4, c4 = i & 15;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (int64_t)r * ld + 4 * c4);
-    uint2 w;
-    w.x = pack_h2(v[0] * down, v[1] * down);
-    w.y = pack_h2(v[2] * down, v[3] * down);
-    *reinterpret_cast<uint2*>(dst + r * SP + 4 * c4) = w;
-  }
-  return ldexpf(1.f, ex);
 }
 
 // the positive row scale s_p of a row that has seen n tokens (§三.3, first two factors)
@@ -209,13 +153,12 @@ __device__ __forceinline__ float row_scale(const Decay& dec, unsigned flags, flo
 // a_p and c_p of row p (p < L)
 __device__ __forceinline__ void row_ac(const BwdP& p, const Decay& dec, float qk, int bh, int row, float& a,
                                        float& c) {
-  if (p.flags & RET_NORM_SCORE) {
-    a = p.ra[(int64_t)bh * p.L + row];
-    c = p.rc[(int64_t)bh * p.L + row];
-  } else {
-    a = row_scale(dec, p.flags, qk, row + 1);
-    c = 0.f;
-  }
+  // the loads are unconditional (a select follows) so that the wait counts of
+  // the loads in flight around them stay exact
+  const float la = p.ra[(int64_t)bh * p.L + row], lc = p.rc[(int64_t)bh * p.L + row];
+  const bool sn = (p.flags & RET_NORM_SCORE) != 0;
+  a = sn ? la : row_scale(dec, p.flags, qk, row + 1);
+  c = sn ? lc : 0.f;
 }
 
 template <typename TG> struct Out2;
@@ -310,27 +253,102 @@ __global__ void __launch_bounds__(BT) bwd_prep_kernel(BwdP p, HeadParams hp) {
   }
 }
 
+// ------------------------------------------------------------ slab pipeline
+// Operand slabs of 64 rows x 64 columns move global -> registers -> LDS with
+// one slab in flight: slab i + 1 is loaded into registers while slab i is
+// multiplied, and two LDS buffers alternate by a running slab count, so one
+// barrier per slab separates a buffer's writes from its reads two slabs
+// earlier.
+struct H16 {          // an fp16 slab: 2 x 16 bytes per thread; rows >= nvalid read as zero
+  u32x4 v[2];
+  __device__ __forceinline__ void load(const uint16_t* src, int ld, int nvalid) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = threadIdx.x + u * BT, r = i >> 3, c8 = i & 7;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)min(r, nvalid - 1) * ld + 8 * c8);
+      v[u] = r < nvalid ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst) const {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = threadIdx.x + u * BT, r = i >> 3, c8 = i & 7;
+      *reinterpret_cast<u32x4*>(dst + r * SP + 8 * c8) = v[u];
+    }
+  }
+};
+struct F32 {          // a 64 x 64 slab of an fp32 state: 4 x 16 bytes per thread, scaled to fp16 on store
+  f32x4 v[4];
+  __device__ __forceinline__ void load(const float* src, int ld) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = threadIdx.x + u * BT, r = i >> 4, c4 = i & 15;
+      v[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)r * ld + 4 * c4);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, float down) const {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = threadIdx.x + u * BT, r = i >> 4, c4 = i & 15;
+      uint2 w;
+      w.x = pack_h2(v[u][0] * down, v[u][1] * down);
+      w.y = pack_h2(v[u][2] * down, v[u][3] * down);
+      *reinterpret_cast<uint2*>(dst + r * SP + 4 * c4) = w;
+    }
+  }
+};
+
+// the power of two of one (bh, chunk) state: 2^-e brings its largest
+// magnitude (the maximum of the scan's NM partial maxima) into [2^14, 2^15);
+// returns 2^e
+template <int NM>
+__device__ __forceinline__ float state_up(const float* smax) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < NM; ++i) m = fmaxf(m, smax[i]);
+  int ex = 0;
+  if (m > 0.f && m < 3.0e38f) {
+    frexpf(m, &ex);
+    ex = min(max(ex - 15, -120), 120);
+  }
+  return ldexpf(1.f, ex);
+}
+
 // ------------------------------------------------------------ state scans
 // REV = false: R_c, z_c for every chunk (R <- gamma^(B_c) R + K'^T (zeta V),
 // zeta_m = gamma^(c1-1-m)), walking the chunks forwards.
 // REV = true: U_c, u_c (U <- gamma^(B_c) U + Q'^T (w G), w_p = gamma^(p-c0) a_p,
-// and c_p in place of a_p for u), walking backwards.  The value stored for
-// chunk c is the state before that chunk is folded in.  A workgroup owns rows
-// [64 db, 64 db + 64) and columns [DVB eb, DVB eb + DVB) of the state.
-template <int DK, int DV, int DVB, bool REV>
+// and c_p in place of a_p for u), walking the chunks backwards.  The value
+// stored for chunk c is the state before that chunk is folded in, with the
+// largest magnitude of each wave's part (for the consumers' power of two).
+// A workgroup owns rows [64 db, 64 db + 64) and columns [DVB eb, DVB eb +
+// DVB) of the state; the next two 64-row tiles are in registers while the
+// current one is multiplied.
+template <int DVB>
 struct StateSmem {
-  uint16_t As[TL * SP];            // weighted k' (q') rows [row][d of the block]
-  uint16_t Bs[TL * (DVB + 8)];     // v (dO) rows [row][e of the block]
-  float w[TL];                     // row weights of As
-  float zw[TL];                    // row weights of the key-sum
+  uint16_t As[2][TL * SP];         // weighted k' (q') rows [row][d of the block]
+  uint16_t Bs[2][TL * (DVB + 8)];  // v (dO) rows [row][e of the block]
+  float zr[2][TL];                 // key-sum weight / row weight of As
+  float zred[4][64];               // partial key-sums of the four row quarters
+};
+
+template <int DVB>
+struct TileRegs {                  // one tile in flight: A and B pieces, weights of the A pieces
+  static constexpr int BPC = TL * DVB / 8 / BT;
+  H16 a;
+  u32x4 b[BPC];
+  float aw[2], az[2];
 };
 
 template <int DK, int DV, int DVB, bool REV>
 __global__ void __launch_bounds__(BT) bwd_state_kernel(BwdP p, HeadParams hp) {
-  typedef StateSmem<DK, DV, DVB, REV> SM;
-  __shared__ SM sm;
+  typedef StateSmem<DVB> SM;
+  typedef TileRegs<DVB> TR;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
   constexpr int NDB = DK / 64, NEB = DV / DVB, NB = DVB / 64;   // NB column blocks of 32 per wave
   constexpr int BP = DVB + 8;
+  constexpr int BPC = TR::BPC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bi = wave >> 1, bj = wave & 1;
   const int eb = blockIdx.x % NEB;
@@ -344,18 +362,72 @@ __global__ void __launch_bounds__(BT) bwd_state_kernel(BwdP p, HeadParams hp) {
   const uint16_t* Y = (REV ? p.Gb : p.Vb) + (int64_t)bh * p.L * DV + DVB * eb;
   float* dst = (REV ? p.Ust : p.Rin) + (int64_t)bh * p.nc * DK * DV;
   float* zdst = (REV ? p.ust : p.zin) + (int64_t)bh * p.nc * DK;
+  float* mdst = (REV ? p.umax : p.rmax) + (int64_t)bh * p.nc * (NDB * NEB * 4) + (db * NEB + eb) * 4;
+
+  // tile t of the walk -> (chunk, first row)
+  const int tpc = p.B / TL;
+  const int tl = p.nt - (p.nc - 1) * tpc;           // tiles of the last chunk
+  auto tile_of = [&](int t, int& c, int& m0) {
+    int tile;
+    if (!REV) {
+      tile = t;
+      c = t / tpc;
+    } else if (t < tl) {
+      c = p.nc - 1;
+      tile = c * tpc + t;
+    } else {
+      const int u = t - tl;
+      c = p.nc - 2 - u / tpc;
+      tile = c * tpc + u % tpc;
+    }
+    m0 = tile * TL;
+  };
+
+  auto load_tile = [&](int t, TR& g) {
+    t = min(t, p.nt - 1);               // past the end: reload the last tile (every step issues the same loads)
+    int c, m0;
+    tile_of(t, c, m0);
+    const int c0 = c * p.B, c1 = min(c0 + p.B, p.L), nv = min(TL, c1 - m0);
+    g.a.load(X + (int64_t)m0 * DK, DK, nv);
+#pragma unroll
+    for (int u = 0; u < BPC; ++u) {
+      const int i = tid + u * BT, r = i / (DVB / 8), c8 = i % (DVB / 8);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(Y + (int64_t)(m0 + min(r, nv - 1)) * DV + 8 * c8);
+      g.b[u] = r < nv ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = (tid + u * BT) >> 3, row = m0 + min(r, nv - 1);
+      float w, z;
+      if (REV) {
+        float a, cc;
+        row_ac(p, dec, qk, bh, row, a, cc);
+        w = dec.pow((float)(row - c0)) * a;
+        z = a > 0.f ? cc / a : 0.f;
+      } else {
+        w = dec.pow((float)(c1 - 1 - row));
+        z = 1.f;
+      }
+      g.aw[u] = r < nv ? w : 0.f;
+      g.az[u] = r < nv ? z : 0.f;
+    }
+  };
 
   f32x16 acc[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) acc[n] = f32x16{};
-  float zreg = 0.f;                         // z / u at d = 64 db + tid (tid < 64, eb == 0)
+  // partial key-sum of d = 64 db + (tid & 63) over rows 16 (tid / 64) .. + 15 of each tile (eb == 0)
+  float zpart = 0.f;
+  const int zd = tid & 63, zq = tid >> 6;
 
-  for (int step = 0; step < p.nc; ++step) {
-    const int c = REV ? p.nc - 1 - step : step;
-    const int c0 = c * p.B, Bc = min(p.B, p.L - c0), c1 = c0 + Bc;
-    // store the state entering chunk c
-    {
+  auto body = [&](int t, TR& g) {
+    int c, m0;
+    tile_of(t, c, m0);
+    const int c0 = c * p.B, c1 = min(c0 + p.B, p.L), nv = min(TL, c1 - m0);
+    if (m0 == c0) {
+      // the state entering chunk c, then its decay over the chunk
       float* Sd = dst + (int64_t)c * DK * DV;
+      float m = 0.f;
 #pragma unroll
       for (int n = 0; n < NB; ++n)
 #pragma unroll
@@ -363,46 +435,58 @@ __global__ void __launch_bounds__(BT) bwd_state_kernel(BwdP p, HeadParams hp) {
           const int d = 64 * db + 32 * bi + acc_row(r, lane);
           const int e = DVB * eb + 64 * n + 32 * bj + (lane & 31);
           Sd[(int64_t)d * DV + e] = acc[n][r];
+          m = fmaxf(m, fabsf(acc[n][r]));
         }
-      if (eb == 0 && tid < 64) zdst[(int64_t)c * DK + 64 * db + tid] = zreg;
-    }
-    const float gB = dec.pow((float)Bc);
 #pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] *= gB;
-    zreg *= gB;
-    for (int m0 = c0; m0 < c1; m0 += TL) {
-      const int nv = min(TL, c1 - m0);
-      __syncthreads();
-      if (tid < TL) {
-        const int row = m0 + tid;
-        float w = 0.f, zw = 0.f;
-        if (tid < nv) {
-          if (REV) {
-            float a, cc;
-            row_ac(p, dec, qk, bh, row, a, cc);
-            const float gp = dec.pow((float)(row - c0));
-            w = gp * a;
-            zw = gp * cc;
-          } else {
-            w = dec.pow((float)(c1 - 1 - row));
-            zw = w;
-          }
-        }
-        sm.w[tid] = w;
-        sm.zw[tid] = zw;
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      if (lane == 0) mdst[(int64_t)c * (NDB * NEB * 4) + wave] = m;
+      const float gB = dec.pow((float)(c1 - c0));
+      if (eb == 0) {
+        sm.zred[zq][zd] = zpart;
+        __syncthreads();
+        if (tid < 64)
+          zdst[(int64_t)c * DK + 64 * db + tid] = sm.zred[0][tid] + sm.zred[1][tid] + sm.zred[2][tid] + sm.zred[3][tid];
+        zpart *= gB;
       }
-      __syncthreads();
-      stage<64>(sm.As, SP, X + (int64_t)m0 * DK, DK, nv, sm.w);
-      stage<DVB>(sm.Bs, BP, Y + (int64_t)m0 * DV, DV, nv, nullptr);
-      __syncthreads();
-      if (eb == 0 && tid < 64) {
-        const uint16_t* xp = X + (int64_t)m0 * DK + tid;
-        for (int i = 0; i < nv; ++i) zreg += sm.zw[i] * h2f(xp[(int64_t)i * DK]);
-      }
-      // acc[d][e] += sum_row As[row][d] Bs[row][e]: both operands read transposed
 #pragma unroll
-      for (int n = 0; n < NB; ++n) mm64<true, true>(acc[n], sm.As, SP, 32 * bi, sm.Bs, BP, 64 * n + 32 * bj, lane);
+      for (int n = 0; n < NB; ++n) acc[n] *= gB;
     }
+    const int buf = t & 1;
+    // registers -> LDS (A rows weighted)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + u * BT, r = i >> 3, c8 = i & 7;
+      const float w = g.aw[u];
+      u32x4 x = g.a.v[u];
+      x.x = pack_h2(h_lo(x.x) * w, h_hi(x.x) * w);
+      x.y = pack_h2(h_lo(x.y) * w, h_hi(x.y) * w);
+      x.z = pack_h2(h_lo(x.z) * w, h_hi(x.z) * w);
+      x.w = pack_h2(h_lo(x.w) * w, h_hi(x.w) * w);
+      *reinterpret_cast<u32x4*>(sm.As[buf] + r * SP + 8 * c8) = x;
+      if (c8 == 0) sm.zr[buf][r] = g.az[u];
+    }
+#pragma unroll
+    for (int u = 0; u < BPC; ++u) {
+      const int i = tid + u * BT, r = i / (DVB / 8), c8 = i % (DVB / 8);
+      *reinterpret_cast<u32x4*>(sm.Bs[buf] + r * BP + 8 * c8) = g.b[u];
+    }
+    __syncthreads();
+    load_tile(t + 2, g);
+    if (eb == 0)
+      for (int i = 16 * zq; i < min(16 * zq + 16, nv); ++i)
+        zpart += h2f(sm.As[buf][i * SP + zd]) * sm.zr[buf][i];
+    // acc[d][e] += sum_row As[row][d] Bs[row][e]: both operands read transposed
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      mm64<true, true>(acc[n], sm.As[buf], SP, 32 * bi, sm.Bs[buf], BP, 64 * n + 32 * bj, lane);
+  };
+
+  TR g0, g1;
+  load_tile(0, g0);
+  load_tile(1, g1);
+  for (int t = 0; t < p.nt; t += 2) {
+    body(t, g0);
+    if (t + 1 < p.nt) body(t + 1, g1);
   }
 }
 
@@ -412,10 +496,9 @@ template <int DK, int DV>
 struct StatsSmem {
   uint16_t Qs[TL * (DK + 8)];
   uint16_t Gs[TL * (DV + 8)];
-  uint16_t Sl[TL * SP];
+  uint16_t Sl[2][TL * SP];
   float red[2][2][TL];             // [den / gnum][column half][row]
   float qz[TL];                    // q'_p . z_c
-  float mx[4];
 };
 
 template <int DK, int DV>
@@ -423,7 +506,8 @@ __global__ void __launch_bounds__(BT) bwd_stats_kernel(BwdP p, HeadParams hp) {
   typedef StatsSmem<DK, DV> SM;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  constexpr int QP = DK + 8, GP = DV + 8;
+  constexpr int QP = DK + 8, GP = DV + 8, ND = DK / 64, NE = DV / 64;
+  constexpr int NM = (DK / 64) * (DV / (DV < 256 ? DV : 256)) * 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
   const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
@@ -443,52 +527,35 @@ __global__ void __launch_bounds__(BT) bwd_stats_kernel(BwdP p, HeadParams hp) {
   float dsum[16], gsum[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) dsum[r] = gsum[r] = 0.f;
+  int sc = 0;
 
-  // intra-chunk key tiles up to the diagonal
-  for (int m0 = c0; m0 <= r0; m0 += TL) {
-    const int nk = min(TL, p.L - m0);
-    f32x16 S = {}, T = {};
-    for (int ds = 0; ds < DK / 64; ++ds) {
-      __syncthreads();
-      stage<64>(sm.Sl, SP, Kr + (int64_t)m0 * DK + 64 * ds, DK, nk, nullptr);
-      __syncthreads();
-      mm64<false, false>(S, sm.Qs + 64 * ds, QP, 32 * bi, sm.Sl, SP, 32 * bj, lane);
-    }
-    for (int es = 0; es < DV / 64; ++es) {
-      __syncthreads();
-      stage<64>(sm.Sl, SP, Vb + (int64_t)m0 * DV + 64 * es, DV, nk, nullptr);
-      __syncthreads();
-      mm64<false, false>(T, sm.Gs + 64 * es, GP, 32 * bi, sm.Sl, SP, 32 * bj, lane);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = r0 + 32 * bi + acc_row(r, lane), col = m0 + 32 * bj + l32;
-      const bool ok = col <= row && col < p.L && row < p.L;
-      const float A = ok ? S[r] * dec.pow((float)(row - col)) : 0.f;
-      dsum[r] += A;
-      gsum[r] += A * T[r];
-    }
-  }
-  // cross part of g . num: xi_p (q'_p R_c) . g_p, column block by column block
+  // cross part of g . num: xi_p (q'_p R_c) . g_p, one 64-column block of R at a time
   if (c > 0) {
     const float* R = p.Rin + ((int64_t)bh * p.nc + c) * DK * DV;
-    for (int es = 0; es < DV / 64; ++es) {
+    const float up = state_up<NM>(p.rmax + ((int64_t)bh * p.nc + c) * NM), down = 1.f / up;
+    F32 fr[2];
+    fr[0].load(R, DV);
+    if (NE * ND > 1) fr[1].load(R + (int64_t)(64 * (1 % ND)) * DV + 64 * (1 / ND), DV);
+#pragma unroll
+    for (int es = 0; es < NE; ++es) {
       f32x16 X = {};
-      for (int ds = 0; ds < DK / 64; ++ds) {
+#pragma unroll
+      for (int ds = 0; ds < ND; ++ds) {
+        const int i = es * ND + ds;
+        uint16_t* b = sm.Sl[sc++ & 1];
+        fr[i & 1].store(b, down);
         __syncthreads();
-        const float up = stage_f32(sm.Sl, R + (int64_t)(64 * ds) * DV + 64 * es, DV, sm.mx);
-        __syncthreads();
+        const int nx = i + 2;
+        if (nx < NE * ND) fr[i & 1].load(R + (int64_t)(64 * (nx % ND)) * DV + 64 * (nx / ND), DV);
         // X[p][e] += sum_d Q'[p][d] R[d][e]; R staged [d][e] (k = d): transposed B
-        f32x16 t = {};
-        mm64<false, true>(t, sm.Qs + 64 * ds, QP, 32 * bi, sm.Sl, SP, 32 * bj, lane);
-        X += up * t;
+        mm64<false, true>(X, sm.Qs + 64 * ds, QP, 32 * bi, b, SP, 32 * bj, lane);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int pl = 32 * bi + acc_row(r, lane);
         const float xi = dec.pow((float)(r0 + pl - c0 + 1));
         const float gv = h2f(sm.Gs[pl * GP + 64 * es + 32 * bj + l32]);
-        gsum[r] += xi * X[r] * gv;
+        gsum[r] += xi * up * X[r] * gv;
       }
     }
     // q'_p . z_c: 4 threads per row
@@ -501,6 +568,47 @@ __global__ void __launch_bounds__(BT) bwd_stats_kernel(BwdP p, HeadParams hp) {
     if (part == 0) sm.qz[row] = acc * dec.pow((float)(r0 + row - c0 + 1));
   } else if (tid < TL) {
     sm.qz[tid] = 0.f;
+  }
+
+  // intra-chunk key tiles up to the diagonal: K' slabs, then V slabs (an even
+  // number per tile, so a slab's register set is fixed by its place in the tile)
+  constexpr int PT = ND + NE;
+  const int nsl = ((r0 - c0) / TL + 1) * PT;
+  auto src = [&](int i, H16& r) {
+    i = min(i, nsl - 1);            // past the end: reload the last slab (every step issues the same loads)
+    const int j = i / PT, w = i - j * PT, m0 = c0 + TL * j, nk = min(TL, p.L - m0);
+    if (w < ND) r.load(Kr + (int64_t)m0 * DK + 64 * w, DK, nk);
+    else r.load(Vb + (int64_t)m0 * DV + 64 * (w - ND), DV, nk);
+  };
+  H16 hr[2];
+  src(0, hr[0]);
+  src(1, hr[1]);
+  for (int m0 = c0, i0 = 0; m0 <= r0; m0 += TL, i0 += PT) {
+    f32x16 S = {}, T = {};
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds) {
+      uint16_t* b = sm.Sl[sc++ & 1];
+      hr[ds & 1].store(b);
+      __syncthreads();
+      src(i0 + ds + 2, hr[ds & 1]);
+      mm64<false, false>(S, sm.Qs + 64 * ds, QP, 32 * bi, b, SP, 32 * bj, lane);
+    }
+#pragma unroll
+    for (int es = 0; es < NE; ++es) {
+      uint16_t* b = sm.Sl[sc++ & 1];
+      hr[(ND + es) & 1].store(b);
+      __syncthreads();
+      src(i0 + ND + es + 2, hr[(ND + es) & 1]);
+      mm64<false, false>(T, sm.Gs + 64 * es, GP, 32 * bi, b, SP, 32 * bj, lane);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = r0 + 32 * bi + acc_row(r, lane), col = m0 + 32 * bj + l32;
+      const bool ok = col <= row && col < p.L && row < p.L;
+      const float A = ok ? S[r] * dec.pow((float)(row - col)) : 0.f;
+      dsum[r] += A;
+      gsum[r] += A * T[r];
+    }
   }
   // row sums over the 32 columns of each half-wave, then over the two column blocks
 #pragma unroll
@@ -564,12 +672,11 @@ struct DqSmem {
     struct {
       uint16_t Gs[TL * (DV + 8)];
       uint16_t Es[TL * SP];
-      uint16_t Sl[TL * SP];
+      uint16_t Sl[2][TL * SP];
     } w;
     float out[TL * (DK + 4)];
   } u;
   float ra[TL], rc[TL], xi[TL];
-  float mx[4];
 };
 
 template <typename TG, int DK, int DV>
@@ -577,7 +684,8 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
   typedef DqSmem<DK, DV> SM;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  constexpr int GP = DV + 8, ND = DK / 64;
+  constexpr int GP = DV + 8, ND = DK / 64, NE = DV / 64;
+  constexpr int NM = (DK / 64) * (DV / (DV < 256 ? DV : 256)) * 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
   const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
@@ -591,32 +699,55 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
   const uint16_t* Vb = p.Vb + (int64_t)bh * p.L * DV;
   const uint16_t* Gb = p.Gb + (int64_t)bh * p.L * DV;
 
-  if (tid < TL) {
-    float a = 0.f, cc = 0.f;
-    if (tid < nq) row_ac(p, dec, qk, bh, r0 + tid, a, cc);
-    sm.ra[tid] = a;
-    sm.rc[tid] = cc;
-    sm.xi[tid] = dec.pow((float)(r0 + tid - c0 + 1));
+  {
+    float a, cc;
+    row_ac(p, dec, qk, bh, r0 + min(tid & 63, nq - 1), a, cc);
+    if (tid < TL) {
+      sm.ra[tid] = tid < nq ? a : 0.f;
+      sm.rc[tid] = tid < nq ? cc : 0.f;
+      sm.xi[tid] = dec.pow((float)(r0 + tid - c0 + 1));
+    }
   }
   stage<DV>(sm.u.w.Gs, GP, Gb + (int64_t)r0 * DV, DV, nq, nullptr);
   f32x16 acc[ND];
 #pragma unroll
   for (int n = 0; n < ND; ++n) acc[n] = f32x16{};
+  int sc = 0;
+  // the intra-chunk slab stream (per key tile: V slabs, then K' slabs; an even
+  // number, so a slab's register set is fixed by its place in the tile); its
+  // first two slabs are requested now
+  constexpr int PT = NE + ND;
+  const int nsl = ((r0 - c0) / TL + 1) * PT;
+  auto src = [&](int i, H16& r) {
+    i = min(i, nsl - 1);            // past the end: reload the last slab (every step issues the same loads)
+    const int j = i / PT, w = i - j * PT, m0 = c0 + TL * j, nk = min(TL, p.L - m0);
+    if (w < NE) r.load(Vb + (int64_t)m0 * DV + 64 * w, DV, nk);
+    else r.load(Kr + (int64_t)m0 * DK + 64 * (w - NE), DK, nk);
+  };
+  H16 hr[2];
+  src(0, hr[0]);
+  src(1, hr[1]);
 
   // cross: xi_p (a_p (G R_c^T)_pd + c_p z_c[d])
   if (c > 0) {
     const float* R = p.Rin + ((int64_t)bh * p.nc + c) * DK * DV;
     const float* z = p.zin + ((int64_t)bh * p.nc + c) * DK;
+    const float up = state_up<NM>(p.rmax + ((int64_t)bh * p.nc + c) * NM), down = 1.f / up;
+    F32 fr[2];
+    fr[0].load(R, DV);
+    if (ND * NE > 1) fr[1].load(R + (int64_t)(64 * (1 / NE)) * DV + 64 * (1 % NE), DV);
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds)
-      for (int es = 0; es < DV / 64; ++es) {
+#pragma unroll
+      for (int es = 0; es < NE; ++es) {
+        const int i = ds * NE + es;
+        uint16_t* b = sm.u.w.Sl[sc++ & 1];
+        fr[i & 1].store(b, down);
         __syncthreads();
-        const float up = stage_f32(sm.u.w.Sl, R + (int64_t)(64 * ds) * DV + 64 * es, DV, sm.mx);
-        __syncthreads();
+        const int nx = i + 2;
+        if (nx < ND * NE) fr[i & 1].load(R + (int64_t)(64 * (nx / NE)) * DV + 64 * (nx % NE), DV);
         // B[n = d][k = e] = R[d][e], staged [d][e]: "nt"
-        f32x16 t = {};
-        mm64<false, false>(t, sm.u.w.Gs + 64 * es, GP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
-        acc[ds] += up * t;
+        mm64<false, false>(acc[ds], sm.u.w.Gs + 64 * es, GP, 32 * bi, b, SP, 32 * bj, lane);
       }
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds) {
@@ -624,19 +755,20 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int pl = 32 * bi + acc_row(r, lane);
-        acc[ds][r] = sm.xi[pl] * (sm.ra[pl] * acc[ds][r] + sm.rc[pl] * zd);
+        acc[ds][r] = sm.xi[pl] * (sm.ra[pl] * up * acc[ds][r] + sm.rc[pl] * zd);
       }
     }
   }
-  // intra-chunk key tiles up to the diagonal
-  for (int m0 = c0; m0 <= r0; m0 += TL) {
-    const int nk = min(TL, p.L - m0);
+  // intra-chunk key tiles up to the diagonal: V slabs (T = G V^T), E, then K' slabs
+  for (int m0 = c0, i0 = 0; m0 <= r0; m0 += TL, i0 += PT) {
     f32x16 T = {};
-    for (int es = 0; es < DV / 64; ++es) {
+#pragma unroll
+    for (int es = 0; es < NE; ++es) {
+      uint16_t* b = sm.u.w.Sl[sc++ & 1];
+      hr[es & 1].store(b);
       __syncthreads();
-      stage<64>(sm.u.w.Sl, SP, Vb + (int64_t)m0 * DV + 64 * es, DV, nk, nullptr);
-      __syncthreads();
-      mm64<false, false>(T, sm.u.w.Gs + 64 * es, GP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
+      src(i0 + es + 2, hr[es & 1]);
+      mm64<false, false>(T, sm.u.w.Gs + 64 * es, GP, 32 * bi, b, SP, 32 * bj, lane);
     }
     // E[p][m] -> LDS (row p, column m)
 #pragma unroll
@@ -649,11 +781,12 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
     }
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds) {
+      uint16_t* b = sm.u.w.Sl[sc++ & 1];
+      hr[(NE + ds) & 1].store(b);
       __syncthreads();
-      stage<64>(sm.u.w.Sl, SP, Kr + (int64_t)m0 * DK + 64 * ds, DK, nk, nullptr);
-      __syncthreads();
+      src(i0 + NE + ds + 2, hr[(NE + ds) & 1]);
       // dq'[p][d] += sum_m E[p][m] K'[m][d]; K' staged [m][d] (k = m): transposed B
-      mm64<false, true>(acc[ds], sm.u.w.Es, SP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
+      mm64<false, true>(acc[ds], sm.u.w.Es, SP, 32 * bi, b, SP, 32 * bj, lane);
     }
   }
   __syncthreads();
@@ -673,12 +806,11 @@ struct DkSmem {
     struct {
       uint16_t Vs[TL * (DV + 8)];
       uint16_t Es[TL * SP];        // E^T [m][p]
-      uint16_t Sl[TL * SP];
+      uint16_t Sl[2][TL * SP];
     } w;
     float out[TL * (DK + 4)];
   } u;
   float pa[TL], pc[TL];
-  float mx[4];
 };
 
 template <typename TG, int DK, int DV>
@@ -686,7 +818,8 @@ __global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
   typedef DkSmem<DK, DV> SM;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  constexpr int VP = DV + 8, ND = DK / 64;
+  constexpr int VP = DV + 8, ND = DK / 64, NE = DV / 64;
+  constexpr int NM = (DK / 64) * (DV / (DV < 256 ? DV : 256)) * 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
   const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
@@ -704,20 +837,39 @@ __global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
   f32x16 acc[ND];
 #pragma unroll
   for (int n = 0; n < ND; ++n) acc[n] = f32x16{};
+  int sc = 0;
+  // the intra-chunk slab stream (per query tile: dO slabs, then Q' slabs)
+  constexpr int PT = NE + ND;
+  const int nsl = ((c1 - m0 + TL - 1) / TL) * PT;
+  auto src = [&](int i, H16& r) {
+    i = min(i, nsl - 1);            // past the end: reload the last slab (every step issues the same loads)
+    const int j = i / PT, w = i - j * PT, q0 = m0 + TL * j, nq = min(TL, p.L - q0);
+    if (w < NE) r.load(Gb + (int64_t)q0 * DV + 64 * w, DV, nq);
+    else r.load(Qr + (int64_t)q0 * DK + 64 * (w - NE), DK, nq);
+  };
+  H16 hr[2];
+  src(0, hr[0]);
+  src(1, hr[1]);
 
   // cross: gamma^(c1-m) ((V U_c^T)[m][d] + u_c[d])
   if (c + 1 < p.nc) {
     const float* U = p.Ust + ((int64_t)bh * p.nc + c) * DK * DV;
     const float* u = p.ust + ((int64_t)bh * p.nc + c) * DK;
+    const float up = state_up<NM>(p.umax + ((int64_t)bh * p.nc + c) * NM), down = 1.f / up;
+    F32 fr[2];
+    fr[0].load(U, DV);
+    if (ND * NE > 1) fr[1].load(U + (int64_t)(64 * (1 / NE)) * DV + 64 * (1 % NE), DV);
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds)
-      for (int es = 0; es < DV / 64; ++es) {
+#pragma unroll
+      for (int es = 0; es < NE; ++es) {
+        const int i = ds * NE + es;
+        uint16_t* b = sm.u.w.Sl[sc++ & 1];
+        fr[i & 1].store(b, down);
         __syncthreads();
-        const float up = stage_f32(sm.u.w.Sl, U + (int64_t)(64 * ds) * DV + 64 * es, DV, sm.mx);
-        __syncthreads();
-        f32x16 t = {};
-        mm64<false, false>(t, sm.u.w.Vs + 64 * es, VP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
-        acc[ds] += up * t;
+        const int nx = i + 2;
+        if (nx < ND * NE) fr[i & 1].load(U + (int64_t)(64 * (nx / NE)) * DV + 64 * (nx % NE), DV);
+        mm64<false, false>(acc[ds], sm.u.w.Vs + 64 * es, VP, 32 * bi, b, SP, 32 * bj, lane);
       }
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds) {
@@ -725,27 +877,30 @@ __global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + 32 * bi + acc_row(r, lane);
-        acc[ds][r] = dec.pow((float)(c1 - row)) * (acc[ds][r] + ud);
+        acc[ds][r] = dec.pow((float)(c1 - row)) * (up * acc[ds][r] + ud);
       }
     }
   }
-  // intra-chunk query tiles from the diagonal to the chunk end
-  for (int q0 = m0; q0 < c1; q0 += TL) {
+  // intra-chunk query tiles from the diagonal to the chunk end: dO slabs (T^T = V dO^T), E^T, then Q' slabs
+  for (int q0 = m0, i0 = 0; q0 < c1; q0 += TL, i0 += PT) {
     const int nq = min(TL, p.L - q0);
-    __syncthreads();
-    if (tid < TL) {
-      float a = 0.f, cc = 0.f;
-      if (tid < nq) row_ac(p, dec, qk, bh, q0 + tid, a, cc);
-      sm.pa[tid] = a;
-      sm.pc[tid] = cc;
+    {
+      float a, cc;
+      row_ac(p, dec, qk, bh, q0 + min(tid & 63, nq - 1), a, cc);
+      if (tid < TL) {
+        sm.pa[tid] = tid < nq ? a : 0.f;
+        sm.pc[tid] = tid < nq ? cc : 0.f;
+      }
     }
     f32x16 T = {};
-    for (int es = 0; es < DV / 64; ++es) {
+#pragma unroll
+    for (int es = 0; es < NE; ++es) {
+      uint16_t* b = sm.u.w.Sl[sc++ & 1];
+      hr[es & 1].store(b);
       __syncthreads();
-      stage<64>(sm.u.w.Sl, SP, Gb + (int64_t)q0 * DV + 64 * es, DV, nq, nullptr);
-      __syncthreads();
+      src(i0 + es + 2, hr[es & 1]);
       // T^T[m][p] = sum_e V[m][e] G[p][e]
-      mm64<false, false>(T, sm.u.w.Vs + 64 * es, VP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
+      mm64<false, false>(T, sm.u.w.Vs + 64 * es, VP, 32 * bi, b, SP, 32 * bj, lane);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -757,11 +912,12 @@ __global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
     }
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds) {
+      uint16_t* b = sm.u.w.Sl[sc++ & 1];
+      hr[(NE + ds) & 1].store(b);
       __syncthreads();
-      stage<64>(sm.u.w.Sl, SP, Qr + (int64_t)q0 * DK + 64 * ds, DK, nq, nullptr);
-      __syncthreads();
+      src(i0 + NE + ds + 2, hr[(NE + ds) & 1]);
       // dk'[m][d] += sum_p E^T[m][p] Q'[p][d]; Q' staged [p][d] (k = p): transposed B
-      mm64<false, true>(acc[ds], sm.u.w.Es, SP, 32 * bi, sm.u.w.Sl, SP, 32 * bj, lane);
+      mm64<false, true>(acc[ds], sm.u.w.Es, SP, 32 * bi, b, SP, 32 * bj, lane);
     }
   }
   __syncthreads();
@@ -779,10 +935,8 @@ template <int DK, int DV>
 struct DvSmem {
   uint16_t Ks[TL * (DK + 8)];
   uint16_t As[TL * SP];            // a_p A^T [m][p]
-  uint16_t Sl[TL * SP];
-  uint16_t Ub[DK * SP];            // one 64-column block of U_c, all d rows
+  uint16_t Sl[2][TL * SP];
   float pa[TL];
-  float mx[4];
 };
 
 template <typename TG, int DK, int DV>
@@ -790,7 +944,8 @@ __global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
   typedef DvSmem<DK, DV> SM;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  constexpr int KP = DK + 8, NE = DV / 64;
+  constexpr int KP = DK + 8, ND = DK / 64, NE = DV / 64;
+  constexpr int NM = (DK / 64) * (DV / (DV < 256 ? DV : 256)) * 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
   const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
@@ -808,43 +963,64 @@ __global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
   f32x16 acc[NE];
 #pragma unroll
   for (int n = 0; n < NE; ++n) acc[n] = f32x16{};
+  int sc = 0;
+  // the intra-chunk slab stream (per query tile: Q' slabs, then dO slabs)
+  constexpr int PT = ND + NE;
+  const int nsl = ((c1 - m0 + TL - 1) / TL) * PT;
+  auto src = [&](int i, H16& r) {
+    i = min(i, nsl - 1);            // past the end: reload the last slab (every step issues the same loads)
+    const int j = i / PT, w = i - j * PT, q0 = m0 + TL * j, nq = min(TL, p.L - q0);
+    if (w < ND) r.load(Qr + (int64_t)q0 * DK + 64 * w, DK, nq);
+    else r.load(Gb + (int64_t)q0 * DV + 64 * (w - ND), DV, nq);
+  };
+  H16 hr[2];
+  src(0, hr[0]);
+  src(1, hr[1]);
 
   // cross: gamma^(c1-m) (K' U_c)[m][e]
   if (c + 1 < p.nc) {
     const float* U = p.Ust + ((int64_t)bh * p.nc + c) * DK * DV;
+    const float up = state_up<NM>(p.umax + ((int64_t)bh * p.nc + c) * NM), down = 1.f / up;
+    F32 fr[2];
+    fr[0].load(U, DV);
+    if (ND * NE > 1) fr[1].load(U + (int64_t)(64 * (1 % ND)) * DV + 64 * (1 / ND), DV);
 #pragma unroll
-    for (int es = 0; es < NE; ++es) {
-      __syncthreads();
-      const float up = stage_f32_rows<DK>(sm.Ub, U + 64 * es, DV, sm.mx);
-      __syncthreads();
-      // B[n = e][k = d] = U[d][e], staged [d][e]: transposed B; acc[es] starts at zero
+    for (int es = 0; es < NE; ++es)
 #pragma unroll
-      for (int ds = 0; ds < DK / 64; ++ds)
-        mm64<false, true>(acc[es], sm.Ks + 64 * ds, KP, 32 * bi, sm.Ub + 64 * ds * SP, SP, 32 * bj, lane);
-      acc[es] *= up;
-    }
+      for (int ds = 0; ds < ND; ++ds) {
+        const int i = es * ND + ds;
+        uint16_t* b = sm.Sl[sc++ & 1];
+        fr[i & 1].store(b, down);
+        __syncthreads();
+        const int nx = i + 2;
+        if (nx < ND * NE) fr[i & 1].load(U + (int64_t)(64 * (nx % ND)) * DV + 64 * (nx / ND), DV);
+        // B[n = e][k = d] = U[d][e], staged [d][e]: transposed B
+        mm64<false, true>(acc[es], sm.Ks + 64 * ds, KP, 32 * bi, b, SP, 32 * bj, lane);
+      }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float f = dec.pow((float)(c1 - (m0 + 32 * bi + acc_row(r, lane))));
+      const float f = up * dec.pow((float)(c1 - (m0 + 32 * bi + acc_row(r, lane))));
 #pragma unroll
       for (int es = 0; es < NE; ++es) acc[es][r] *= f;
     }
   }
-  for (int q0 = m0; q0 < c1; q0 += TL) {
+  // intra-chunk query tiles from the diagonal to the chunk end: Q' slabs (S^T = K' Q'^T), a A^T, then dO slabs
+  for (int q0 = m0, i0 = 0; q0 < c1; q0 += TL, i0 += PT) {
     const int nq = min(TL, p.L - q0);
-    __syncthreads();
-    if (tid < TL) {
-      float a = 0.f, cc = 0.f;
-      if (tid < nq) row_ac(p, dec, qk, bh, q0 + tid, a, cc);
-      sm.pa[tid] = a;
+    {
+      float a, cc;
+      row_ac(p, dec, qk, bh, q0 + min(tid & 63, nq - 1), a, cc);
+      if (tid < TL) sm.pa[tid] = tid < nq ? a : 0.f;
     }
     f32x16 S = {};
-    for (int ds = 0; ds < DK / 64; ++ds) {
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds) {
+      uint16_t* b = sm.Sl[sc++ & 1];
+      hr[ds & 1].store(b);
       __syncthreads();
-      stage<64>(sm.Sl, SP, Qr + (int64_t)q0 * DK + 64 * ds, DK, nq, nullptr);
-      __syncthreads();
+      src(i0 + ds + 2, hr[ds & 1]);
       // S^T[m][p] = sum_d K'[m][d] Q'[p][d]
-      mm64<false, false>(S, sm.Ks + 64 * ds, KP, 32 * bi, sm.Sl, SP, 32 * bj, lane);
+      mm64<false, false>(S, sm.Ks + 64 * ds, KP, 32 * bi, b, SP, 32 * bj, lane);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -856,11 +1032,12 @@ __global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
     }
 #pragma unroll
     for (int es = 0; es < NE; ++es) {
+      uint16_t* b = sm.Sl[sc++ & 1];
+      hr[(ND + es) & 1].store(b);
       __syncthreads();
-      stage<64>(sm.Sl, SP, Gb + (int64_t)q0 * DV + 64 * es, DV, nq, nullptr);
-      __syncthreads();
+      src(i0 + ND + es + 2, hr[(ND + es) & 1]);
       // dv[m][e] += sum_p (a A^T)[m][p] G[p][e]; G staged [p][e] (k = p): transposed B
-      mm64<false, true>(acc[es], sm.As, SP, 32 * bi, sm.Sl, SP, 32 * bj, lane);
+      mm64<false, true>(acc[es], sm.As, SP, 32 * bi, b, SP, 32 * bj, lane);
     }
   }
   TG* o = reinterpret_cast<TG*>(p.dv) + bb * p.sdv.b + head * p.sdv.h;
@@ -878,7 +1055,7 @@ __global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-  size_t qr, kr, vb, gb, rin, zin, ust, us, ra, rc, tmax, gsc, total;
+  size_t qr, kr, vb, gb, rin, zin, ust, us, ra, rc, tmax, gsc, rmax, umax, total;
 };
 
 Carve carve_bwd(int b, int h, int L, int dk, int dv, int B) {
@@ -897,6 +1074,9 @@ Carve carve_bwd(int b, int h, int L, int dk, int dv, int B) {
   c.rc = o; o += al256(bh * L * 4);
   c.tmax = o; o += al256(bh * (size_t)((L + TL - 1) / TL) * 4);
   c.gsc = o; o += al256(bh * 4);
+  const size_t nm = (size_t)(dk / 64) * (dv / (dv < 256 ? dv : 256)) * 4;
+  c.rmax = o; o += al256(bh * nc * nm * 4);
+  c.umax = o; o += al256(bh * nc * nm * 4);
   c.total = o;
   return c;
 }
@@ -930,6 +1110,8 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t st) {
   p.rc = reinterpret_cast<float*>(w + cv.rc);
   p.tmax = reinterpret_cast<float*>(w + cv.tmax);
   p.gsc = reinterpret_cast<float*>(w + cv.gsc);
+  p.rmax = reinterpret_cast<float*>(w + cv.rmax);
+  p.umax = reinterpret_cast<float*>(w + cv.umax);
   const int bh = a.b * a.h;
   const HeadParams& hp = *a.hp;
   constexpr int DVB = DV < 256 ? DV : 256;
@@ -939,16 +1121,24 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_prep_kernel<T, DK, DV>), tiles, blk, 0, st, p, hp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_state_kernel<DK, DV, DVB, false>), sgrid, blk, 0, st, p, hp);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    auto k = bwd_state_kernel<DK, DV, DVB, false>;
+    if ((e = set_smem(k, sizeof(StateSmem<DVB>))) != hipSuccess) return e;
+    hipLaunchKernelGGL(k, sgrid, blk, sizeof(StateSmem<DVB>), st, p, hp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (a.flags & RET_NORM_SCORE) {
     auto k = bwd_stats_kernel<DK, DV>;
     if ((e = set_smem(k, sizeof(StatsSmem<DK, DV>))) != hipSuccess) return e;
     hipLaunchKernelGGL(k, tiles, blk, sizeof(StatsSmem<DK, DV>), st, p, hp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((bwd_state_kernel<DK, DV, DVB, true>), sgrid, blk, 0, st, p, hp);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    auto k = bwd_state_kernel<DK, DV, DVB, true>;
+    if ((e = set_smem(k, sizeof(StateSmem<DVB>))) != hipSuccess) return e;
+    hipLaunchKernelGGL(k, sgrid, blk, sizeof(StateSmem<DVB>), st, p, hp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   {
     auto k = bwd_dq_kernel<TG, DK, DV>;
     if ((e = set_smem(k, sizeof(DqSmem<DK, DV>))) != hipSuccess) return e;
