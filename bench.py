@@ -7,7 +7,8 @@ three normalisations, bf16 output): value = tokens/s = b*L / step time.  The
 inputs are resident in HBM before timing; three input/output buffer sets are
 rotated so the 256 MB MALL cannot serve a repeated set.  Secondary lines in
 the same JSON record: the same workload at B = 64, the long workload (L =
-32768, 16 heads), the chunkwise backward on the medium workload, the decode
+32768, 16 heads), the parallel form on short sequences (32 x 8 heads x 512)
+against the chunkwise form, the chunkwise backward on the medium workload, the decode
 step (batch 128, 16 heads, 64 steps from
 position 8192), the GroupNorm + gate epilogue at the block shape, the gated
 MSR block (2 x 8192 tokens, d_model 4096), one RetNet layer around it
@@ -154,7 +155,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true", help="time the primary workload only")
-    ap.add_argument("--secondary", default="medium_B64,backward,long,decode,gate_norm,block,layer,decode_layer,copy",
+    ap.add_argument("--secondary", default="medium_B64,parallel_short,backward,long,decode,gate_norm,block,layer,decode_layer,copy",
                     help="comma list of secondary measurements to run (empty for none)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -224,6 +225,22 @@ def main():
                                "tflops": round(f64_ / (ms64 * 1e-3) / 1e12, 1),
                                "mfma_frac": round(f64_ / (ms64 * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
                                "gbs": round(nbytes / (ms64 * 1e-3) / 1e9, 1)}
+    if "parallel_short" in todo:
+        # short sequences (32 x 8 heads x 512 tokens, the medium head shape): the
+        # parallel form (one chunk) against the chunkwise form at B = 64 and 128
+        sb, sL = 32, 512
+        sq, sk, sv = (dev(x) for x in W.chunkwise_inputs(sb, h, sL, dk, dv, "bf16", 1.0 / 16, seed=5))
+        so = torch.empty((sb, h, sL, dv), dtype=torch.bfloat16, device="cuda")
+        wsp = torch.empty(max(1, R.LIB.retention_parallel_workspace_bytes(sb, h, sL, dk, dv, 1, flags)),
+                          dtype=torch.uint8, device="cuda")
+        msp = time_calls(lambda: R.parallel_fwd(sq, sk, sv, g, th, flags, out=so, workspace=wsp), 10, 3, torch)
+        ent = {"parallel_ms": round(msp, 4), "tokens_per_s": sb * sL / (msp * 1e-3),
+               "tflops": round(chunk_flops(sb, h, sL, dk, dv, sL) / (msp * 1e-3) / 1e12, 1)}
+        for Bc in (64, 128):
+            mc = time_calls(lambda: R.chunkwise_fwd(sq, sk, sv, g, th, Bc, flags, out=so), 10, 3, torch)
+            ent[f"chunkwise_B{Bc}_ms"] = round(mc, 4)
+        extra["parallel_short"] = ent
+        del sq, sk, sv, so, wsp
     if "backward" in todo:
         # chunkwise backward on the medium workload (dq, dk, dv in fp32 from a bf16 dO)
         qd, kd, vd, _ = sets[0]

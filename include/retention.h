@@ -118,6 +118,28 @@ size_t retention_chunkwise_workspace_bytes(int b, int h, int L, int d_k, int d_v
                                            unsigned flags);
 
 /*
+ * retention_parallel_fwd -- the parallel form of a fresh sequence ([notes]
+ * §2.3 with §三.3): O = (Q'K'^T (.) D) V, row-normalised as in
+ * retention_chunkwise_fwd, for short sequences where the whole L x L causal
+ * score matrix is one chunk.  It is retention_chunkwise_fwd with chunk_B = L
+ * (rounded up to a multiple of 64 for the bf16 / f16 (256, 512) kernels), no
+ * state in or out and n_prev = 0: every query tile takes every key tile up to
+ * its diagonal, and no state is carried.  Arguments as in
+ * retention_chunkwise_fwd; the workspace comes from
+ * retention_parallel_workspace_bytes() (may be 0).  The work grows as L^2:
+ * for long sequences the chunkwise call is the one to use.
+ */
+int retention_parallel_fwd(const void* q, ret_strides sq, const void* k, ret_strides sk,
+                           const void* v, ret_strides sv, void* o, ret_strides so,
+                           int b, int h, int L, int d_k, int d_v,
+                           const double* gamma, const double* theta, int64_t pos0, unsigned flags,
+                           ret_dtype in_dt, ret_dtype out_dt,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace retention_parallel_fwd needs for this problem. */
+size_t retention_parallel_workspace_bytes(int b, int h, int L, int d_k, int d_v, ret_dtype in_dt, unsigned flags);
+
+/*
  * retention_chunkwise_bwd -- gradients of retention_chunkwise_fwd for a fresh
  * sequence (the training path of [notes] §四, chunkwise as in §2.4):
  * given g = dL/dO, writes dq = dL/dq, dk = dL/dk, dv = dL/dv of

@@ -49,6 +49,11 @@ def load_library(path=LIB_PATH):
     lib.msr_gate_norm.restype = i32
     lib.msr_gemm.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp]
     lib.msr_gemm.restype = i32
+    lib.retention_parallel_fwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides,
+                                           i32, i32, i32, i32, i32, dp, dp, i64, u32, i32, i32, vp, sz, vp]
+    lib.retention_parallel_fwd.restype = i32
+    lib.retention_parallel_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, u32]
+    lib.retention_parallel_workspace_bytes.restype = sz
     lib.retention_chunkwise_bwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides,
                                             vp, Strides, vp, Strides, vp, Strides,
                                             i32, i32, i32, i32, i32, i32, dp, dp, i64, u32, i32, i32, vp, sz, vp]
@@ -146,6 +151,30 @@ def chunkwise_fwd(q, k, v, gamma, theta, chunk, flags, pos0=0, n_prev=0, state_i
         in_dt, _dt(out), _ptr(state_in), _ptr(state_out), _ptr(z_in), _ptr(z_out),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
     _check(st, "retention_chunkwise_fwd")
+    return out
+
+
+def parallel_fwd(q, k, v, gamma, theta, flags, pos0=0, out=None, out_dtype=None, workspace=None, stream=None):
+    """O = the parallel form of retention ([b,h,L,d] views on the GPU) for a
+    fresh sequence: the whole causal L x L score matrix as one chunk."""
+    b, h, L, dk = q.shape
+    dv = v.shape[-1]
+    in_dt = _dt(q)
+    if _dt(k) != in_dt or _dt(v) != in_dt:
+        raise TypeError("q, k and v must share one dtype")
+    if out is None:
+        od = _torch_dt(in_dt) if out_dtype is None else out_dtype
+        out = torch.empty((b, h, L, dv), dtype=od, device=q.device)
+    g, gp = _f64(gamma, h, "gamma")
+    th, tp = (None, None) if theta is None else _f64(theta, dk // 2, "theta")
+    need = LIB.retention_parallel_workspace_bytes(b, h, L, dk, dv, in_dt, flags)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = LIB.retention_parallel_fwd(
+        _ptr(q), _strides4(q, "q"), _ptr(k), _strides4(k, "k"), _ptr(v), _strides4(v, "v"),
+        _ptr(out), _strides4(out, "o"), b, h, L, dk, dv, gp, tp, pos0, flags, in_dt, _dt(out),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
+    _check(st, "retention_parallel_fwd")
     return out
 
 

@@ -136,6 +136,37 @@ int retention_chunkwise_fwd(const void* q, ret_strides sq, const void* k, ret_st
   return hip_status(e, "retention_chunkwise_fwd launch");
 }
 
+// the chunk that makes the chunkwise kernels compute the parallel form: one
+// chunk covering the sequence (rounded up to a multiple of 64 where the
+// large-chunk kernels serve the shape; a ragged chunk is the same form)
+static int parallel_chunk(ret_dtype in_dt, int L, int d_k, int d_v) {
+  const int B64 = (L + 63) / 64 * 64;
+  return ret::three_phase_applies(in_dt, d_k, d_v, B64) ? B64 : L;
+}
+
+size_t retention_parallel_workspace_bytes(int b, int h, int L, int d_k, int d_v, ret_dtype in_dt, unsigned flags) {
+  if (b <= 0 || h <= 0 || L <= 0 || d_k <= 0 || d_v <= 0 || !valid_dt(in_dt)) return 0;
+  const int B = parallel_chunk(in_dt, L, d_k, d_v);
+  return ret::three_phase_applies(in_dt, d_k, d_v, B) ? ret::three_phase_workspace(b, h, L, B) : 0;
+}
+
+int retention_parallel_fwd(const void* q, ret_strides sq, const void* k, ret_strides sk,
+                           const void* v, ret_strides sv, void* o, ret_strides so,
+                           int b, int h, int L, int d_k, int d_v,
+                           const double* gamma, const double* theta, int64_t pos0, unsigned flags,
+                           ret_dtype in_dt, ret_dtype out_dt,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (L <= 0) return fail(RET_E_INVAL, "sizes must be positive (L=%d)", L);
+  if (!valid_dt(in_dt)) return fail(RET_E_INVAL, "unknown dtype");
+  const int B = parallel_chunk(in_dt, L, d_k, d_v);
+  const size_t need = retention_parallel_workspace_bytes(b, h, L, d_k, d_v, in_dt, flags);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(RET_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : 0);
+  return retention_chunkwise_fwd(q, sq, k, sk, v, sv, o, so, b, h, L, d_k, d_v, B, gamma, theta, pos0, 0, flags,
+                                 in_dt, out_dt, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes,
+                                 stream);
+}
+
 size_t retention_chunkwise_bwd_workspace_bytes(int b, int h, int L, int d_k, int d_v, int chunk_B) {
   if (b <= 0 || h <= 0 || L <= 0 || d_k <= 0 || d_v <= 0 || chunk_B <= 0) return 0;
   return ret::chunkwise_bwd_workspace(b, h, L, d_k, d_v, chunk_B);
