@@ -14,6 +14,9 @@
 // read while step s multiplies.  Rows and columns beyond M / N are clamped on
 // load and skipped on store; K must be a multiple of 32.
 //
+// For M <= 128 rows (a decode step) a column-split kernel without LDS staging
+// is used instead (below).
+//
 // Epilogue options (the RetNet layer, reading notes §四.4): the exact gelu
 // x Phi(x) of each output (FFN's first projection), then the addition of a
 // residual (the layer's two residual connections) stored as fp32, bf16 or
@@ -215,10 +218,151 @@ static hipError_t launch_gemm_a(const void* A, const void* B, void* C, ret_dtype
   return launch_gemm_t<TA, float>(A, B, C, M, N, K, R, r_dt, act, st);
 }
 
+// ---------------------------------------------------------------- skinny
+// M <= 128 rows (a decode step: one token per sequence).  The product is
+// bound by reading the weight B once; the activations A (M x K) are shared by
+// every workgroup and read from L2.  A workgroup owns SKN = 32 columns for all
+// M rows (N / 32 workgroups) and its eight waves split K; each wave multiplies
+// its activation fragments against both 16-column blocks, so a workgroup reads
+// A once per 32 columns.  Every MFMA operand (16x16x32: lane l supplies row or
+// column l % 16 and eight k values) is read straight from global memory.  A
+// 64-deep step is two MFMAs; since the sum over k may take any order shared by
+// A and B, lane l reads the 16 contiguous k values 16 (l / 16) .. + 15 of its
+// row and gives the first eight to one MFMA and the rest to the other, so each
+// row read covers one whole 128-byte line.  The eight partial 128 x 32 tiles
+// are summed through LDS before the epilogue.
+constexpr int SKM = 128, SKN = 32, SKW = 8, SKT = 64 * SKW;
+
+template <typename TA> struct SkOp;
+template <> struct SkOp<bf16> {
+  __device__ __forceinline__ static void mma(f32x4& c, u32x4 a, u32x4 b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                0, 0, 0);
+  }
+  __device__ __forceinline__ static u32x4 cvt_b(u32x4 u) { return u; }
+};
+template <> struct SkOp<half> {
+  __device__ __forceinline__ static void mma(f32x4& c, u32x4 a, u32x4 b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                               0);
+  }
+  __device__ __forceinline__ static u32x4 cvt_b(u32x4 u) { return bf16x8_to_f16x8(u); }
+};
+
+template <typename TA, typename TO>
+__global__ void __launch_bounds__(SKT)
+gemm_skinny_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, TO* C, int M, int N, int K,
+                   const void* R, int r_dt, int act) {
+  __shared__ float red[SKW][SKM * SKN];
+  // the wave index is wave-uniform (readfirstlane): the K loop below is then a
+  // uniform loop, with exact wait counts across its back edge
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * SKN;
+  const int l16 = lane & 15, kq = 16 * (lane >> 4);
+  const int MB = (M + 15) / 16;                      // row blocks in use (<= 8)
+  // this lane's operand rows: weight rows n0 + 16 j + l16, activation rows 16 i + l16 (clamped)
+  const uint16_t* bp[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) bp[j] = B + (int64_t)min(n0 + 16 * j + l16, N - 1) * K + kq;
+  const uint16_t* ap[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ap[i] = A + (int64_t)min(16 * i + l16, M - 1) * K + kq;
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // wave w takes the 64-deep steps w, w + SKW, ...; the next step's operands
+  // are in flight while the current one is multiplied.  A 32-deep tail (K not
+  // a multiple of 64) is taken by wave 0 with the lane's 8 values at 8 (l / 16).
+  const int steps = K / 64;
+  u32x4 bn[2][2] = {}, an[8][2];
+  auto load = [&](int st, u32x4 (&b2)[2][2], u32x4 (&a8)[8][2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b2[j][h] = *reinterpret_cast<const u32x4*>(bp[j] + 64 * st + 8 * h);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a8[i][h] = *reinterpret_cast<const u32x4*>(ap[i] + 64 * st + 8 * h);
+    }
+  };
+  int s = wave;
+  if (s < steps) load(s, bn, an);
+  for (; s < steps; s += SKW) {
+    u32x4 bc[2][2], ac[8][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bc[j][h] = SkOp<TA>::cvt_b(bn[j][h]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ac[i][h] = an[i][h];
+    }
+    load(min(s + SKW, steps - 1), bn, an);          // past the end: reload the last step
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < MB)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) SkOp<TA>::mma(acc[i][j], ac[i][h], bc[j][h]);
+  }
+  if ((K % 64) && wave == 0) {
+    const int kt = 64 * steps - kq + 8 * (lane >> 4);   // this lane's 8 values of the tail
+    u32x4 bt[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bt[j] = SkOp<TA>::cvt_b(*reinterpret_cast<const u32x4*>(bp[j] + kt));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < MB) {
+        const u32x4 at = *reinterpret_cast<const u32x4*>(ap[i] + kt);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) SkOp<TA>::mma(acc[i][j], at, bt[j]);
+      }
+  }
+  // partial tiles -> LDS: lane l holds column l % 16, rows 4 (l / 16) + r of each block
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][(16 * i + 4 * (lane >> 4) + r) * SKN + 16 * j + l16] = acc[i][j][r];
+  __syncthreads();
+  for (int e = tid; e < SKM * SKN; e += SKT) {
+    const int m = e / SKN, n = n0 + e % SKN;
+    if (m < M && n < N) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < SKW; ++w) v += red[w][e];
+      if (act) v = gelu_exact(v);
+      if (R) v += ld_residual(R, r_dt, (size_t)m * N + n);
+      C[(size_t)m * N + n] = Store<TO>::cvt(v);
+    }
+  }
+}
+
+template <typename TA, typename TO>
+static hipError_t launch_skinny_t(const void* A, const void* B, void* C, int M, int N, int K, const void* R, int r_dt,
+                                  int act, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_skinny_kernel<TA, TO>), dim3((N + SKN - 1) / SKN), dim3(SKT), 0, st,
+                     (const uint16_t*)A, (const uint16_t*)B, (TO*)C, M, N, K, R, r_dt, act);
+  return hipGetLastError();
+}
+
+template <typename TA>
+static hipError_t launch_skinny_a(const void* A, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                                  const void* R, int r_dt, int act, hipStream_t st) {
+  if (c_dt == RET_BF16) return launch_skinny_t<TA, bf16>(A, B, C, M, N, K, R, r_dt, act, st);
+  if (c_dt == RET_F16) return launch_skinny_t<TA, half>(A, B, C, M, N, K, R, r_dt, act, st);
+  return launch_skinny_t<TA, float>(A, B, C, M, N, K, R, r_dt, act, st);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
                        const void* R, ret_dtype r_dt, int act, hipStream_t st) {
+  if (M <= SKM)
+    return a_dt == RET_F16 ? launch_skinny_a<half>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, st)
+                           : launch_skinny_a<bf16>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, st);
   return a_dt == RET_F16 ? launch_gemm_a<half>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, st)
                          : launch_gemm_a<bf16>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, st);
 }

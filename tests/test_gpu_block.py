@@ -19,7 +19,9 @@ def R():
     return binding
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 200, 256), (256, 256, 32), (1, 1000, 96), (513, 257, 4096)])
+# M <= 128 takes the column-split (decode) kernel: full, ragged M and N, one K step
+@pytest.mark.parametrize("M,N,K", [(300, 200, 256), (256, 256, 32), (1, 1000, 96), (513, 257, 4096),
+                                   (128, 640, 4096), (77, 300, 512), (128, 17, 32), (129, 64, 64)])
 def test_gemm(R, M, N, K):
     rng = np.random.default_rng(M + N + K)
     a = W.draw(rng, (M, K), 1.0, "bf16")

@@ -64,7 +64,7 @@ def test_layer_norm_rejects(R):
         R.layer_norm(x, -1.0)                      # negative eps
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 200, 256), (1, 1000, 96), (513, 257, 4096)])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 256), (1, 1000, 96), (513, 257, 4096), (128, 512, 2048)])
 def test_gemm_epilogue(R, M, N, K):
     rng = np.random.default_rng(M * 3 + N + K)
     a = W.draw(rng, (M, K), 1.0, "bf16")
