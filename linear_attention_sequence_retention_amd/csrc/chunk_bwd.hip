@@ -298,6 +298,57 @@ struct F32 {          // a 64 x 64 slab of an fp32 state: 4 x 16 bytes per threa
   }
 };
 
+// a wide slab: 64 rows x NC columns of fp16 (NC <= 256), NC / 32 pieces of
+// 16 bytes per thread; rows >= nvalid read as zero (loads clamped, not skipped)
+template <int NC>
+struct HW {
+  static constexpr int PR = NC / 8, NP = TL * PR / BT;
+  u32x4 v[NP];
+  __device__ __forceinline__ void load(const uint16_t* src, int ld, int nvalid) {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int i = threadIdx.x + u * BT, r = i / PR, c8 = i % PR;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src + (int64_t)min(r, nvalid - 1) * ld + 8 * c8);
+      v[u] = r < nvalid ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int pitch) const {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int i = threadIdx.x + u * BT, r = i / PR, c8 = i % PR;
+      *reinterpret_cast<u32x4*>(dst + r * pitch + 8 * c8) = v[u];
+    }
+  }
+};
+// a wide slab of an fp32 state: 64 rows x NC columns, NC / 16 pieces of 16
+// bytes per thread, scaled to fp16 on store
+template <int NC>
+struct FW {
+  static constexpr int PR = NC / 4, NP = TL * PR / BT;
+  f32x4 v[NP];
+  __device__ __forceinline__ void load(const float* src, int ld) {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int i = threadIdx.x + u * BT, r = i / PR, c4 = i % PR;
+      v[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)r * ld + 4 * c4);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int pitch, float down) const {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int i = threadIdx.x + u * BT, r = i / PR, c4 = i % PR;
+      uint2 w;
+      w.x = pack_h2(v[u][0] * down, v[u][1] * down);
+      w.y = pack_h2(v[u][2] * down, v[u][3] * down);
+      *reinterpret_cast<uint2*>(dst + r * pitch + 4 * c4) = w;
+    }
+  }
+};
+
+template <int D, int WM = 256> struct Wide {   // the wide slabs (at most WM columns) of a D-column operand
+  static constexpr int N = D < WM ? D : WM, W = D / N;
+};
+
 // the power of two of one (bh, chunk) state: 2^-e brings its largest
 // magnitude (the maximum of the scan's NM partial maxima) into [2^14, 2^15);
 // returns 2^e
@@ -494,9 +545,10 @@ __global__ void __launch_bounds__(BT) bwd_state_kernel(BwdP p, HeadParams hp) {
 // a_p and c_p of one 64-row query tile (only with the score normalisation)
 template <int DK, int DV>
 struct StatsSmem {
+  static constexpr int PW = (Wide<DK, 128>::N > Wide<DV, 128>::N ? Wide<DK, 128>::N : Wide<DV, 128>::N) + 8;
   uint16_t Qs[TL * (DK + 8)];
   uint16_t Gs[TL * (DV + 8)];
-  uint16_t Sl[2][TL * SP];
+  uint16_t Sl[2][TL * PW];         // wide slabs (the cross term's narrow slabs use pitch SP)
   float red[2][2][TL];             // [den / gnum][column half][row]
   float qz[TL];                    // q'_p . z_c
 };
@@ -533,30 +585,36 @@ __global__ void __launch_bounds__(BT) bwd_stats_kernel(BwdP p, HeadParams hp) {
   if (c > 0) {
     const float* R = p.Rin + ((int64_t)bh * p.nc + c) * DK * DV;
     const float up = state_up<NM>(p.rmax + ((int64_t)bh * p.nc + c) * NM), down = 1.f / up;
-    F32 fr[2];
-    fr[0].load(R, DV);
-    if (NE * ND > 1) fr[1].load(R + (int64_t)(64 * (1 % ND)) * DV + 64 * (1 / ND), DV);
+    // wide slabs R[64 ds ..][NX ew ..], one in flight
+    constexpr int NX = Wide<DV, 128>::N, WX = Wide<DV, 128>::W, PWX = SM::PW;
+    FW<NX> fr;
+    fr.load(R, DV);
 #pragma unroll
-    for (int es = 0; es < NE; ++es) {
-      f32x16 X = {};
+    for (int ew = 0; ew < WX; ++ew) {
+      f32x16 X[NX / 64];
+#pragma unroll
+      for (int u = 0; u < NX / 64; ++u) X[u] = f32x16{};
 #pragma unroll
       for (int ds = 0; ds < ND; ++ds) {
-        const int i = es * ND + ds;
+        const int i = ew * ND + ds, nx = min(i + 1, WX * ND - 1);
         uint16_t* b = sm.Sl[sc++ & 1];
-        fr[i & 1].store(b, down);
+        fr.store(b, PWX, down);
         __syncthreads();
-        const int nx = i + 2;
-        if (nx < NE * ND) fr[i & 1].load(R + (int64_t)(64 * (nx % ND)) * DV + 64 * (nx / ND), DV);
+        fr.load(R + (int64_t)(64 * (nx % ND)) * DV + NX * (nx / ND), DV);
         // X[p][e] += sum_d Q'[p][d] R[d][e]; R staged [d][e] (k = d): transposed B
-        mm64<false, true>(X, sm.Qs + 64 * ds, QP, 32 * bi, b, SP, 32 * bj, lane);
+#pragma unroll
+        for (int u = 0; u < NX / 64; ++u)
+          mm64<false, true>(X[u], sm.Qs + 64 * ds, QP, 32 * bi, b + 64 * u, PWX, 32 * bj, lane);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int pl = 32 * bi + acc_row(r, lane);
-        const float xi = dec.pow((float)(r0 + pl - c0 + 1));
-        const float gv = h2f(sm.Gs[pl * GP + 64 * es + 32 * bj + l32]);
-        gsum[r] += xi * up * X[r] * gv;
-      }
+      for (int u = 0; u < NX / 64; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int pl = 32 * bi + acc_row(r, lane);
+          const float xi = dec.pow((float)(r0 + pl - c0 + 1));
+          const float gv = h2f(sm.Gs[pl * GP + NX * ew + 64 * u + 32 * bj + l32]);
+          gsum[r] += xi * up * X[u][r] * gv;
+        }
     }
     // q'_p . z_c: 4 threads per row
     const float* z = p.zin + ((int64_t)bh * p.nc + c) * DK;
@@ -570,36 +628,46 @@ __global__ void __launch_bounds__(BT) bwd_stats_kernel(BwdP p, HeadParams hp) {
     sm.qz[tid] = 0.f;
   }
 
-  // intra-chunk key tiles up to the diagonal: K' slabs, then V slabs (an even
-  // number per tile, so a slab's register set is fixed by its place in the tile)
-  constexpr int PT = ND + NE;
-  const int nsl = ((r0 - c0) / TL + 1) * PT;
-  auto src = [&](int i, H16& r) {
-    i = min(i, nsl - 1);            // past the end: reload the last slab (every step issues the same loads)
-    const int j = i / PT, w = i - j * PT, m0 = c0 + TL * j, nk = min(TL, p.L - m0);
-    if (w < ND) r.load(Kr + (int64_t)m0 * DK + 64 * w, DK, nk);
-    else r.load(Vb + (int64_t)m0 * DV + 64 * (w - ND), DV, nk);
+  // intra-chunk key tiles up to the diagonal: wide K' slabs, then wide V
+  // slabs, the next one in flight
+  constexpr int N1 = Wide<DK, 128>::N, W1 = Wide<DK, 128>::W, N2 = Wide<DV, 128>::N, W2 = Wide<DV, 128>::W;
+  constexpr int PW = SM::PW;
+  const int nkt = (r0 - c0) / TL + 1;
+  HW<N1> h1;
+  HW<N2> h2;
+  auto ld1 = [&](int j, int w) {                    // past the end: reload the last tile's slab
+    const int m0 = c0 + TL * min(j, nkt - 1);
+    h1.load(Kr + (int64_t)m0 * DK + N1 * w, DK, min(TL, p.L - m0));
   };
-  H16 hr[2];
-  src(0, hr[0]);
-  src(1, hr[1]);
-  for (int m0 = c0, i0 = 0; m0 <= r0; m0 += TL, i0 += PT) {
+  auto ld2 = [&](int j, int w) {
+    const int m0 = c0 + TL * j;
+    h2.load(Vb + (int64_t)m0 * DV + N2 * w, DV, min(TL, p.L - m0));
+  };
+  ld1(0, 0);
+  for (int j = 0; j < nkt; ++j) {
+    const int m0 = c0 + TL * j;
     f32x16 S = {}, T = {};
 #pragma unroll
-    for (int ds = 0; ds < ND; ++ds) {
+    for (int w = 0; w < W1; ++w) {
       uint16_t* b = sm.Sl[sc++ & 1];
-      hr[ds & 1].store(b);
+      h1.store(b, PW);
       __syncthreads();
-      src(i0 + ds + 2, hr[ds & 1]);
-      mm64<false, false>(S, sm.Qs + 64 * ds, QP, 32 * bi, b, SP, 32 * bj, lane);
+      if (w + 1 < W1) ld1(j, w + 1);
+      else ld2(j, 0);
+#pragma unroll
+      for (int u = 0; u < N1 / 64; ++u)
+        mm64<false, false>(S, sm.Qs + N1 * w + 64 * u, QP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
     }
 #pragma unroll
-    for (int es = 0; es < NE; ++es) {
+    for (int w = 0; w < W2; ++w) {
       uint16_t* b = sm.Sl[sc++ & 1];
-      hr[(ND + es) & 1].store(b);
+      h2.store(b, PW);
       __syncthreads();
-      src(i0 + ND + es + 2, hr[(ND + es) & 1]);
-      mm64<false, false>(T, sm.Gs + 64 * es, GP, 32 * bi, b, SP, 32 * bj, lane);
+      if (w + 1 < W2) ld2(j, w + 1);
+      else ld1(j + 1, 0);
+#pragma unroll
+      for (int u = 0; u < N2 / 64; ++u)
+        mm64<false, false>(T, sm.Gs + N2 * w + 64 * u, GP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -668,11 +736,12 @@ __device__ __forceinline__ void store_rotated(const float* t, TG* out, const ret
 // ------------------------------------------------------------ dq
 template <int DK, int DV>
 struct DqSmem {
+  static constexpr int PW = (Wide<DV>::N > Wide<DK>::N ? Wide<DV>::N : Wide<DK>::N) + 8;
   union {
     struct {
       uint16_t Gs[TL * (DV + 8)];
       uint16_t Es[TL * SP];
-      uint16_t Sl[2][TL * SP];
+      uint16_t Sl[2][TL * PW];     // wide slabs (the cross term's narrow slabs use pitch SP)
     } w;
     float out[TL * (DK + 4)];
   } u;
@@ -713,41 +782,43 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
 #pragma unroll
   for (int n = 0; n < ND; ++n) acc[n] = f32x16{};
   int sc = 0;
-  // the intra-chunk slab stream (per key tile: V slabs, then K' slabs; an even
-  // number, so a slab's register set is fixed by its place in the tile); its
-  // first two slabs are requested now
-  constexpr int PT = NE + ND;
-  const int nsl = ((r0 - c0) / TL + 1) * PT;
-  auto src = [&](int i, H16& r) {
-    i = min(i, nsl - 1);            // past the end: reload the last slab (every step issues the same loads)
-    const int j = i / PT, w = i - j * PT, m0 = c0 + TL * j, nk = min(TL, p.L - m0);
-    if (w < NE) r.load(Vb + (int64_t)m0 * DV + 64 * w, DV, nk);
-    else r.load(Kr + (int64_t)m0 * DK + 64 * (w - NE), DK, nk);
+  // the intra-chunk stream of wide slabs: per key tile the V slabs (columns
+  // N1 at a time), then the K' slabs (N2 at a time); the next one is in flight
+  constexpr int N1 = Wide<DV>::N, W1 = Wide<DV>::W, N2 = Wide<DK>::N, W2 = Wide<DK>::W, PW = SM::PW;
+  const int nkt = (r0 - c0) / TL + 1;
+  HW<N1> h1;
+  HW<N2> h2;
+  auto ld1 = [&](int j, int w) {                    // past the end: reload the last tile's slab
+    const int m0 = c0 + TL * min(j, nkt - 1);
+    h1.load(Vb + (int64_t)m0 * DV + N1 * w, DV, min(TL, p.L - m0));
   };
-  H16 hr[2];
-  src(0, hr[0]);
-  src(1, hr[1]);
+  auto ld2 = [&](int j, int w) {
+    const int m0 = c0 + TL * j;
+    h2.load(Kr + (int64_t)m0 * DK + N2 * w, DK, min(TL, p.L - m0));
+  };
+  ld1(0, 0);
 
   // cross: xi_p (a_p (G R_c^T)_pd + c_p z_c[d])
   if (c > 0) {
     const float* R = p.Rin + ((int64_t)bh * p.nc + c) * DK * DV;
     const float* z = p.zin + ((int64_t)bh * p.nc + c) * DK;
     const float up = state_up<NM>(p.rmax + ((int64_t)bh * p.nc + c) * NM), down = 1.f / up;
-    F32 fr[2];
-    fr[0].load(R, DV);
-    if (ND * NE > 1) fr[1].load(R + (int64_t)(64 * (1 / NE)) * DV + 64 * (1 % NE), DV);
+    // wide slabs R[64 ds ..][N1 ew ..], one in flight
+    FW<N1> fr;
+    fr.load(R, DV);
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds)
 #pragma unroll
-      for (int es = 0; es < NE; ++es) {
-        const int i = ds * NE + es;
+      for (int ew = 0; ew < W1; ++ew) {
+        const int i = ds * W1 + ew, nx = min(i + 1, ND * W1 - 1);
         uint16_t* b = sm.u.w.Sl[sc++ & 1];
-        fr[i & 1].store(b, down);
+        fr.store(b, PW, down);
         __syncthreads();
-        const int nx = i + 2;
-        if (nx < ND * NE) fr[i & 1].load(R + (int64_t)(64 * (nx / NE)) * DV + 64 * (nx % NE), DV);
+        fr.load(R + (int64_t)(64 * (nx / W1)) * DV + N1 * (nx % W1), DV);
         // B[n = d][k = e] = R[d][e], staged [d][e]: "nt"
-        mm64<false, false>(acc[ds], sm.u.w.Gs + 64 * es, GP, 32 * bi, b, SP, 32 * bj, lane);
+#pragma unroll
+        for (int u = 0; u < N1 / 64; ++u)
+          mm64<false, false>(acc[ds], sm.u.w.Gs + N1 * ew + 64 * u, GP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
       }
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds) {
@@ -760,15 +831,19 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
     }
   }
   // intra-chunk key tiles up to the diagonal: V slabs (T = G V^T), E, then K' slabs
-  for (int m0 = c0, i0 = 0; m0 <= r0; m0 += TL, i0 += PT) {
+  for (int j = 0; j < nkt; ++j) {
+    const int m0 = c0 + TL * j;
     f32x16 T = {};
 #pragma unroll
-    for (int es = 0; es < NE; ++es) {
+    for (int w = 0; w < W1; ++w) {
       uint16_t* b = sm.u.w.Sl[sc++ & 1];
-      hr[es & 1].store(b);
+      h1.store(b, PW);
       __syncthreads();
-      src(i0 + es + 2, hr[es & 1]);
-      mm64<false, false>(T, sm.u.w.Gs + 64 * es, GP, 32 * bi, b, SP, 32 * bj, lane);
+      if (w + 1 < W1) ld1(j, w + 1);
+      else ld2(j, 0);
+#pragma unroll
+      for (int u = 0; u < N1 / 64; ++u)
+        mm64<false, false>(T, sm.u.w.Gs + N1 * w + 64 * u, GP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
     }
     // E[p][m] -> LDS (row p, column m)
 #pragma unroll
@@ -780,13 +855,16 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
       sm.u.w.Es[pl * SP + ml] = f2h(e);
     }
 #pragma unroll
-    for (int ds = 0; ds < ND; ++ds) {
+    for (int w = 0; w < W2; ++w) {
       uint16_t* b = sm.u.w.Sl[sc++ & 1];
-      hr[(NE + ds) & 1].store(b);
+      h2.store(b, PW);
       __syncthreads();
-      src(i0 + NE + ds + 2, hr[(NE + ds) & 1]);
+      if (w + 1 < W2) ld2(j, w + 1);
+      else ld1(j + 1, 0);
       // dq'[p][d] += sum_m E[p][m] K'[m][d]; K' staged [m][d] (k = m): transposed B
-      mm64<false, true>(acc[ds], sm.u.w.Es, SP, 32 * bi, b, SP, 32 * bj, lane);
+#pragma unroll
+      for (int u = 0; u < N2 / 64; ++u)
+        mm64<false, true>(acc[(N2 / 64) * w + u], sm.u.w.Es, SP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
     }
   }
   __syncthreads();
@@ -802,11 +880,12 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
 // ------------------------------------------------------------ dk
 template <int DK, int DV>
 struct DkSmem {
+  static constexpr int PW = (Wide<DV>::N > Wide<DK>::N ? Wide<DV>::N : Wide<DK>::N) + 8;
   union {
     struct {
       uint16_t Vs[TL * (DV + 8)];
       uint16_t Es[TL * SP];        // E^T [m][p]
-      uint16_t Sl[2][TL * SP];
+      uint16_t Sl[2][TL * PW];     // wide slabs (the cross term's narrow slabs use pitch SP)
     } w;
     float out[TL * (DK + 4)];
   } u;
@@ -838,38 +917,42 @@ __global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
 #pragma unroll
   for (int n = 0; n < ND; ++n) acc[n] = f32x16{};
   int sc = 0;
-  // the intra-chunk slab stream (per query tile: dO slabs, then Q' slabs)
-  constexpr int PT = NE + ND;
-  const int nsl = ((c1 - m0 + TL - 1) / TL) * PT;
-  auto src = [&](int i, H16& r) {
-    i = min(i, nsl - 1);            // past the end: reload the last slab (every step issues the same loads)
-    const int j = i / PT, w = i - j * PT, q0 = m0 + TL * j, nq = min(TL, p.L - q0);
-    if (w < NE) r.load(Gb + (int64_t)q0 * DV + 64 * w, DV, nq);
-    else r.load(Qr + (int64_t)q0 * DK + 64 * (w - NE), DK, nq);
+  // the intra-chunk stream of wide slabs: per query tile the dO slabs, then
+  // the Q' slabs; the next one is in flight
+  constexpr int N1 = Wide<DV>::N, W1 = Wide<DV>::W, N2 = Wide<DK>::N, W2 = Wide<DK>::W, PW = SM::PW;
+  const int nqt = (c1 - m0 + TL - 1) / TL;
+  HW<N1> h1;
+  HW<N2> h2;
+  auto ld1 = [&](int j, int w) {                    // past the end: reload the last tile's slab
+    const int q0 = m0 + TL * min(j, nqt - 1);
+    h1.load(Gb + (int64_t)q0 * DV + N1 * w, DV, min(TL, p.L - q0));
   };
-  H16 hr[2];
-  src(0, hr[0]);
-  src(1, hr[1]);
+  auto ld2 = [&](int j, int w) {
+    const int q0 = m0 + TL * j;
+    h2.load(Qr + (int64_t)q0 * DK + N2 * w, DK, min(TL, p.L - q0));
+  };
+  ld1(0, 0);
 
   // cross: gamma^(c1-m) ((V U_c^T)[m][d] + u_c[d])
   if (c + 1 < p.nc) {
     const float* U = p.Ust + ((int64_t)bh * p.nc + c) * DK * DV;
     const float* u = p.ust + ((int64_t)bh * p.nc + c) * DK;
     const float up = state_up<NM>(p.umax + ((int64_t)bh * p.nc + c) * NM), down = 1.f / up;
-    F32 fr[2];
-    fr[0].load(U, DV);
-    if (ND * NE > 1) fr[1].load(U + (int64_t)(64 * (1 / NE)) * DV + 64 * (1 % NE), DV);
+    // wide slabs U[64 ds ..][N1 ew ..], one in flight
+    FW<N1> fr;
+    fr.load(U, DV);
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds)
 #pragma unroll
-      for (int es = 0; es < NE; ++es) {
-        const int i = ds * NE + es;
+      for (int ew = 0; ew < W1; ++ew) {
+        const int i = ds * W1 + ew, nx = min(i + 1, ND * W1 - 1);
         uint16_t* b = sm.u.w.Sl[sc++ & 1];
-        fr[i & 1].store(b, down);
+        fr.store(b, PW, down);
         __syncthreads();
-        const int nx = i + 2;
-        if (nx < ND * NE) fr[i & 1].load(U + (int64_t)(64 * (nx / NE)) * DV + 64 * (nx % NE), DV);
-        mm64<false, false>(acc[ds], sm.u.w.Vs + 64 * es, VP, 32 * bi, b, SP, 32 * bj, lane);
+        fr.load(U + (int64_t)(64 * (nx / W1)) * DV + N1 * (nx % W1), DV);
+#pragma unroll
+        for (int u = 0; u < N1 / 64; ++u)
+          mm64<false, false>(acc[ds], sm.u.w.Vs + N1 * ew + 64 * u, VP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
       }
 #pragma unroll
     for (int ds = 0; ds < ND; ++ds) {
@@ -882,8 +965,8 @@ __global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
     }
   }
   // intra-chunk query tiles from the diagonal to the chunk end: dO slabs (T^T = V dO^T), E^T, then Q' slabs
-  for (int q0 = m0, i0 = 0; q0 < c1; q0 += TL, i0 += PT) {
-    const int nq = min(TL, p.L - q0);
+  for (int j = 0; j < nqt; ++j) {
+    const int q0 = m0 + TL * j, nq = min(TL, p.L - q0);
     {
       float a, cc;
       row_ac(p, dec, qk, bh, q0 + min(tid & 63, nq - 1), a, cc);
@@ -894,13 +977,16 @@ __global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
     }
     f32x16 T = {};
 #pragma unroll
-    for (int es = 0; es < NE; ++es) {
+    for (int w = 0; w < W1; ++w) {
       uint16_t* b = sm.u.w.Sl[sc++ & 1];
-      hr[es & 1].store(b);
+      h1.store(b, PW);
       __syncthreads();
-      src(i0 + es + 2, hr[es & 1]);
+      if (w + 1 < W1) ld1(j, w + 1);
+      else ld2(j, 0);
       // T^T[m][p] = sum_e V[m][e] G[p][e]
-      mm64<false, false>(T, sm.u.w.Vs + 64 * es, VP, 32 * bi, b, SP, 32 * bj, lane);
+#pragma unroll
+      for (int u = 0; u < N1 / 64; ++u)
+        mm64<false, false>(T, sm.u.w.Vs + N1 * w + 64 * u, VP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -911,13 +997,16 @@ __global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
       sm.u.w.Es[ml * SP + pl] = f2h(e);
     }
 #pragma unroll
-    for (int ds = 0; ds < ND; ++ds) {
+    for (int w = 0; w < W2; ++w) {
       uint16_t* b = sm.u.w.Sl[sc++ & 1];
-      hr[(NE + ds) & 1].store(b);
+      h2.store(b, PW);
       __syncthreads();
-      src(i0 + NE + ds + 2, hr[(NE + ds) & 1]);
+      if (w + 1 < W2) ld2(j, w + 1);
+      else ld1(j + 1, 0);
       // dk'[m][d] += sum_p E^T[m][p] Q'[p][d]; Q' staged [p][d] (k = p): transposed B
-      mm64<false, true>(acc[ds], sm.u.w.Es, SP, 32 * bi, b, SP, 32 * bj, lane);
+#pragma unroll
+      for (int u = 0; u < N2 / 64; ++u)
+        mm64<false, true>(acc[(N2 / 64) * w + u], sm.u.w.Es, SP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
     }
   }
   __syncthreads();
@@ -931,11 +1020,21 @@ __global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
 }
 
 // ------------------------------------------------------------ dv
+// the d_v columns of a key tile go to two workgroups (each recomputing K' Q'^T)
+// where that keeps an even number of slabs per query tile: half the
+// accumulators per wave, so two workgroups fit on a CU
+template <int DK, int DV> struct DvSplit {
+  static constexpr int ND = DK / 64, NE = DV / 64;
+  static constexpr int NEH = (NE > 1 && (ND + NE / 2) % 2 == 0) ? NE / 2 : NE;
+};
+
 template <int DK, int DV>
 struct DvSmem {
+  static constexpr int PW = (Wide<DK, 128>::N > Wide<DvSplit<DK, DV>::NEH * 64, 128>::N
+                                 ? Wide<DK, 128>::N : Wide<DvSplit<DK, DV>::NEH * 64, 128>::N) + 8;
   uint16_t Ks[TL * (DK + 8)];
   uint16_t As[TL * SP];            // a_p A^T [m][p]
-  uint16_t Sl[2][TL * SP];
+  uint16_t Sl[2][TL * PW];         // wide slabs (the cross term's narrow slabs use pitch SP)
   float pa[TL];
 };
 
@@ -946,9 +1045,13 @@ __global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   constexpr int KP = DK + 8, ND = DK / 64, NE = DV / 64;
   constexpr int NM = (DK / 64) * (DV / (DV < 256 ? DV : 256)) * 4;
+  // the d_v columns are split over DvSplit<DK, DV>::N workgroups of NEH 64-column blocks each
+  constexpr int NEH = DvSplit<DK, DV>::NEH, NSPLIT = NE / NEH;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
-  const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
+  const int part = blockIdx.x % NSPLIT, wg = blockIdx.x / NSPLIT;
+  const int e0 = part * NEH * 64;
+  const int bh = wg / p.nt, tile = wg % p.nt;
   const int bb = bh / p.h, head = bh % p.h;
   const int m0 = tile * TL, nk = min(TL, p.L - m0);
   const int c = m0 / p.B, c0 = c * p.B, c1 = min(c0 + p.B, p.L);
@@ -960,53 +1063,58 @@ __global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
   const uint16_t* Gb = p.Gb + (int64_t)bh * p.L * DV;
 
   stage<DK>(sm.Ks, KP, Kr + (int64_t)m0 * DK, DK, nk, nullptr);
-  f32x16 acc[NE];
+  f32x16 acc[NEH];
 #pragma unroll
-  for (int n = 0; n < NE; ++n) acc[n] = f32x16{};
+  for (int n = 0; n < NEH; ++n) acc[n] = f32x16{};
   int sc = 0;
-  // the intra-chunk slab stream (per query tile: Q' slabs, then dO slabs)
-  constexpr int PT = ND + NE;
-  const int nsl = ((c1 - m0 + TL - 1) / TL) * PT;
-  auto src = [&](int i, H16& r) {
-    i = min(i, nsl - 1);            // past the end: reload the last slab (every step issues the same loads)
-    const int j = i / PT, w = i - j * PT, q0 = m0 + TL * j, nq = min(TL, p.L - q0);
-    if (w < ND) r.load(Qr + (int64_t)q0 * DK + 64 * w, DK, nq);
-    else r.load(Gb + (int64_t)q0 * DV + 64 * (w - ND), DV, nq);
+  // the intra-chunk stream of wide slabs: per query tile the Q' slabs, then
+  // this part's dO slabs; the next one is in flight
+  constexpr int N1 = Wide<DK, 128>::N, W1 = Wide<DK, 128>::W;
+  constexpr int N2 = Wide<NEH * 64, 128>::N, W2 = Wide<NEH * 64, 128>::W, PW = SM::PW;
+  const int nqt = (c1 - m0 + TL - 1) / TL;
+  HW<N1> h1;
+  HW<N2> h2;
+  auto ld1 = [&](int j, int w) {                    // past the end: reload the last tile's slab
+    const int q0 = m0 + TL * min(j, nqt - 1);
+    h1.load(Qr + (int64_t)q0 * DK + N1 * w, DK, min(TL, p.L - q0));
   };
-  H16 hr[2];
-  src(0, hr[0]);
-  src(1, hr[1]);
+  auto ld2 = [&](int j, int w) {
+    const int q0 = m0 + TL * j;
+    h2.load(Gb + (int64_t)q0 * DV + e0 + N2 * w, DV, min(TL, p.L - q0));
+  };
+  ld1(0, 0);
 
   // cross: gamma^(c1-m) (K' U_c)[m][e]
   if (c + 1 < p.nc) {
     const float* U = p.Ust + ((int64_t)bh * p.nc + c) * DK * DV;
     const float up = state_up<NM>(p.umax + ((int64_t)bh * p.nc + c) * NM), down = 1.f / up;
-    F32 fr[2];
-    fr[0].load(U, DV);
-    if (ND * NE > 1) fr[1].load(U + (int64_t)(64 * (1 % ND)) * DV + 64 * (1 / ND), DV);
+    // wide slabs U[64 ds ..][e0 + N2 eh ..], one in flight
+    FW<N2> fr;
+    fr.load(U + e0, DV);
 #pragma unroll
-    for (int es = 0; es < NE; ++es)
+    for (int ds = 0; ds < ND; ++ds)
 #pragma unroll
-      for (int ds = 0; ds < ND; ++ds) {
-        const int i = es * ND + ds;
+      for (int eh = 0; eh < W2; ++eh) {
+        const int i = ds * W2 + eh, nx = min(i + 1, ND * W2 - 1);
         uint16_t* b = sm.Sl[sc++ & 1];
-        fr[i & 1].store(b, down);
+        fr.store(b, PW, down);
         __syncthreads();
-        const int nx = i + 2;
-        if (nx < ND * NE) fr[i & 1].load(U + (int64_t)(64 * (nx % ND)) * DV + 64 * (nx / ND), DV);
+        fr.load(U + (int64_t)(64 * (nx / W2)) * DV + e0 + N2 * (nx % W2), DV);
         // B[n = e][k = d] = U[d][e], staged [d][e]: transposed B
-        mm64<false, true>(acc[es], sm.Ks + 64 * ds, KP, 32 * bi, b, SP, 32 * bj, lane);
+#pragma unroll
+        for (int u = 0; u < N2 / 64; ++u)
+          mm64<false, true>(acc[(N2 / 64) * eh + u], sm.Ks + 64 * ds, KP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
       }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float f = up * dec.pow((float)(c1 - (m0 + 32 * bi + acc_row(r, lane))));
 #pragma unroll
-      for (int es = 0; es < NE; ++es) acc[es][r] *= f;
+      for (int es = 0; es < NEH; ++es) acc[es][r] *= f;
     }
   }
   // intra-chunk query tiles from the diagonal to the chunk end: Q' slabs (S^T = K' Q'^T), a A^T, then dO slabs
-  for (int q0 = m0, i0 = 0; q0 < c1; q0 += TL, i0 += PT) {
-    const int nq = min(TL, p.L - q0);
+  for (int j = 0; j < nqt; ++j) {
+    const int q0 = m0 + TL * j, nq = min(TL, p.L - q0);
     {
       float a, cc;
       row_ac(p, dec, qk, bh, q0 + min(tid & 63, nq - 1), a, cc);
@@ -1014,13 +1122,16 @@ __global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
     }
     f32x16 S = {};
 #pragma unroll
-    for (int ds = 0; ds < ND; ++ds) {
+    for (int w = 0; w < W1; ++w) {
       uint16_t* b = sm.Sl[sc++ & 1];
-      hr[ds & 1].store(b);
+      h1.store(b, PW);
       __syncthreads();
-      src(i0 + ds + 2, hr[ds & 1]);
+      if (w + 1 < W1) ld1(j, w + 1);
+      else ld2(j, 0);
       // S^T[m][p] = sum_d K'[m][d] Q'[p][d]
-      mm64<false, false>(S, sm.Ks + 64 * ds, KP, 32 * bi, b, SP, 32 * bj, lane);
+#pragma unroll
+      for (int u = 0; u < N1 / 64; ++u)
+        mm64<false, false>(S, sm.Ks + N1 * w + 64 * u, KP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -1031,23 +1142,26 @@ __global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
       sm.As[ml * SP + pl] = f2h(x);
     }
 #pragma unroll
-    for (int es = 0; es < NE; ++es) {
+    for (int w = 0; w < W2; ++w) {
       uint16_t* b = sm.Sl[sc++ & 1];
-      hr[(ND + es) & 1].store(b);
+      h2.store(b, PW);
       __syncthreads();
-      src(i0 + ND + es + 2, hr[(ND + es) & 1]);
+      if (w + 1 < W2) ld2(j, w + 1);
+      else ld1(j + 1, 0);
       // dv[m][e] += sum_p (a A^T)[m][p] G[p][e]; G staged [p][e] (k = p): transposed B
-      mm64<false, true>(acc[es], sm.As, SP, 32 * bi, b, SP, 32 * bj, lane);
+#pragma unroll
+      for (int u = 0; u < N2 / 64; ++u)
+        mm64<false, true>(acc[(N2 / 64) * w + u], sm.As, SP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
     }
   }
   TG* o = reinterpret_cast<TG*>(p.dv) + bb * p.sdv.b + head * p.sdv.h;
   const float gs = p.gsc[bh];
 #pragma unroll
-  for (int es = 0; es < NE; ++es)
+  for (int es = 0; es < NEH; ++es)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ml = 32 * bi + acc_row(r, lane);
-      if (ml < nk) o[(int64_t)(m0 + ml) * p.sdv.l + 64 * es + 32 * bj + l32] = Store<TG>::cvt(gs * acc[es][r]);
+      if (ml < nk) o[(int64_t)(m0 + ml) * p.sdv.l + e0 + 64 * es + 32 * bj + l32] = Store<TG>::cvt(gs * acc[es][r]);
     }
 }
 
@@ -1154,7 +1268,8 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t st) {
   {
     auto k = bwd_dv_kernel<TG, DK, DV>;
     if ((e = set_smem(k, sizeof(DvSmem<DK, DV>))) != hipSuccess) return e;
-    hipLaunchKernelGGL(k, tiles, blk, sizeof(DvSmem<DK, DV>), st, p, hp);
+    constexpr int NS = (DV / 64) / DvSplit<DK, DV>::NEH;
+    hipLaunchKernelGGL(k, dim3(bh * p.nt * NS), blk, sizeof(DvSmem<DK, DV>), st, p, hp);
   }
   return hipGetLastError();
 }
