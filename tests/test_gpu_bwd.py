@@ -103,3 +103,11 @@ def test_bwd_medium_sampled(R, chunk):
     c = W.CHUNKWISE["medium"]
     _case(R, c["b"], c["h"], c["L"], c["dk"], c["dv"], chunk, c["flags"], seed=0,
           heads=[(0, 0), (2, 5), (3, 7)])
+
+
+@pytest.mark.parametrize("L,chunk,dk,dv", [(1, 64, 128, 256), (65, 64, 128, 256), (130, 128, 128, 128),
+                                           (64, 128, 64, 64), (129, 64, 256, 512)])
+def test_bwd_edges(R, L, chunk, dk, dv):
+    """A single token, a last chunk of one row, the (128, 128) shape, a chunk
+    longer than the sequence, and one row past two full chunks."""
+    _case(R, 2, 2, L, dk, dv, chunk, W.XPOS | W.NORM_ALL, seed=L + dk)

@@ -71,3 +71,8 @@ def test_parallel_equals_chunkwise(R):
     e1 = check("parallel (f32 out)", host64(o), ref, TOL["bf16"])
     e2 = check("chunkwise B64 (f32 out)", host64(oc), ref, TOL["bf16"])
     check("parallel vs chunkwise B64", host64(o), host64(oc), 2 * max(e1, e2) + 1e-6)
+
+
+@pytest.mark.parametrize("L", [1, 2])
+def test_parallel_tiny_lengths(R, L):
+    _case(R, 2, 2, L, 256, 512, "bf16", W.XPOS | W.NORM_ALL, seed=40 + L)
