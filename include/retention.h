@@ -161,7 +161,8 @@ size_t retention_parallel_workspace_bytes(int b, int h, int L, int d_k, int d_v,
  * exactly on the results), so g has no range precondition; q, k, v have the
  * forward's (|q|, |k| < 2^15, |v| < 2^16, s_p |q'_p . k'_m| < 2^16), and
  * |a_p (g_p . v_m) + c_p| < 2^15 must hold for the scaled g (a_p = s_p / n_p,
- * c_p the clamp term).  Supported (d_k, d_v): (64,64), (128,128), (128,256),
+ * c_p the clamp term), with the score normalisation also s_p |g_p . v_m| < 2^15.
+ * Supported (d_k, d_v): (64,64), (128,128), (128,256),
  * (256,512).
  */
 int retention_chunkwise_bwd(const void* q, ret_strides sq, const void* k, ret_strides sk,

@@ -19,10 +19,10 @@
 //   den_p += gamma^(p-c0+1) q'_p . z_c,      g_p . num_p += gamma^(p-c0+1) (q'_p R_c) . g_p
 // and dq, dk are dq', dk' rotated back by -p theta.
 //
-// Kernels, in order: prep (rotated q', k' and bf16 copies of v, dO, once),
-// fstate (R_c, z_c: a scan over the chunks), stats (a_p, c_p; only with the
-// score normalisation), rstate (U_c, u_c: a scan over the chunks from the
-// end), then dq, dk and dv, one 64-row tile per workgroup.  Every product is
+// Kernels, in order: prep (rotated q', k' and fp16 copies of v, dO, once),
+// fstate (R_c, z_c: a scan over the chunks), dq (with the score normalisation
+// it also finds a_p, c_p), rstate (U_c, u_c: a scan over the chunks from the
+// end), then dk and dv, one 64-row tile per workgroup.  Every product is
 // an fp16 v_mfma_f32_32x32x16 with fp32 accumulation on 64-row tiles staged in
 // LDS (fp16's 11-bit significand: bf16 operands would make the roundings of
 // q', k' and of the E / a A tiles 8x larger).  Range: every gradient is linear
@@ -31,7 +31,8 @@
 // back exactly; each 64 x 64 slab of a state copied to fp16 gets its own
 // power of two, undone when its product is added to the fp32 accumulator.
 // The remaining preconditions are the forward's (|q|, |k| < 2^15, |v| < 2^16,
-// s_p |q'_p . k'_m| < 2^16) and |a_p (g_p . v_m) + c_p| < 2^15 for the scaled dO.
+// s_p |q'_p . k'_m| < 2^16) and |a_p (g_p . v_m) + c_p|, s_p |g_p . v_m| < 2^15
+// for the scaled dO.
 // A workgroup is 4 waves; wave w owns the 32 x 32 block (w / 2, w % 2) of
 // each 64 x 64 output tile.
 #include "internal.h"
@@ -541,173 +542,6 @@ __global__ void __launch_bounds__(BT) bwd_state_kernel(BwdP p, HeadParams hp) {
   }
 }
 
-// ------------------------------------------------------------ row statistics
-// a_p and c_p of one 64-row query tile (only with the score normalisation)
-template <int DK, int DV>
-struct StatsSmem {
-  static constexpr int PW = (Wide<DK, 128>::N > Wide<DV, 128>::N ? Wide<DK, 128>::N : Wide<DV, 128>::N) + 8;
-  uint16_t Qs[TL * (DK + 8)];
-  uint16_t Gs[TL * (DV + 8)];
-  uint16_t Sl[2][TL * PW];         // wide slabs (the cross term's narrow slabs use pitch SP)
-  float red[2][2][TL];             // [den / gnum][column half][row]
-  float qz[TL];                    // q'_p . z_c
-};
-
-template <int DK, int DV>
-__global__ void __launch_bounds__(BT) bwd_stats_kernel(BwdP p, HeadParams hp) {
-  typedef StatsSmem<DK, DV> SM;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  constexpr int QP = DK + 8, GP = DV + 8, ND = DK / 64, NE = DV / 64;
-  constexpr int NM = (DK / 64) * (DV / (DV < 256 ? DV : 256)) * 4;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
-  const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
-  const int head = bh % p.h;
-  const int r0 = tile * TL, nq = min(TL, p.L - r0);
-  const int c = r0 / p.B, c0 = c * p.B;
-  Decay dec;
-  dec.init(hp.gamma[head]);
-  const float qk = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
-  const uint16_t* Qr = p.Qr + (int64_t)bh * p.L * DK;
-  const uint16_t* Kr = p.Kr + (int64_t)bh * p.L * DK;
-  const uint16_t* Vb = p.Vb + (int64_t)bh * p.L * DV;
-  const uint16_t* Gb = p.Gb + (int64_t)bh * p.L * DV;
-
-  stage<DK>(sm.Qs, QP, Qr + (int64_t)r0 * DK, DK, nq, nullptr);
-  stage<DV>(sm.Gs, GP, Gb + (int64_t)r0 * DV, DV, nq, nullptr);
-  float dsum[16], gsum[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) dsum[r] = gsum[r] = 0.f;
-  int sc = 0;
-
-  // cross part of g . num: xi_p (q'_p R_c) . g_p, one 64-column block of R at a time
-  if (c > 0) {
-    const float* R = p.Rin + ((int64_t)bh * p.nc + c) * DK * DV;
-    const float up = state_up<NM>(p.rmax + ((int64_t)bh * p.nc + c) * NM), down = 1.f / up;
-    // wide slabs R[64 ds ..][NX ew ..], one in flight
-    constexpr int NX = Wide<DV, 128>::N, WX = Wide<DV, 128>::W, PWX = SM::PW;
-    FW<NX> fr;
-    fr.load(R, DV);
-#pragma unroll
-    for (int ew = 0; ew < WX; ++ew) {
-      f32x16 X[NX / 64];
-#pragma unroll
-      for (int u = 0; u < NX / 64; ++u) X[u] = f32x16{};
-#pragma unroll
-      for (int ds = 0; ds < ND; ++ds) {
-        const int i = ew * ND + ds, nx = min(i + 1, WX * ND - 1);
-        uint16_t* b = sm.Sl[sc++ & 1];
-        fr.store(b, PWX, down);
-        __syncthreads();
-        fr.load(R + (int64_t)(64 * (nx % ND)) * DV + NX * (nx / ND), DV);
-        // X[p][e] += sum_d Q'[p][d] R[d][e]; R staged [d][e] (k = d): transposed B
-#pragma unroll
-        for (int u = 0; u < NX / 64; ++u)
-          mm64<false, true>(X[u], sm.Qs + 64 * ds, QP, 32 * bi, b + 64 * u, PWX, 32 * bj, lane);
-      }
-#pragma unroll
-      for (int u = 0; u < NX / 64; ++u)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int pl = 32 * bi + acc_row(r, lane);
-          const float xi = dec.pow((float)(r0 + pl - c0 + 1));
-          const float gv = h2f(sm.Gs[pl * GP + NX * ew + 64 * u + 32 * bj + l32]);
-          gsum[r] += xi * up * X[u][r] * gv;
-        }
-    }
-    // q'_p . z_c: 4 threads per row
-    const float* z = p.zin + ((int64_t)bh * p.nc + c) * DK;
-    const int row = tid >> 2, part = tid & 3;
-    float acc = 0.f;
-    for (int d = part * (DK / 4); d < (part + 1) * (DK / 4); ++d) acc += h2f(sm.Qs[row * QP + d]) * z[d];
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    if (part == 0) sm.qz[row] = acc * dec.pow((float)(r0 + row - c0 + 1));
-  } else if (tid < TL) {
-    sm.qz[tid] = 0.f;
-  }
-
-  // intra-chunk key tiles up to the diagonal: wide K' slabs, then wide V
-  // slabs, the next one in flight
-  constexpr int N1 = Wide<DK, 128>::N, W1 = Wide<DK, 128>::W, N2 = Wide<DV, 128>::N, W2 = Wide<DV, 128>::W;
-  constexpr int PW = SM::PW;
-  const int nkt = (r0 - c0) / TL + 1;
-  HW<N1> h1;
-  HW<N2> h2;
-  auto ld1 = [&](int j, int w) {                    // past the end: reload the last tile's slab
-    const int m0 = c0 + TL * min(j, nkt - 1);
-    h1.load(Kr + (int64_t)m0 * DK + N1 * w, DK, min(TL, p.L - m0));
-  };
-  auto ld2 = [&](int j, int w) {
-    const int m0 = c0 + TL * j;
-    h2.load(Vb + (int64_t)m0 * DV + N2 * w, DV, min(TL, p.L - m0));
-  };
-  ld1(0, 0);
-  for (int j = 0; j < nkt; ++j) {
-    const int m0 = c0 + TL * j;
-    f32x16 S = {}, T = {};
-#pragma unroll
-    for (int w = 0; w < W1; ++w) {
-      uint16_t* b = sm.Sl[sc++ & 1];
-      h1.store(b, PW);
-      __syncthreads();
-      if (w + 1 < W1) ld1(j, w + 1);
-      else ld2(j, 0);
-#pragma unroll
-      for (int u = 0; u < N1 / 64; ++u)
-        mm64<false, false>(S, sm.Qs + N1 * w + 64 * u, QP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
-    }
-#pragma unroll
-    for (int w = 0; w < W2; ++w) {
-      uint16_t* b = sm.Sl[sc++ & 1];
-      h2.store(b, PW);
-      __syncthreads();
-      if (w + 1 < W2) ld2(j, w + 1);
-      else ld1(j + 1, 0);
-#pragma unroll
-      for (int u = 0; u < N2 / 64; ++u)
-        mm64<false, false>(T, sm.Gs + N2 * w + 64 * u, GP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = r0 + 32 * bi + acc_row(r, lane), col = m0 + 32 * bj + l32;
-      const bool ok = col <= row && col < p.L && row < p.L;
-      const float A = ok ? S[r] * dec.pow((float)(row - col)) : 0.f;
-      dsum[r] += A;
-      gsum[r] += A * T[r];
-    }
-  }
-  // row sums over the 32 columns of each half-wave, then over the two column blocks
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float d = dsum[r], g = gsum[r];
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) {
-      d += __shfl_xor(d, o, 64);
-      g += __shfl_xor(g, o, 64);
-    }
-    if (l32 == 0) {
-      const int pl = 32 * bi + acc_row(r, lane);
-      sm.red[0][bj][pl] = d;
-      sm.red[1][bj][pl] = g;
-    }
-  }
-  __syncthreads();
-  if (tid < nq) {
-    const int row = r0 + tid;
-    const float den = sm.red[0][0][tid] + sm.red[0][1][tid] + sm.qz[tid];
-    const float gn = sm.red[1][0][tid] + sm.red[1][1][tid];
-    const float s = row_scale(dec, p.flags, qk, row + 1);
-    const float sd = fabsf(s * den);
-    const float n = fmaxf(sd, 1.f);
-    float cc = 0.f;
-    if (sd > 1.f) cc = -(s * s) * (den > 0.f ? 1.f : -1.f) * gn / (n * n);
-    p.ra[(int64_t)bh * p.L + row] = s / n;
-    p.rc[(int64_t)bh * p.L + row] = cc;
-  }
-}
-
 // ------------------------------------------------------------ epilogue
 // an fp32 tile [64][DK + 4] in LDS -> rows of dq / dk, times gs (the 2^e of
 // the head's dO) and rotated back by -p theta
@@ -741,14 +575,20 @@ struct DqSmem {
     struct {
       uint16_t Gs[TL * (DV + 8)];
       uint16_t Es[TL * SP];
+      uint16_t Ys[TL * SP];        // the decay tile (only with the row statistics)
       uint16_t Sl[2][TL * PW];     // wide slabs (the cross term's narrow slabs use pitch SP)
     } w;
     float out[TL * (DK + 4)];
   } u;
   float ra[TL], rc[TL], xi[TL];
+  float red[2][2][TL];             // [den / s g.num][column half][row]
 };
 
-template <typename TG, int DK, int DV>
+// With ST (score normalisation) the kernel also finds a_p and c_p: it carries
+// X = diag(s) ((Gamma o T) K' + xi G R_c^T) and Y = Gamma K' + xi z_c apart, so
+// that den_p = q'_p . Y_p and s_p (g_p . num_p) = q'_p . X_p, then
+// dq'_p = X_p / n_p + c_p Y_p; a_p and c_p go to ra / rc for the later kernels.
+template <typename TG, int DK, int DV, bool ST>
 __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
   typedef DqSmem<DK, DV> SM;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -768,7 +608,12 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
   const uint16_t* Vb = p.Vb + (int64_t)bh * p.L * DV;
   const uint16_t* Gb = p.Gb + (int64_t)bh * p.L * DV;
 
-  {
+  if (ST) {
+    if (tid < TL) {                                 // ra holds s_p until the statistics are known
+      sm.ra[tid] = row_scale(dec, p.flags, qk, r0 + min(tid, nq - 1) + 1);
+      sm.xi[tid] = dec.pow((float)(r0 + tid - c0 + 1));
+    }
+  } else {
     float a, cc;
     row_ac(p, dec, qk, bh, r0 + min(tid & 63, nq - 1), a, cc);
     if (tid < TL) {
@@ -778,9 +623,11 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
     }
   }
   stage<DV>(sm.u.w.Gs, GP, Gb + (int64_t)r0 * DV, DV, nq, nullptr);
-  f32x16 acc[ND];
+  f32x16 acc[ND], Y[ST ? ND : 1];
 #pragma unroll
   for (int n = 0; n < ND; ++n) acc[n] = f32x16{};
+#pragma unroll
+  for (int n = 0; n < (ST ? ND : 1); ++n) Y[n] = f32x16{};
   int sc = 0;
   // the intra-chunk stream of wide slabs: per key tile the V slabs (columns
   // N1 at a time), then the K' slabs (N2 at a time); the next one is in flight
@@ -826,7 +673,12 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int pl = 32 * bi + acc_row(r, lane);
-        acc[ds][r] = sm.xi[pl] * (sm.ra[pl] * up * acc[ds][r] + sm.rc[pl] * zd);
+        if (ST) {
+          acc[ds][r] = sm.xi[pl] * sm.ra[pl] * up * acc[ds][r];
+          Y[ds][r] = sm.xi[pl] * zd;
+        } else {
+          acc[ds][r] = sm.xi[pl] * (sm.ra[pl] * up * acc[ds][r] + sm.rc[pl] * zd);
+        }
       }
     }
   }
@@ -851,8 +703,13 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
       const int pl = 32 * bi + acc_row(r, lane), ml = 32 * bj + l32;
       const int row = r0 + pl, col = m0 + ml;
       const bool ok = col <= row && col < p.L && row < p.L;
-      const float e = ok ? dec.pow((float)(row - col)) * (sm.ra[pl] * T[r] + sm.rc[pl]) : 0.f;
-      sm.u.w.Es[pl * SP + ml] = f2h(e);
+      const float gm = ok ? dec.pow((float)(row - col)) : 0.f;
+      if (ST) {
+        sm.u.w.Es[pl * SP + ml] = f2h(gm * sm.ra[pl] * T[r]);
+        sm.u.w.Ys[pl * SP + ml] = f2h(gm);
+      } else {
+        sm.u.w.Es[pl * SP + ml] = f2h(gm * (sm.ra[pl] * T[r] + sm.rc[pl]));
+      }
     }
 #pragma unroll
     for (int w = 0; w < W2; ++w) {
@@ -863,9 +720,69 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
       else ld1(j + 1, 0);
       // dq'[p][d] += sum_m E[p][m] K'[m][d]; K' staged [m][d] (k = m): transposed B
 #pragma unroll
-      for (int u = 0; u < N2 / 64; ++u)
+      for (int u = 0; u < N2 / 64; ++u) {
         mm64<false, true>(acc[(N2 / 64) * w + u], sm.u.w.Es, SP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
+        if (ST)
+          mm64<false, true>(Y[ST ? (N2 / 64) * w + u : 0], sm.u.w.Ys, SP, 32 * bi, b + 64 * u, PW, 32 * bj, lane);
+      }
     }
+  }
+  if (ST) {
+    // row sums q'_p . Y_p (den_p) and q'_p . X_p (s_p g_p . num_p): q' staged
+    // over the G tile (last read before the final slab's barrier), 32 columns
+    // per half-wave, then the two column halves
+    constexpr int QP = DK + 8;
+    stage<DK>(sm.u.w.Gs, QP, p.Qr + ((int64_t)bh * p.L + r0) * DK, DK, nq, nullptr);
+    __syncthreads();
+    float d[16], g[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) d[r] = g[r] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float qv = h2f(sm.u.w.Gs[(32 * bi + acc_row(r, lane)) * QP + 64 * ds + 32 * bj + l32]);
+        d[r] += qv * Y[ST ? ds : 0][r];
+        g[r] += qv * acc[ds][r];
+      }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) {
+        d[r] += __shfl_xor(d[r], o, 64);
+        g[r] += __shfl_xor(g[r], o, 64);
+      }
+      if (l32 == 0) {
+        const int pl = 32 * bi + acc_row(r, lane);
+        sm.red[0][bj][pl] = d[r];
+        sm.red[1][bj][pl] = g[r];
+      }
+    }
+    __syncthreads();
+    if (tid < TL) {
+      const int row = r0 + tid;
+      const float den = sm.red[0][0][tid] + sm.red[0][1][tid];
+      const float sg = sm.red[1][0][tid] + sm.red[1][1][tid];
+      const float s = sm.ra[tid];
+      const float sd = fabsf(s * den);
+      const float n = fmaxf(sd, 1.f);
+      const float cc = sd > 1.f ? -s * (den > 0.f ? 1.f : -1.f) * sg / (n * n) : 0.f;
+      const bool ok = tid < nq;
+      if (ok) {
+        p.ra[(int64_t)bh * p.L + row] = s / n;
+        p.rc[(int64_t)bh * p.L + row] = cc;
+      }
+      sm.rc[tid] = ok ? cc : 0.f;
+      sm.xi[tid] = ok ? 1.f / n : 0.f;              // the factor on X
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ds = 0; ds < ND; ++ds)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pl = 32 * bi + acc_row(r, lane);
+        acc[ds][r] = sm.xi[pl] * acc[ds][r] + sm.rc[pl] * Y[ST ? ds : 0][r];
+      }
   }
   __syncthreads();
 #pragma unroll
@@ -1241,22 +1158,18 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k, sgrid, blk, sizeof(StateSmem<DVB>), st, p, hp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (a.flags & RET_NORM_SCORE) {
-    auto k = bwd_stats_kernel<DK, DV>;
-    if ((e = set_smem(k, sizeof(StatsSmem<DK, DV>))) != hipSuccess) return e;
-    hipLaunchKernelGGL(k, tiles, blk, sizeof(StatsSmem<DK, DV>), st, p, hp);
+  {
+    // dq needs only the forward states; with the score normalisation it also
+    // writes the a_p, c_p that the reverse scan, dk and dv read
+    auto k = (a.flags & RET_NORM_SCORE) ? bwd_dq_kernel<TG, DK, DV, true> : bwd_dq_kernel<TG, DK, DV, false>;
+    if ((e = set_smem(k, sizeof(DqSmem<DK, DV>))) != hipSuccess) return e;
+    hipLaunchKernelGGL(k, tiles, blk, sizeof(DqSmem<DK, DV>), st, p, hp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {
     auto k = bwd_state_kernel<DK, DV, DVB, true>;
     if ((e = set_smem(k, sizeof(StateSmem<DVB>))) != hipSuccess) return e;
     hipLaunchKernelGGL(k, sgrid, blk, sizeof(StateSmem<DVB>), st, p, hp);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  {
-    auto k = bwd_dq_kernel<TG, DK, DV>;
-    if ((e = set_smem(k, sizeof(DqSmem<DK, DV>))) != hipSuccess) return e;
-    hipLaunchKernelGGL(k, tiles, blk, sizeof(DqSmem<DK, DV>), st, p, hp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {
