@@ -251,6 +251,28 @@ int msr_gemm_ex(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype
                 const void* residual, ret_dtype r_dt, unsigned epilogue, hipStream_t stream);
 
 /*
+ * msr_gemm_ws -- msr_gemm_ex with a caller-provided workspace, for the
+ * projections of a decode step (one token per sequence, M <= 128 rows; the
+ * same products as msr_gemm_ex, [notes] §三.2 and §四.4).  With M <= 128 and
+ * K a multiple of 128 the columns are taken 128 per workgroup and K is split
+ * into up to 8 slices whose fp32 partial products go to the workspace; a
+ * second kernel sums them in slice order (the result does not depend on
+ * scheduling) and applies the epilogue.  Otherwise msr_gemm_ex runs and the
+ * workspace is not touched.
+ *   workspace   device memory of msr_gemm_workspace_bytes(M, N, K) bytes,
+ *               256-byte aligned, overlapping none of A, B, C and residual;
+ *               may be NULL when that size is 0; its contents on entry do
+ *               not matter and are overwritten
+ * Calls that share a workspace must be ordered (one stream, or events).
+ * Everything else, including the errors, as msr_gemm_ex; RET_E_WORKSPACE when
+ * the workspace is missing or too small, RET_E_ALIGN when it is misaligned.
+ */
+size_t msr_gemm_workspace_bytes(int M, int N, int K);
+int msr_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                const void* residual, ret_dtype r_dt, unsigned epilogue, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/*
  * ret_layer_norm -- the LayerNorm of the RetNet layer ([notes] §四.4):
  *   y = (x - mean) / sqrt(biased variance + eps) over each row, then the
  *   optional per-channel affine

@@ -62,6 +62,10 @@ def load_library(path=LIB_PATH):
     lib.retention_chunkwise_bwd_workspace_bytes.restype = sz
     lib.msr_gemm_ex.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, u32, vp]
     lib.msr_gemm_ex.restype = i32
+    lib.msr_gemm_ws.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, u32, vp, sz, vp]
+    lib.msr_gemm_ws.restype = i32
+    lib.msr_gemm_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.msr_gemm_workspace_bytes.restype = sz
     lib.ret_layer_norm.argtypes = [vp, vp, i32, i32, vp, vp, f32, i32, i32, vp]
     lib.ret_layer_norm.restype = i32
     lib.retention_last_error.argtypes = []
@@ -243,10 +247,17 @@ def gate_norm(y, g, eps, weight=None, bias=None, out=None, out_dtype=None, strea
     return out
 
 
-def gemm(a, b_nk, out=None, out_dtype=torch.bfloat16, residual=None, gelu=False, stream=None):
+def gemm_workspace_bytes(M, N, K):
+    return int(LIB.msr_gemm_workspace_bytes(M, N, K))
+
+
+def gemm(a, b_nk, out=None, out_dtype=torch.bfloat16, residual=None, gelu=False, workspace=None, stream=None):
     """C = act(a . b_nk^T) (+ residual) for a [M, K] (bf16 or fp16) and a bf16
     weight b_nk [N, K]; act is the exact gelu when gelu is set, and residual
-    ([M, N], float32, bf16 or fp16, added in fp32) may be out itself."""
+    ([M, N], float32, bf16 or fp16, added in fp32) may be out itself.  With
+    M <= 128 (a decode step) and K a multiple of 128 the split-K path runs
+    (msr_gemm_ws) in workspace, a uint8 device tensor of at least
+    gemm_workspace_bytes(M, N, K) bytes, allocated here when not given."""
     if a.dtype not in (torch.bfloat16, torch.float16) or b_nk.dtype != torch.bfloat16:
         raise TypeError("gemm takes a bf16 or fp16 A and a bf16 weight")
     if not a.is_contiguous() or not b_nk.is_contiguous():
@@ -257,13 +268,24 @@ def gemm(a, b_nk, out=None, out_dtype=torch.bfloat16, residual=None, gelu=False,
         raise ValueError("inner dimensions differ")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    if residual is not None:
+        if tuple(residual.shape) != (M, N) or not residual.is_contiguous():
+            raise ValueError("residual must be a contiguous [M, N] tensor")
+    need = gemm_workspace_bytes(M, N, K)
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+            if stream is not None:
+                workspace.record_stream(stream)
+        st = LIB.msr_gemm_ws(_ptr(a), _dt(a), _ptr(b_nk), _ptr(out), _dt(out), M, N, K, _ptr(residual),
+                             _dt(out if residual is None else residual), 1 if gelu else 0,
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+        _check(st, "msr_gemm_ws")
+        return out
     if residual is None and not gelu:
         st = LIB.msr_gemm(_ptr(a), _dt(a), _ptr(b_nk), _ptr(out), _dt(out), M, N, K, _stream(stream))
         _check(st, "msr_gemm")
         return out
-    if residual is not None:
-        if tuple(residual.shape) != (M, N) or not residual.is_contiguous():
-            raise ValueError("residual must be a contiguous [M, N] tensor")
     st = LIB.msr_gemm_ex(_ptr(a), _dt(a), _ptr(b_nk), _ptr(out), _dt(out), M, N, K, _ptr(residual),
                          _dt(out if residual is None else residual), 1 if gelu else 0, _stream(stream))
     _check(st, "msr_gemm_ex")

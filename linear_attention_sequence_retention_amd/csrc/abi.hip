@@ -276,8 +276,8 @@ int msr_gate_norm(const void* y, ret_strides sy, const void* g, void* out,
   return hip_status(ret::launch_gate_norm(a, stream), "msr_gate_norm launch");
 }
 
-int msr_gemm_ex(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
-                const void* residual, ret_dtype r_dt, unsigned epilogue, hipStream_t stream) {
+static int gemm_checks(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                       const void* residual, ret_dtype r_dt, unsigned epilogue) {
   if (M <= 0 || N <= 0 || K <= 0) return fail(RET_E_INVAL, "sizes must be positive (M=%d N=%d K=%d)", M, N, K);
   if (K % 32) return fail(RET_E_UNSUPPORTED, "K must be a multiple of 32 (got %d)", K);
   if (!valid_dt(c_dt) || !valid_dt(a_dt) || (residual && !valid_dt(r_dt))) return fail(RET_E_INVAL, "unknown dtype");
@@ -289,9 +289,46 @@ int msr_gemm_ex(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype
   if (C == A || C == B) return fail(RET_E_INVAL, "C must not alias A or B");
   if (residual && (residual == A || residual == B)) return fail(RET_E_INVAL, "residual must not alias A or B");
   if (residual == C && r_dt != c_dt) return fail(RET_E_INVAL, "a residual that is C must have C's dtype");
+  return RET_OK;
+}
+
+int msr_gemm_ex(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                const void* residual, ret_dtype r_dt, unsigned epilogue, hipStream_t stream) {
+  const int st = gemm_checks(A, a_dt, B, C, c_dt, M, N, K, residual, r_dt, epilogue);
+  if (st != RET_OK) return st;
   return hip_status(ret::launch_gemm(A, a_dt, B, C, c_dt, M, N, K, residual, r_dt, (epilogue & MSR_GEMM_GELU) ? 1 : 0,
                                      stream),
                     "msr_gemm launch");
+}
+
+size_t msr_gemm_workspace_bytes(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return ret::gemm_workspace_bytes(M, N, K);
+}
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return a && b && x < y + nb && y < x + na;
+}
+
+int msr_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                const void* residual, ret_dtype r_dt, unsigned epilogue, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  const int st = gemm_checks(A, a_dt, B, C, c_dt, M, N, K, residual, r_dt, epilogue);
+  if (st != RET_OK) return st;
+  const size_t need = ret::gemm_workspace_bytes(M, N, K);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(RET_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : 0);
+    if (!aligned(workspace, 256)) return fail(RET_E_ALIGN, "workspace must be 256-byte aligned");
+    const size_t ea = 2, ec = c_dt == RET_F32 ? 4 : 2, er = r_dt == RET_F32 ? 4 : 2;
+    if (overlaps(workspace, need, A, ea * M * K) || overlaps(workspace, need, B, (size_t)2 * N * K) ||
+        overlaps(workspace, need, C, ec * M * N) || (residual && overlaps(workspace, need, residual, er * M * N)))
+      return fail(RET_E_INVAL, "workspace must not overlap A, B, C or residual");
+  }
+  return hip_status(ret::launch_gemm_ws(A, a_dt, B, C, c_dt, M, N, K, residual, r_dt,
+                                        (epilogue & MSR_GEMM_GELU) ? 1 : 0, workspace, stream),
+                    "msr_gemm_ws launch");
 }
 
 int msr_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,

@@ -15,7 +15,8 @@
 // load and skipped on store; K must be a multiple of 32.
 //
 // For M <= 128 rows (a decode step) a column-split kernel without LDS staging
-// is used instead (below).
+// is used instead, or, when the caller brings a workspace, a split-K kernel
+// with the activation rows staged in LDS (below).
 //
 // Epilogue options (the RetNet layer, reading notes §四.4): the exact gelu
 // x Phi(x) of each output (FFN's first projection), then the addition of a
@@ -356,6 +357,131 @@ static hipError_t launch_skinny_a(const void* A, const void* B, void* C, ret_dty
   return launch_skinny_t<TA, float>(A, B, C, M, N, K, R, r_dt, act, st);
 }
 
+// ---------------------------------------------------------------- split-K
+// M <= 128 rows with a workspace.  Every workgroup that works on a column
+// block reads all M rows of A over its K range, so the activation bytes moved
+// from L2 are (N / columns per workgroup) x |A|: at 32 columns per workgroup
+// and K = 4096 that is 4x the weight bytes.  Here a workgroup owns SPN = 128
+// columns and one of KS slices of K; the slice's A rows are staged through LDS
+// (SPK = 128 deep, two buffers, one barrier per step) and shared by the eight
+// waves, each of which owns 16 columns and reads its weight fragments straight
+// from global memory (lane l: column l % 16, the eight k values 8 (l / 16) of
+// each 32-deep block, a contiguous 64 bytes per column and block).  Each slice
+// writes its fp32 partial tile; a second kernel sums the KS partials in slice
+// order (so the result does not depend on scheduling) and applies the
+// epilogue.
+constexpr int SPN = 128, SPK = 128, SPT = 512, SPP = SPK + 8;
+
+// slices: the most (up to 8) that keep at least 128 x 128 per workgroup
+// and at most ~512 workgroups
+__host__ inline int splitk_slices(int N, int K) {
+  const int nb = (N + SPN - 1) / SPN;
+  int ks = 1;
+  while (ks < 8 && nb * ks * 2 <= 512 && K % (SPK * ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+template <typename TA>
+__global__ void __launch_bounds__(SPT)
+gemm_splitk_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, float* __restrict__ P, int M,
+                   int N, int K) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][SKM * SPP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * SPN, KL = K / gridDim.y, k0 = blockIdx.y * KL;
+  const int l16 = lane & 15, kq = 8 * (lane >> 4);
+  const uint16_t* bp = B + (int64_t)min(n0 + 16 * wave + l16, N - 1) * K + k0 + kq;
+  // A staging: 128 rows x 128 k = 2048 pieces of 16 bytes, 4 per thread (row e / 16, piece e % 16)
+  const uint16_t* apc[4];
+  int aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + i * SPT, r = e >> 4, c = e & 15;
+    apc[i] = A + (int64_t)min(r, M - 1) * K + k0 + 8 * c;
+    aoff[i] = r * SPP + 8 * c;
+  }
+  const int steps = KL / SPK;
+  u32x4 an[4], bn[4];
+  auto load = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) an[i] = *reinterpret_cast<const u32x4*>(apc[i] + SPK * st);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) bn[kb] = *reinterpret_cast<const u32x4*>(bp + SPK * st + 32 * kb);
+  };
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&As[0][aoff[i]]) = an[i];
+  __syncthreads();
+  for (int st = 0; st < steps; ++st) {
+    u32x4 bc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) bc[kb] = SkOp<TA>::cvt_b(bn[kb]);
+    load(min(st + 1, steps - 1));                   // past the end: reload the last step
+    const uint16_t* a = As[st & 1];
+    // all eight row blocks, also past M (rows clamped on staging, never
+    // stored): a branch per block would copy the accumulators at every join
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(a + (16 * i + l16) * SPP + 32 * kb + kq);
+        SkOp<TA>::mma(acc[i], af, bc[kb]);
+      }
+    // the other buffer was last read in step st - 1, before this step's barrier
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&As[(st + 1) & 1][aoff[i]]) = an[i];
+    __syncthreads();
+  }
+  // partial tile: lane l holds column 16 w + l % 16, rows 16 i + 4 (l / 16) + r
+  const int n = n0 + 16 * wave + l16;
+  float* pp = P + (int64_t)blockIdx.y * M * N;
+  if (n < N) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * i + 4 * (lane >> 4) + r;
+        if (m < M) pp[(int64_t)m * N + n] = acc[i][r];
+      }
+  }
+}
+
+template <typename TO>
+__global__ void __launch_bounds__(256)
+gemm_splitk_reduce(const float* __restrict__ P, int ks, TO* C, int M, int N, const void* R, int r_dt, int act) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x, mn = (int64_t)M * N;
+  if (e >= mn) return;
+  float v = 0.f;
+  for (int y = 0; y < ks; ++y) v += P[y * mn + e];
+  if (act) v = gelu_exact(v);
+  if (R) v += ld_residual(R, r_dt, (size_t)e);
+  C[e] = Store<TO>::cvt(v);
+}
+
+template <typename TA, typename TO>
+static hipError_t launch_splitk_t(const void* A, const void* B, void* C, int M, int N, int K, const void* R,
+                                  int r_dt, int act, float* P, hipStream_t st) {
+  const int ks = splitk_slices(N, K);
+  hipLaunchKernelGGL((gemm_splitk_kernel<TA>), dim3((N + SPN - 1) / SPN, ks), dim3(SPT), 0, st,
+                     (const uint16_t*)A, (const uint16_t*)B, P, M, N, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t mn = (int64_t)M * N;
+  hipLaunchKernelGGL((gemm_splitk_reduce<TO>), dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st, P, ks,
+                     (TO*)C, M, N, R, r_dt, act);
+  return hipGetLastError();
+}
+
+template <typename TA>
+static hipError_t launch_splitk_a(const void* A, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                                  const void* R, int r_dt, int act, float* P, hipStream_t st) {
+  if (c_dt == RET_BF16) return launch_splitk_t<TA, bf16>(A, B, C, M, N, K, R, r_dt, act, P, st);
+  if (c_dt == RET_F16) return launch_splitk_t<TA, half>(A, B, C, M, N, K, R, r_dt, act, P, st);
+  return launch_splitk_t<TA, float>(A, B, C, M, N, K, R, r_dt, act, P, st);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
@@ -365,6 +491,19 @@ hipError_t launch_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, re
                            : launch_skinny_a<bf16>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, st);
   return a_dt == RET_F16 ? launch_gemm_a<half>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, st)
                          : launch_gemm_a<bf16>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, st);
+}
+
+size_t gemm_workspace_bytes(int M, int N, int K) {
+  if (M > SKM || K % SPK) return 0;
+  return (size_t)splitk_slices(N, K) * M * N * sizeof(float);
+}
+
+hipError_t launch_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                          const void* R, ret_dtype r_dt, int act, void* ws, hipStream_t st) {
+  if (gemm_workspace_bytes(M, N, K) == 0) return launch_gemm(A, a_dt, B, C, c_dt, M, N, K, R, r_dt, act, st);
+  float* P = static_cast<float*>(ws);
+  return a_dt == RET_F16 ? launch_splitk_a<half>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, P, st)
+                         : launch_splitk_a<bf16>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, P, st);
 }
 
 }  // namespace ret

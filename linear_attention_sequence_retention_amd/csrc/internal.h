@@ -98,6 +98,11 @@ hipError_t launch_chunkwise_bwd(const BwdArgs& a, hipStream_t st);
 // R: optional residual [M][N] of c_dt added after the optional exact gelu (act != 0)
 hipError_t launch_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
                        const void* R, ret_dtype r_dt, int act, hipStream_t st);
+// M <= 128 with K a multiple of 128: split-K through a workspace of
+// gemm_workspace_bytes() bytes (0: no workspace is needed and launch_gemm runs)
+size_t gemm_workspace_bytes(int M, int N, int K);
+hipError_t launch_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                          const void* R, ret_dtype r_dt, int act, void* ws, hipStream_t st);
 hipError_t launch_layer_norm(const void* x, void* y, int rows, int d, const float* w, const float* bias, float eps,
                              ret_dtype x_dt, ret_dtype y_dt, hipStream_t st);
 

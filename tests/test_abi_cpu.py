@@ -202,3 +202,12 @@ def test_layer_norm_and_gemm_ex_validation(B):
     assert L.msr_gemm_ex(A, 1, Bm, C, 0, 16, 16, 64, C, 1, 0, None) == 1         # residual C with another dtype
     assert L.msr_gemm_ex(A, 1, Bm, C, 0, 16, 16, 64, A, 1, 0, None) == 1         # residual aliases A
     assert L.msr_gemm_ex(A, 1, Bm, C, 0, 16, 16, 64, FAKE_MIS, 0, 0, None) == 3
+    # split-K workspace: 128 x 128 columns per workgroup, up to 8 slices of K (a multiple of 128)
+    L.msr_gemm_workspace_bytes.argtypes = [ctypes.c_int] * 3
+    L.msr_gemm_workspace_bytes.restype = ctypes.c_size_t
+    assert L.msr_gemm_workspace_bytes(128, 4096, 4096) == 8 * 128 * 4096 * 4
+    assert L.msr_gemm_workspace_bytes(128, 16384, 4096) == 4 * 128 * 16384 * 4
+    assert L.msr_gemm_workspace_bytes(1, 640, 128) == 1 * 1 * 640 * 4
+    assert L.msr_gemm_workspace_bytes(129, 4096, 4096) == 0        # column-split / tiled kernels
+    assert L.msr_gemm_workspace_bytes(128, 4096, 4128) == 0        # K not a multiple of 128
+    assert L.msr_gemm_workspace_bytes(0, 4096, 4096) == 0

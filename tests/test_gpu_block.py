@@ -40,6 +40,63 @@ def test_gemm(R, M, N, K):
     check(f"gemm {M}x{N}x{K} f16 A", host64(c), ref, TOL["f32"])
 
 
+# M <= 128: the column-split kernel (msr_gemm_ex) and the split-K kernel with
+# a workspace (msr_gemm_ws): K from one 128-deep step to 16384 (8 slices of
+# 2048), ragged M and N, fp16 and bf16 activations, gelu and an in-place residual
+@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (1, 640, 128), (77, 300, 512), (128, 17, 1024),
+                                   (100, 1000, 16384), (128, 16384, 256)])
+def test_gemm_decode_paths(R, M, N, K):
+    rng = np.random.default_rng(7 * M + N + K)
+    a = W.draw(rng, (M, K), 1.0, "bf16")
+    b = W.draw(rng, (N, K), 1.0 / np.sqrt(K), "bf16")
+    r = W.draw(rng, (M, N), 1.0, "f32")
+    z = f64(a, "bf16") @ f64(b, "bf16").T
+    need = R.gemm_workspace_bytes(M, N, K)
+    assert need > 0
+    announce(f"gemm decode paths M{M} N{N} K{K} workspace {need}")
+    ad, bd = dev(a, "bf16"), dev(b, "bf16")
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = {}
+    for name, adt in (("bf16", ad), ("f16", ad.to(torch.float16))):
+        c_ws = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        c_ws2 = torch.empty_like(c_ws)
+        c_ex = torch.empty_like(c_ws)
+        for c in (c_ws, c_ws2):
+            R._check(R.LIB.msr_gemm_ws(R._ptr(adt), R._dt(adt), R._ptr(bd), R._ptr(c), R._dt(c), M, N, K, None,
+                                       R._dt(c), 0, R._ptr(ws), need, R._stream()), "msr_gemm_ws")
+        R._check(R.LIB.msr_gemm_ex(R._ptr(adt), R._dt(adt), R._ptr(bd), R._ptr(c_ex), R._dt(c_ex), M, N, K, None,
+                                   R._dt(c_ex), 0, R._stream()), "msr_gemm_ex")
+        outs[name] = (c_ws, c_ws2, c_ex)
+    # gelu + residual in place, bf16 output from an fp32 residual
+    inplace = dev(r, "f32")
+    R.gemm(ad, bd, out=inplace, gelu=True, residual=inplace, workspace=ws)
+    gbf = R.gemm(ad, bd, out_dtype=torch.bfloat16, gelu=True, residual=dev(r, "f32"), workspace=ws)
+    torch.cuda.synchronize()
+    for name, (c_ws, c_ws2, c_ex) in outs.items():
+        check(f"gemm split-K {name} A {M}x{N}x{K}", host64(c_ws), z, TOL["f32"])
+        check(f"gemm column-split {name} A {M}x{N}x{K}", host64(c_ex), z, TOL["f32"])
+        assert torch.equal(c_ws, c_ws2), "split-K result differs between two calls"
+    check(f"gemm split-K gelu+residual in place {M}x{N}x{K}", host64(inplace), oracle.gelu(z) + r, TOL["f32"])
+    check_bf16_out(f"gemm split-K gelu+residual bf16 {M}x{N}x{K}", host64(gbf), oracle.gelu(z) + r, TOL["bf16"])
+
+
+def test_gemm_ws_rejects(R):
+    M, N, K = 64, 256, 512
+    a = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((N, K), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    need = R.gemm_workspace_bytes(M, N, K)
+    ws = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    call = lambda w, n: R.LIB.msr_gemm_ws(R._ptr(a), R._dt(a), R._ptr(b), R._ptr(c), R._dt(c), M, N, K, None,
+                                          R._dt(c), 0, w, n, R._stream())
+    assert call(None, 0) == 4                                              # missing
+    assert call(R._ptr(ws), need - 4) == 4                                 # too small
+    import ctypes
+    assert call(ctypes.c_void_p(ws.data_ptr() + 16), need) == 3            # misaligned
+    assert call(R._ptr(c), need) == 1                                      # overlaps C
+    assert call(R._ptr(ws), need) == 0
+
+
 def test_gemm_block_shapes_sampled(R):
     """The block's projection shape (16384 x 4096 activations times a
     4096 -> 8192 weight); 16 sampled rows recomputed in fp64."""
