@@ -448,16 +448,32 @@ gemm_splitk_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
   }
 }
 
-template <typename TO>
+// four consecutive outputs per thread (16-byte partial loads) when M N is a
+// multiple of 4, else one
+template <typename TO, int V>
 __global__ void __launch_bounds__(256)
 gemm_splitk_reduce(const float* __restrict__ P, int ks, TO* C, int M, int N, const void* R, int r_dt, int act) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x, mn = (int64_t)M * N;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V, mn = (int64_t)M * N;
   if (e >= mn) return;
-  float v = 0.f;
-  for (int y = 0; y < ks; ++y) v += P[y * mn + e];
-  if (act) v = gelu_exact(v);
-  if (R) v += ld_residual(R, r_dt, (size_t)e);
-  C[e] = Store<TO>::cvt(v);
+  float v[V];
+#pragma unroll
+  for (int u = 0; u < V; ++u) v[u] = 0.f;
+  for (int y = 0; y < ks; ++y) {
+    if (V == 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(P + y * mn + e);
+#pragma unroll
+      for (int u = 0; u < V; ++u) v[u] += x[u];
+    } else {
+      v[0] += P[y * mn + e];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    float w = v[u];
+    if (act) w = gelu_exact(w);
+    if (R) w += ld_residual(R, r_dt, (size_t)(e + u));
+    C[e + u] = Store<TO>::cvt(w);
+  }
 }
 
 template <typename TA, typename TO>
@@ -469,8 +485,12 @@ static hipError_t launch_splitk_t(const void* A, const void* B, void* C, int M, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t mn = (int64_t)M * N;
-  hipLaunchKernelGGL((gemm_splitk_reduce<TO>), dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st, P, ks,
-                     (TO*)C, M, N, R, r_dt, act);
+  if (mn % 4 == 0)
+    hipLaunchKernelGGL((gemm_splitk_reduce<TO, 4>), dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, st, P,
+                       ks, (TO*)C, M, N, R, r_dt, act);
+  else
+    hipLaunchKernelGGL((gemm_splitk_reduce<TO, 1>), dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, st, P, ks,
+                       (TO*)C, M, N, R, r_dt, act);
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ def test_gemm(R, M, N, K):
 # M <= 128: the column-split kernel (msr_gemm_ex) and the split-K kernel with
 # a workspace (msr_gemm_ws): K from one 128-deep step to 16384 (8 slices of
 # 2048), ragged M and N, fp16 and bf16 activations, gelu and an in-place residual
-@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (1, 640, 128), (77, 300, 512), (128, 17, 1024),
+@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (1, 640, 128), (77, 300, 512), (77, 301, 512), (128, 17, 1024),
                                    (100, 1000, 16384), (128, 16384, 256)])
 def test_gemm_decode_paths(R, M, N, K):
     rng = np.random.default_rng(7 * M + N + K)
