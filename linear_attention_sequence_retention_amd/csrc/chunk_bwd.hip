@@ -44,6 +44,7 @@ namespace {
 constexpr int BT = 256;        // threads per workgroup
 constexpr int TL = 64;         // rows per tile
 constexpr int SP = TL + 8;     // pitch (elements) of a 64-column LDS slab
+constexpr int SCAN_DVB = 128; // widest column block of the state scans (128 measured ahead of 64 and 256)
 
 typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef short s16x8 __attribute__((__vector_size__(16)));
@@ -375,7 +376,11 @@ __device__ __forceinline__ float state_up(const float* smax) {
 // largest magnitude of each wave's part (for the consumers' power of two).
 // A workgroup owns rows [64 db, 64 db + 64) and columns [DVB eb, DVB eb +
 // DVB) of the state; the next two 64-row tiles are in registers while the
-// current one is multiplied.
+// current one is multiplied.  DVB = scan_dvb(d_v) columns per workgroup; each
+// of its 4 waves records one partial maximum per chunk, so a chunk's state
+// has state_nm(d_k, d_v) of them.
+__host__ __device__ constexpr int scan_dvb(int dv) { return dv < SCAN_DVB ? dv : SCAN_DVB; }
+__host__ __device__ constexpr int state_nm(int dk, int dv) { return (dk / 64) * (dv / scan_dvb(dv)) * 4; }
 template <int DVB>
 struct StateSmem {
   uint16_t As[2][TL * SP];         // weighted k' (q') rows [row][d of the block]
@@ -594,7 +599,7 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   constexpr int GP = DV + 8, ND = DK / 64, NE = DV / 64;
-  constexpr int NM = (DK / 64) * (DV / (DV < 256 ? DV : 256)) * 4;
+  constexpr int NM = state_nm(DK, DV);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
   const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
@@ -815,7 +820,7 @@ __global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   constexpr int VP = DV + 8, ND = DK / 64, NE = DV / 64;
-  constexpr int NM = (DK / 64) * (DV / (DV < 256 ? DV : 256)) * 4;
+  constexpr int NM = state_nm(DK, DV);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bi = wave >> 1, bj = wave & 1, l32 = lane & 31;
   const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
@@ -961,7 +966,7 @@ __global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   constexpr int KP = DK + 8, ND = DK / 64, NE = DV / 64;
-  constexpr int NM = (DK / 64) * (DV / (DV < 256 ? DV : 256)) * 4;
+  constexpr int NM = state_nm(DK, DV);
   // the d_v columns are split over DvSplit<DK, DV>::N workgroups of NEH 64-column blocks each
   constexpr int NEH = DvSplit<DK, DV>::NEH, NSPLIT = NE / NEH;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1105,7 +1110,7 @@ Carve carve_bwd(int b, int h, int L, int dk, int dv, int B) {
   c.rc = o; o += al256(bh * L * 4);
   c.tmax = o; o += al256(bh * (size_t)((L + TL - 1) / TL) * 4);
   c.gsc = o; o += al256(bh * 4);
-  const size_t nm = (size_t)(dk / 64) * (dv / (dv < 256 ? dv : 256)) * 4;
+  const size_t nm = (size_t)state_nm(dk, dv);
   c.rmax = o; o += al256(bh * nc * nm * 4);
   c.umax = o; o += al256(bh * nc * nm * 4);
   c.total = o;
@@ -1145,7 +1150,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t st) {
   p.umax = reinterpret_cast<float*>(w + cv.umax);
   const int bh = a.b * a.h;
   const HeadParams& hp = *a.hp;
-  constexpr int DVB = DV < 256 ? DV : 256;
+  constexpr int DVB = scan_dvb(DV);
   const dim3 tiles(bh * p.nt), sgrid(bh * (DK / 64) * (DV / DVB)), blk(BT);
   hipError_t e;
   hipLaunchKernelGGL((bwd_gmax_kernel<T, DV>), tiles, blk, 0, st, p);
