@@ -175,20 +175,31 @@ template <> struct Out2<bf16> {
   }
 };
 
+// eight 16-bit values of T (bf16 or fp16) packed in 16 bytes, as floats
+template <typename T> __device__ __forceinline__ float2 un2(uint32_t u);
+template <> __device__ __forceinline__ float2 un2<bf16>(uint32_t u) { return make_float2(lo_bf(u), hi_bf(u)); }
+template <> __device__ __forceinline__ float2 un2<half>(uint32_t u) { return make_float2(h_lo(u), h_hi(u)); }
+
 // ------------------------------------------------------------ gmax
-// the largest |dO| of each 64-row tile
+// the largest |dO| of each 64-row tile (16-byte loads: rows are 16-byte
+// aligned and d_v is a multiple of 8)
 template <typename T, int DV>
 __global__ void __launch_bounds__(BT) bwd_gmax_kernel(BwdP p) {
   const int bh = blockIdx.x / p.nt, tile = blockIdx.x % p.nt;
   const int bb = bh / p.h, hh = bh % p.h;
   const int r0 = tile * TL, nv = min(TL, p.L - r0);
   const T* g = reinterpret_cast<const T*>(p.dout) + bb * p.sdo.b + hh * p.sdo.h + r0 * p.sdo.l;
-  constexpr int VP = DV / 2;
+  constexpr int V8 = DV / 8;
   float m = 0.f;
-  for (int i = threadIdx.x; i < nv * VP; i += BT) {
-    const int r = i / VP, cp = i - r * VP;
-    const float2 y = Elem<T>::ld2(g + (int64_t)r * p.sdo.l + 2 * cp);
-    m = fmaxf(m, fmaxf(fabsf(y.x), fabsf(y.y)));
+  for (int i = threadIdx.x; i < nv * V8; i += BT) {
+    const int r = i / V8, c8 = i - r * V8;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(g + (int64_t)r * p.sdo.l + 8 * c8);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float2 y = un2<T>(w[u]);
+      m = fmaxf(m, fmaxf(fabsf(y.x), fabsf(y.y)));
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -245,13 +256,21 @@ __global__ void __launch_bounds__(BT) bwd_prep_kernel(BwdP p, HeadParams hp) {
   }
   const float down = ldexpf(1.f, -ex);
   if (tile == 0 && threadIdx.x == 0) p.gsc[bh] = ldexpf(1.f, ex);
-  constexpr int VP = DV / 2;
-  for (int i = threadIdx.x; i < nv * VP; i += BT) {
-    const int r = i / VP, cp = i - r * VP;
-    const float2 x = Elem<T>::ld2(v + (int64_t)r * p.sv.l + 2 * cp);
-    const float2 y = Elem<T>::ld2(g + (int64_t)r * p.sdo.l + 2 * cp);
-    *reinterpret_cast<uint32_t*>(p.Vb + (ro + r) * DV + 2 * cp) = pack_h2(x.x, x.y);
-    *reinterpret_cast<uint32_t*>(p.Gb + (ro + r) * DV + 2 * cp) = pack_h2(y.x * down, y.y * down);
+  constexpr int V8 = DV / 8;
+  for (int i = threadIdx.x; i < nv * V8; i += BT) {
+    const int r = i / V8, c8 = i - r * V8;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(v + (int64_t)r * p.sv.l + 8 * c8);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(g + (int64_t)r * p.sdo.l + 8 * c8);
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
+    uint32_t xo[4], yo[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float2 a = un2<T>(xw[u]), b = un2<T>(yw[u]);
+      xo[u] = pack_h2(a.x, a.y);
+      yo[u] = pack_h2(b.x * down, b.y * down);
+    }
+    *reinterpret_cast<u32x4*>(p.Vb + (ro + r) * DV + 8 * c8) = u32x4{xo[0], xo[1], xo[2], xo[3]};
+    *reinterpret_cast<u32x4*>(p.Gb + (ro + r) * DV + 8 * c8) = u32x4{yo[0], yo[1], yo[2], yo[3]};
   }
 }
 
