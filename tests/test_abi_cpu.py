@@ -211,3 +211,17 @@ def test_layer_norm_and_gemm_ex_validation(B):
     assert L.msr_gemm_workspace_bytes(129, 4096, 4096) == 0        # column-split / tiled kernels
     assert L.msr_gemm_workspace_bytes(128, 4096, 4128) == 0        # K not a multiple of 128
     assert L.msr_gemm_workspace_bytes(0, 4096, 4096) == 0
+    # msr_gemm_ws argument checks (all before any device work)
+    L.msr_gemm_ws.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_uint,
+                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.msr_gemm_ws.restype = ctypes.c_int
+    need = L.msr_gemm_workspace_bytes(64, 256, 512)
+    W = ctypes.c_void_p(0x10000000)
+    ws = lambda w, n, **kw: L.msr_gemm_ws(A, 1, Bm, C, 0, 64, 256, 512, kw.get("r"), 0, kw.get("ep", 0), w, n, None)
+    assert ws(None, 0) == 4                                        # workspace missing
+    assert ws(W, need - 1) == 4                                    # too small
+    assert ws(ctypes.c_void_p(0x10000010), need) == 3              # not 256-byte aligned
+    assert ws(ctypes.c_void_p(0x300000 - 256), need) == 1          # overlaps C
+    assert ws(W, need, ep=2) == 1                                  # unknown epilogue bit
+    assert L.msr_gemm_ws(A, 1, Bm, C, 0, 64, 256, 500, None, 0, 0, W, need, None) == 2   # K % 32
