@@ -78,15 +78,16 @@ def bwd_flops(b, h, L, dk, dv, B, score_norm):
     """Algorithmic flops of the chunkwise backward, each product counted once:
     the causal half of the intra-chunk products Q'K'^T and dO V^T, E K',
     E^T Q' and (a A)^T dO; the cross terms dO R^T (chunks >= 1), V U^T and
-    K' U (chunks before the last), q' R . dO for the clamp statistics (with
-    the score normalisation); and the two state scans K'^T (zeta V) and
-    Q'^T (w dO)."""
+    K' U (chunks before the last); and the two state scans K'^T (zeta V) and
+    Q'^T (w dO).  The score normalisation's row statistics add no product:
+    (q' R) . dO is q' . (dO R^T), a row dot product of a term dq needs anyway.
+    score_norm is kept for the signature."""
     nc = (L + B - 1) // B
     pairs = sum(min(B, L - c * B) * (min(B, L - c * B) + 1) // 2 for c in range(nc))
     intra = 2 * pairs * ((dk + dv) + (2 * dk + dv))
     rows_after_first = max(L - B, 0)
     rows_before_last = L - min(B, L - (nc - 1) * B)
-    cross = 2 * dk * dv * (rows_after_first * (2 if score_norm else 1) + 2 * rows_before_last)
+    cross = 2 * dk * dv * (rows_after_first + 2 * rows_before_last)
     states = 2 * 2 * L * dk * dv
     return b * h * (intra + cross + states)
 
