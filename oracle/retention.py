@@ -1,8 +1,8 @@
 """Plain fp64 CPU oracle for RetNet multi-scale retention.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
-execute this module: only the tests, the smoke check of the graft entry point
-and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the
+execute this module: only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the
 HIP library (no kernels, headers, tables or helpers); the only thing both sides
 share is the seeded input generator, which holds none of the method's
 arithmetic.
