@@ -62,13 +62,15 @@ gate_norm_kernel(const TY* __restrict__ y, ret_strides sy, const TG* __restrict_
   const int bb = (int)(bt / L);
   const TY* yp = y + bb * sy.b + hh * sy.h + (int64_t)t * sy.l;
   const int64_t row = gi * dv;   // offset of this group in G and Z
-  float x[NI][8];
+  // the gate is requested with y, so its latency overlaps the two reductions
+  float x[NI][8], gg[NI][8];
   float sum = 0.f;
 #pragma unroll
   for (int it = 0; it < NI; ++it) {
     const int e = 8 * lane + 512 * it;
     if (e < dv) {
       Vec8<TY>::ld(yp + e, x[it]);
+      Vec8<TG>::ld(g + row + e, gg[it]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) sum += x[it][j];
     }
@@ -92,15 +94,14 @@ gate_norm_kernel(const TY* __restrict__ y, ret_strides sy, const TG* __restrict_
   for (int it = 0; it < NI; ++it) {
     const int e = 8 * lane + 512 * it;
     if (e < dv) {
-      float gg[8], r[8];
-      Vec8<TG>::ld(g + row + e, gg);
+      float r[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float yn = (x[it][j] - mean) * rstd;
         const int c = hh * dv + e + j;
         if (w) yn *= w[c];
         if (bias) yn += bias[c];
-        const float sw = gg[j] / (1.f + __expf(-gg[j]));
+        const float sw = gg[it][j] / (1.f + __expf(-gg[it][j]));
         r[j] = sw * yn;
       }
       Vec8<TO>::st(out + row + e, r);
