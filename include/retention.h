@@ -90,8 +90,13 @@ typedef struct { int64_t b, h, l; } ret_strides;   /* element strides of a [b,h,
  *          written); state_out may equal state_in
  *   z_in / z_out  device float32 [b,h,d_k] key-sums or NULL (same rules);
  *          a continued sequence with RET_NORM_SCORE needs z_in
- *   workspace  device scratch of retention_chunkwise_workspace_bytes() bytes
- *          (may be NULL when that size is 0)
+ *   workspace  device scratch of retention_chunkwise_workspace_bytes() bytes,
+ *          256-byte aligned, overlapping none of q, k, v, o and the state /
+ *          key-sum buffers; its contents on entry do not matter.  It may be
+ *          NULL when that size is 0, and for shapes served by the fused kernel
+ *          (those the large-chunk kernels do not take) unless z_out overlaps
+ *          z_in, where it holds a snapshot of z_in.  Calls sharing a
+ *          workspace must be ordered (one stream, or events).
  * Supported: in_dt bf16 with (d_k, d_v) in {(32,32), (64,64), (128,128),
  * (128,256), (256,256), (256,512)}; in_dt f16 with (d_k, d_v) in
  * {(128,256), (256,512)}; in_dt f32 with (d_k, d_v) in {(32,32), (64,64)};
@@ -141,7 +146,7 @@ size_t retention_parallel_workspace_bytes(int b, int h, int L, int d_k, int d_v,
 
 /*
  * retention_chunkwise_bwd -- gradients of retention_chunkwise_fwd for a fresh
- * sequence (the training path of [notes] §四, chunkwise as in §2.4):
+ * sequence (the training path of [notes] §三.5 and §四.3, chunkwise as in §2.4):
  * given g = dL/dO, writes dq = dL/dq, dk = dL/dk, dv = dL/dv of
  *   o_p = s_p num_p / n_p,  num_p = sum_{m<=p} A_pm v_m,
  *   A_pm = (q'_p . k'_m) gamma^(p-m),  n_p = max(|s_p sum_m A_pm|, 1)
@@ -232,8 +237,16 @@ int msr_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_
              hipStream_t stream);
 
 /*
+ * msr_gemm_bf16 -- msr_gemm for bf16 activations: C = A . B^T with A and B
+ * both bf16 ([notes] §三.2 and §2.1, the block's projections).  A thin call
+ * of msr_gemm with a_dt = RET_BF16; arguments, layouts (B is the weight as
+ * [N][K] = [out_features][in_features]) and errors as msr_gemm.
+ */
+int msr_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K, ret_dtype c_dt, hipStream_t stream);
+
+/*
  * msr_gemm_ex -- msr_gemm with an epilogue, for the RetNet layer ([notes]
- * §四.4: Y = MSR(LN(X)) + X, X' = FFN(LN(Y)) + Y, FFN(X) = gelu(X W_1) W_2):
+ * §三.4: Y = MSR(LN(X)) + X, X' = FFN(LN(Y)) + Y, FFN(X) = gelu(X W_1) W_2):
  *   C = act(A . B^T) (+ residual)
  *   epilogue   MSR_GEMM_GELU applies the exact gelu x Phi(x) = x (1 +
  *              erf(x / sqrt 2)) / 2 to each fp32 output (FFN's first
@@ -253,7 +266,7 @@ int msr_gemm_ex(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype
 /*
  * msr_gemm_ws -- msr_gemm_ex with a caller-provided workspace, for the
  * projections of a decode step (one token per sequence, M <= 128 rows; the
- * same products as msr_gemm_ex, [notes] §三.2 and §四.4).  With M <= 128 and
+ * same products as msr_gemm_ex, [notes] §三.2 and §三.4).  With M <= 128 and
  * K a multiple of 128 the columns are taken 128 per workgroup and K is split
  * into up to 8 slices whose fp32 partial products go to the workspace; a
  * second kernel sums them in slice order (the result does not depend on
@@ -273,7 +286,7 @@ int msr_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype
                 hipStream_t stream);
 
 /*
- * ret_layer_norm -- the LayerNorm of the RetNet layer ([notes] §四.4):
+ * ret_layer_norm -- the LayerNorm of the RetNet layer ([notes] §三.4):
  *   y = (x - mean) / sqrt(biased variance + eps) over each row, then the
  *   optional per-channel affine
  *   x  device [rows][d] row-major of x_dt (f32, bf16 or f16)

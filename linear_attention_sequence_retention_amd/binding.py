@@ -8,6 +8,7 @@ the library's HIP kernels.  There is no fallback: if the library is missing
 the import fails.
 """
 import ctypes
+import functools
 import os
 
 import numpy as np
@@ -49,6 +50,8 @@ def load_library(path=LIB_PATH):
     lib.msr_gate_norm.restype = i32
     lib.msr_gemm.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp]
     lib.msr_gemm.restype = i32
+    lib.msr_gemm_bf16.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp]
+    lib.msr_gemm_bf16.restype = i32
     lib.retention_parallel_fwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides,
                                            i32, i32, i32, i32, i32, dp, dp, i64, u32, i32, i32, vp, sz, vp]
     lib.retention_parallel_fwd.restype = i32
@@ -275,8 +278,6 @@ def gemm(a, b_nk, out=None, out_dtype=torch.bfloat16, residual=None, gelu=False,
     if need > 0:
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
-            if stream is not None:
-                workspace.record_stream(stream)
         st = LIB.msr_gemm_ws(_ptr(a), _dt(a), _ptr(b_nk), _ptr(out), _dt(out), M, N, K, _ptr(residual),
                              _dt(out if residual is None else residual), 1 if gelu else 0,
                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
@@ -293,7 +294,7 @@ def gemm(a, b_nk, out=None, out_dtype=torch.bfloat16, residual=None, gelu=False,
 
 
 def layer_norm(x, eps, weight=None, bias=None, out=None, out_dtype=None, stream=None):
-    """LayerNorm over the last axis (RetNet reading notes, §四.4): biased
+    """LayerNorm over the last axis (RetNet reading notes, §三.4): biased
     variance, eps under the square root, optional float32 affine."""
     if not x.is_contiguous():
         raise ValueError("layer_norm needs a contiguous input")
@@ -355,7 +356,7 @@ def msr_block_fwd(x, wq_t, wk_t, wv_t, wg_t, wo_t, gamma, theta, chunk, flags, e
 
 def retnet_layer_fwd(x, msr_w_t, w1_t, w2_t, gamma, theta, chunk, flags, gn_eps, ln_eps, ln1=(None, None),
                      ln2=(None, None), pos0=0, n_prev=0, state=None, state_out=None, out_dtype=None, stream=None):
-    """One RetNet layer forward (reading notes §四.4):
+    """One RetNet layer forward (reading notes §三.4):
         Y = MSR(LN(X)) + X,   X' = FFN(LN(Y)) + Y,   FFN(Y) = gelu(Y W_1) W_2.
 
     x: [b, L, d_model] float32 or bf16; the result has x's dtype (or out_dtype);
@@ -390,7 +391,7 @@ def new_states(n_layers, b, h, d_k, d_v, device="cuda"):
 
 def retnet_stack_fwd(x, layers, gamma, theta, chunk, flags, gn_eps, ln_eps, pos0=0, n_prev=0, states=None,
                      states_out=None, stream=None):
-    """A stack of RetNet layers (reading notes §四.4) over a sequence, the MSR
+    """A stack of RetNet layers (reading notes §三.4) over a sequence, the MSR
     heads in the chunkwise form.  layers: (msr_w_t, w1_t, w2_t, ln1, ln2) per
     layer as in retnet_layer_fwd; states: per-layer (S, z) to continue from;
     states_out: per-layer (S, z) buffers receiving the final states (a
@@ -408,7 +409,7 @@ def retnet_stack_fwd(x, layers, gamma, theta, chunk, flags, gn_eps, ln_eps, pos0
 
 def retnet_decode_step(x, layers, states, gamma, theta, pos, n_tokens, flags, gn_eps, ln_eps, stream=None):
     """One token per sequence through a stack of RetNet layers, each layer's
-    MSR in the recurrent form (reading notes §2.2, §四.4).
+    MSR in the recurrent form (reading notes §2.2, §三.4).
 
     x: [b, d_model] float32 or bf16 (the result has its dtype); states: the
     layers' (S, z), updated in place; pos: the token's position (xPos phase);
@@ -440,3 +441,23 @@ def retnet_decode_step(x, layers, states, gamma, theta, pos, n_tokens, flags, gn
         x = gemm(H, w2, out_dtype=final_dtype if li == len(layers) - 1 else torch.float32, residual=Y,
                  stream=stream)
     return x
+
+
+def _on_stream(fn):
+    """Run fn with ``stream`` as torch's current stream.  Every tensor the
+    wrapper allocates (outputs, workspaces, intermediates) then belongs to the
+    stream its kernels run on, so torch's caching allocator cannot hand the
+    memory to another stream while those kernels still use it."""
+    @functools.wraps(fn)
+    def run(*args, stream=None, **kw):
+        if stream is None or stream == torch.cuda.current_stream(stream.device):
+            return fn(*args, stream=None, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=None, **kw)
+    return run
+
+
+for _name in ("chunkwise_fwd", "parallel_fwd", "chunkwise_bwd", "recurrent_step", "gate_norm", "gemm",
+              "layer_norm", "msr_block_fwd", "retnet_layer_fwd", "retnet_stack_fwd", "retnet_decode_step"):
+    globals()[_name] = _on_stream(globals()[_name])
+del _name

@@ -57,6 +57,16 @@ int check_view(const char* name, const void* p, ret_strides s, size_t esz) {
   return RET_OK;
 }
 
+// bytes from the first to one past the last element of a [b,h,L,d] view
+size_t view_span(ret_strides s, int b, int h, int L, int d, size_t esz) {
+  return ((size_t)(b - 1) * s.b + (size_t)(h - 1) * s.h + (size_t)(L - 1) * s.l + d) * esz;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return a && b && x < y + nb && y < x + na;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(RET_E_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -117,9 +127,22 @@ int retention_chunkwise_fwd(const void* q, ret_strides sq, const void* k, ret_st
   if (!ret::chunkwise_supported(in_dt, d_k, d_v))
     return fail(RET_E_UNSUPPORTED, "no chunkwise kernel for in_dt=%s d_k=%d d_v=%d",
                 in_dt == RET_BF16 ? "bf16" : (in_dt == RET_F16 ? "f16" : "f32"), d_k, d_v);
-  const size_t need = ret::chunkwise_workspace(b, h, L, d_k, d_v, chunk_B, flags);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(RET_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : 0);
+  size_t need = ret::chunkwise_workspace(b, h, L, d_k, d_v, chunk_B, flags);
+  const size_t zb = (size_t)b * h * d_k * sizeof(float), sb = zb * d_v;
+  if (!ret::three_phase_applies(in_dt, d_k, d_v, chunk_B) && !overlaps(z_in, zb, z_out, zb))
+    need = 0;   // the fused kernel uses its workspace only for a key-sum snapshot
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(RET_E_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : 0);
+    if (!aligned(workspace, 256)) return fail(RET_E_ALIGN, "workspace must be 256-byte aligned");
+    if (overlaps(workspace, need, q, view_span(sq, b, h, L, d_k, ie)) ||
+        overlaps(workspace, need, k, view_span(sk, b, h, L, d_k, ie)) ||
+        overlaps(workspace, need, v, view_span(sv, b, h, L, d_v, ie)) ||
+        overlaps(workspace, need, o, view_span(so, b, h, L, d_v, oe)) || overlaps(workspace, need, state_in, sb) ||
+        overlaps(workspace, need, state_out, sb) || overlaps(workspace, need, z_in, zb) ||
+        overlaps(workspace, need, z_out, zb))
+      return fail(RET_E_INVAL, "workspace must not overlap q, k, v, o or the state buffers");
+  }
 
   ret::HeadParams hp;
   fill_params(hp, gamma, h, theta, d_k, flags);
@@ -306,11 +329,6 @@ size_t msr_gemm_workspace_bytes(int M, int N, int K) {
   return ret::gemm_workspace_bytes(M, N, K);
 }
 
-static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return a && b && x < y + nb && y < x + na;
-}
-
 int msr_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
                 const void* residual, ret_dtype r_dt, unsigned epilogue, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
@@ -334,6 +352,10 @@ int msr_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype
 int msr_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
              hipStream_t stream) {
   return msr_gemm_ex(A, a_dt, B, C, c_dt, M, N, K, nullptr, c_dt, 0u, stream);
+}
+
+int msr_gemm_bf16(const void* A, const void* B, void* C, int M, int N, int K, ret_dtype c_dt, hipStream_t stream) {
+  return msr_gemm(A, RET_BF16, B, C, c_dt, M, N, K, stream);
 }
 
 int ret_layer_norm(const void* x, void* y, int rows, int d, const float* weight, const float* bias, float eps,

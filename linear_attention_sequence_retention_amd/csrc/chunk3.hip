@@ -246,11 +246,14 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   auto issue = [&](int kt) {
     const int k0 = kt * TK;
     const int kvalid = min(TK, Bc - k0);
+    // 64-bit tile origin; offsets inside a 64-key tile fit 32 bits (strides < 2^25)
+    const T* Kt = Kg + (int64_t)k0 * p.sk.l;
+    const T* Vt = Vg + (int64_t)k0 * p.sv.l;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kc = min(kq + i, kvalid - 1);
-      kr[i] = *reinterpret_cast<const u32x4*>(Kg + (uint32_t)((k0 + kc) * (int)p.sk.l + 8 * cq));
-      vr[i] = *reinterpret_cast<const u32x4*>(Vg + (uint32_t)((k0 + kc) * (int)p.sv.l + 8 * cq));
+      kr[i] = *reinterpret_cast<const u32x4*>(Kt + (uint32_t)(kc * (int)p.sk.l + 8 * cq));
+      vr[i] = *reinterpret_cast<const u32x4*>(Vt + (uint32_t)(kc * (int)p.sv.l + 8 * cq));
     }
   };
   // transposed-read origin of this lane (see lds_read_tr16): key 8 (lane / 32)
@@ -897,11 +900,12 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     auto issue_v = [&](int kt) {
       const int k0 = kt * TK;
       const int kvalid = min(TK, Bc - k0);
+      const T* Vt = Vg + (int64_t)k0 * p.sv.l;       // offsets inside the tile fit 32 bits
   #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int e = tid + i * NT3;
         const int key = min(e >> 6, kvalid - 1), piece = e & 63;
-        vreg[i] = *reinterpret_cast<const u32x4*>(Vg + (uint32_t)((k0 + key) * (int)p.sv.l + piece * 8));
+        vreg[i] = *reinterpret_cast<const u32x4*>(Vt + (uint32_t)(key * (int)p.sv.l + piece * 8));
       }
     };
     auto commit_k = [&](int kt) {

@@ -522,6 +522,12 @@ __global__ void __launch_bounds__(NT, 1) chunkwise_kernel(KParams p, HeadParams 
   }
   if (p.z_out && slice == 0 && !score_wave && zd < DK) p.z_out[(int64_t)bh * DK + zd] = zreg;
 }
+// n floats from src to dst (the key-sum snapshot of an in-place continuation)
+__global__ void __launch_bounds__(256) copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
 template <typename T, typename TO, int DK, int DV, int SV>
 static hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
   static_assert(DK / 2 <= NT, "pairs per row exceed the workgroup");
@@ -533,6 +539,15 @@ static hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
   p.h = a.h; p.L = a.L; p.B = a.B; p.nslice = DV / SV;
   p.pos0 = a.pos0; p.n_prev = a.n_prev; p.flags = a.flags;
   p.state_in = a.state_in; p.z_in = a.z_in; p.state_out = a.state_out; p.z_out = a.z_out;
+  if (fused_z_snapshot(a)) {
+    // every d_v slice of a head reads z_in, and slice 0 writes z_out when it
+    // ends: with z_out over z_in, a slice that starts after its head's slice 0
+    // has finished would read the new key-sum.  The slices read a copy.
+    const int n = a.b * a.h * a.dk;
+    float* snap = static_cast<float*>(a.ws);
+    hipLaunchKernelGGL(copy_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a.z_in, snap, n);
+    p.z_in = snap;
+  }
   const size_t sh = sizeof(Smem<typename OpOf<T>::type, DK, SV>);
   auto kern = chunkwise_kernel<T, TO, DK, DV, SV>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
@@ -576,8 +591,17 @@ bool chunkwise_supported(ret_dtype in_dt, int dk, int dv) {
 
 size_t chunkwise_workspace(int b, int h, int L, int dk, int dv, int B, unsigned) {
   // the workspace query has no dtype: the large-chunk path serves bf16 / f16
-  // inputs, and no f32 kernel exists for its shape
-  return three_phase_applies(RET_BF16, dk, dv, B) ? three_phase_workspace(b, h, L, B) : 0;
+  // inputs, and no f32 kernel exists for its shape.  The fused kernel needs
+  // room for a snapshot of the key-sums (used only when z_out overlaps z_in).
+  if (three_phase_applies(RET_BF16, dk, dv, B)) return three_phase_workspace(b, h, L, B);
+  return ((size_t)b * h * dk * sizeof(float) + 255) & ~(size_t)255;
+}
+
+bool fused_z_snapshot(const ChunkArgs& a) {
+  if (three_phase_applies(a.in_dt, a.dk, a.dv, a.B) || !a.z_in || !a.z_out) return false;
+  const size_t n = (size_t)a.b * a.h * a.dk * sizeof(float);
+  const uintptr_t x = (uintptr_t)a.z_in, y = (uintptr_t)a.z_out;
+  return x < y + n && y < x + n;
 }
 
 hipError_t launch_chunkwise(const ChunkArgs& a, hipStream_t st, bool* supported) {

@@ -138,7 +138,7 @@ static hipError_t launch_gn_g(const GateArgs& a, hipStream_t st) {
   return launch_gn_o<TY, float>(a, st);
 }
 // ---------------------------------------------------------------- LayerNorm
-// The two LayerNorms of the RetNet layer (reading notes §四.4: Y = MSR(LN(X))
+// The two LayerNorms of the RetNet layer (reading notes §三.4: Y = MSR(LN(X))
 // + X, X' = FFN(LN(Y)) + Y): each row of d values (one token) is normalised by
 // its mean and biased variance (eps added to the variance), then the optional
 // per-channel affine.  One wave per row, the row in registers (8 values per

@@ -18,7 +18,7 @@
 // is used instead, or, when the caller brings a workspace, a split-K kernel
 // with the activation rows staged in LDS (below).
 //
-// Epilogue options (the RetNet layer, reading notes §四.4): the exact gelu
+// Epilogue options (the RetNet layer, reading notes §三.4): the exact gelu
 // x Phi(x) of each output (FFN's first projection), then the addition of a
 // residual (the layer's two residual connections) stored as fp32, bf16 or
 // fp16 independently of the output, so that an fp32 residual stream can feed

@@ -74,6 +74,9 @@ struct ChunkArgs {
 hipError_t launch_chunkwise(const ChunkArgs& a, hipStream_t st, bool* supported);
 bool chunkwise_supported(ret_dtype in_dt, int dk, int dv);
 size_t chunkwise_workspace(int b, int h, int L, int dk, int dv, int B, unsigned flags);
+// true when the call takes the fused kernel with z_out overlapping z_in: the
+// key-sums are then read from a snapshot in the workspace
+bool fused_z_snapshot(const ChunkArgs& a);
 // large-chunk path (delta / scan / output kernels)
 bool three_phase_applies(ret_dtype in_dt, int dk, int dv, int B);
 size_t three_phase_workspace(int b, int h, int L, int B);

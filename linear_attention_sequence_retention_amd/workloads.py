@@ -91,7 +91,7 @@ DECODE = dict(b=128, h=16, dk=256, dv=512, s0_sigma=0.1, sigma=1.0 / 16,
 BLOCK = dict(b=2, L=8192, d_model=4096, h=16, dk=256, dv=512, x_sigma=1.0,
              w_sigma=0.02, chunk=512, flags=XPOS | NORM_ALL, eps=1e-5)
 
-# One RetNet layer (reading notes §四.4) around the block workload: the FFN
+# One RetNet layer (reading notes §三.4) around the block workload: the FFN
 # width is not stated there; the one width the pages print is the hotelren.com
 # article's example model (§5.1: hidden 768, FFN 3072), i.e. 4 x d_model.
 LAYER = dict(BLOCK, d_ff=4 * BLOCK['d_model'], ln_eps=1e-5, ln_sigma=0.1)

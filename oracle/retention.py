@@ -15,7 +15,7 @@ next to the code.  Sources (page title, section):
 * RetNet reading notes (mzeromiko.github.io, "阅读笔记：RetNet"):
   §2.1 architecture motivation (the complex-phase derivation),
   §2.2 recurrent mode, §2.3 parallel mode, §2.4 chunkwise recurrent mode,
-  §三.2 MSR module, §三.3 normalisation, §四.4 single-layer structure
+  §三.2 MSR module, §三.3 normalisation, §三.4 single-layer structure
   (LN, residuals and the gelu FFN around the MSR module; layers stacked).
 * zyxy.net lecture ("RetNet（Retentive Network）：多尺度指数衰减…"), §5
   multi-scale grouping: the head split of d_model into contiguous column
@@ -35,7 +35,7 @@ under tests/ that start with ``test_oracle``.  Readings that are choices
 rather than facts of the pages ("parity unpinned" by the pages themselves):
 the real xPos layout (interleaved pairs, both q and k rotated by +p*theta),
 GroupNorm epsilon and affine, the meaning of sigma in N(0, sigma), and for
-the layer of §四.4 the LayerNorm variant (biased variance, eps, affine), the
+the layer of §三.4 the LayerNorm variant (biased variance, eps, affine), the
 exact gelu x Phi(x), and the FFN width (a parameter).
 """
 
@@ -236,7 +236,7 @@ def retention_chunkwise(q, k, v, gamma, theta, flags, chunk, pos0=0, n_prev=0,
 def retention_parallel_bwd(q, k, v, do, gamma, theta, flags, pos0=0):
     """Gradients dL/dq, dL/dk, dL/dv of the normalised retention of a fresh
     sequence, given dL/dO (the chunkwise backward's definition: the training
-    path of §四 differentiates the forward of §2.3 with §三.3's normalisers).
+    path of §三.5 and §四.3 differentiates the forward of §2.3 with §三.3's normalisers).
 
     Written out on the parallel form: with q', k' the rotated inputs,
       A_pm   = (q'_p . k'_m) gamma^(p-m)  for m <= p         (unscaled scores)
@@ -380,7 +380,7 @@ def msr_forward(X, WQ, WK, WV, WG, WO, h, theta, flags, chunk, eps, pos0=0, n_pr
 
 
 # ---------------------------------------------------------------------------
-# One RetNet layer (reading notes §四.4, the single-layer structure):
+# One RetNet layer (reading notes §三.4, the single-layer structure):
 #   Y = MSR(LN(X)) + X,   X' = FFN(LN(Y)) + Y,   FFN(X) = gelu(X W_1) W_2
 # The page names LN and gelu without their variants; the readings taken are
 # LayerNorm over the model width with the biased variance, eps under the
@@ -399,7 +399,7 @@ def _erf(x):
 
 def layer_norm(x, eps, weight=None, bias=None):
     """LN over the last axis (d_model): (x - mean) / sqrt(biased var + eps),
-    then the optional per-channel affine (§四.4; variant: see above)."""
+    then the optional per-channel affine (§三.4; variant: see above)."""
     x = _f64(x)
     mu = x.mean(axis=-1, keepdims=True)
     var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
@@ -412,19 +412,19 @@ def layer_norm(x, eps, weight=None, bias=None):
 
 
 def gelu(x):
-    """gelu(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2 (§四.4, exact form)."""
+    """gelu(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2 (§三.4, exact form)."""
     x = _f64(x)
     return 0.5 * x * (1.0 + _erf(x / np.sqrt(2.0)))
 
 
 def ffn(X, W1, W2):
-    """FFN(X) = gelu(X W_1) W_2 (§四.4).  W_1: [d_model, d_ff], W_2: [d_ff, d_model]."""
+    """FFN(X) = gelu(X W_1) W_2 (§三.4).  W_1: [d_model, d_ff], W_2: [d_ff, d_model]."""
     return gelu(_f64(X) @ _f64(W1)) @ _f64(W2)
 
 
 def retnet_layer(X, msr_w, W1, W2, h, theta, flags, chunk, gn_eps, ln_eps,
                  ln1=(None, None), ln2=(None, None), pos0=0, n_prev=0, state=None, return_state=False):
-    """One RetNet layer (§四.4): Y = MSR(LN(X)) + X;  X' = FFN(LN(Y)) + Y.
+    """One RetNet layer (§三.4): Y = MSR(LN(X)) + X;  X' = FFN(LN(Y)) + Y.
 
     msr_w = (W_Q, W_K, W_V, W_G, W_O) as in msr_forward; ln1 / ln2 are the
     (weight, bias) of the two LayerNorms (None = 1 and 0).  Returns X' of the
@@ -440,7 +440,7 @@ def retnet_layer(X, msr_w, W1, W2, h, theta, flags, chunk, gn_eps, ln_eps,
 
 # ---------------------------------------------------------------------------
 # A stack of layers and its token-by-token decode.  The model stacks identical
-# layers (§四.4); decoding runs each layer's MSR in the recurrent form (§2.2),
+# layers (§三.4); decoding runs each layer's MSR in the recurrent form (§2.2),
 # one token at a time, each layer carrying its own heads' state (S, z):
 # [b,h,dk,dv] and [b,h,dk].  A layer's parameters are the tuple
 # (msr_w, W1, W2, ln1, ln2) of retnet_layer.

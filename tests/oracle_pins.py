@@ -398,6 +398,29 @@ def pin_block(m):
     ynorm = (out2 @ WO2.T / gate).reshape(b, L, h, dv)
     assert np.max(np.abs(ynorm.mean(-1))) < 1e-12
     assert np.max(np.abs((ynorm ** 2).mean(-1) - 1.0)) < 1e-10
+    # hand-assembled block: per head, the projections taken column block by
+    # column block, the brute-force parallel form (a separate, separately
+    # pinned path), GroupNorm written out as the group mean and biased
+    # variance, then swish(X W_G) times the normalised heads, then W_O
+    eps = 1e-5
+    hand = np.zeros((b, L, dm))
+    Yn = np.zeros((b, L, h * dv))
+    for i in range(h):
+        qi = X @ WQ[:, i * dk:(i + 1) * dk]
+        ki = X @ WK[:, i * dk:(i + 1) * dk]
+        vi = X @ WV[:, i * dv:(i + 1) * dv]
+        oi = m.retention_parallel(qi[:, None], ki[:, None], vi[:, None], m.gammas(h)[i:i + 1], th, flags)[:, 0]
+        for bb in range(b):
+            for t in range(L):
+                row = oi[bb, t]
+                mu = sum(row) / dv
+                var = sum((x - mu) ** 2 for x in row) / dv
+                Yn[bb, t, i * dv:(i + 1) * dv] = (row - mu) / np.sqrt(var + eps)
+    G = X @ WG
+    hand = (G / (1.0 + np.exp(-G)) * Yn) @ WO
+    _close(m.msr_forward(X, WQ, WK, WV, WG, WO, h, th, flags, 5, eps), hand, 1e-10, "block vs hand-assembled")
+    swapped = m.msr_forward(X, WK, WQ, WV, WG, WO, h, th, flags, 5, eps)
+    assert np.max(np.abs(swapped - hand)) > 1e-3 * np.max(np.abs(hand)), "W_Q / W_K swap not visible"
     # split_heads: column c of head i is input column i*d + c
     x = np.arange(2 * 3 * 8, dtype=np.float64).reshape(2, 3, 8)
     s = m.split_heads(x, 2)
@@ -436,7 +459,7 @@ def pin_pages_shape_example(m):
 
 
 def pin_layer_norm(m):
-    """LayerNorm of the RetNet layer (§四.4): [1,2,3,4] has mean 2.5 and biased
+    """LayerNorm of the RetNet layer (§三.4): [1,2,3,4] has mean 2.5 and biased
     variance 1.25, so it maps to [-3,-1,1,3]/sqrt(5); rows are independent; eps
     enters under the square root; the affine is per channel; and LN(a x + c) =
     LN(x) for a > 0."""
@@ -457,7 +480,7 @@ def pin_gelu(m):
     gelu(1) = Phi(1) = 0.8413447460685429, gelu(-1) = -(1 - Phi(1)),
     gelu(2) = 2 Phi(2) = 2 * 0.9772498680518208 (textbook values of Phi);
     gelu(x) - gelu(-x) = x since Phi(x) + Phi(-x) = 1; gelu(40) = 40,
-    gelu(-40) = 0.  FFN with identity weights is gelu itself (§四.4)."""
+    gelu(-40) = 0.  FFN with identity weights is gelu itself (§三.4)."""
     g = m.gelu(np.array([0.0, 1.0, -1.0, 2.0, 40.0, -40.0]))
     assert g[0] == 0.0
     assert abs(g[1] - 0.8413447460685429) < 1e-15
@@ -476,7 +499,7 @@ def pin_gelu(m):
 
 
 def pin_retnet_layer(m):
-    """One RetNet layer (§四.4), Y = MSR(LN(X)) + X, X' = FFN(LN(Y)) + Y:
+    """One RetNet layer (§三.4), Y = MSR(LN(X)) + X, X' = FFN(LN(Y)) + Y:
     zero W_O and W_2 give X' = X; with W_2 = 0, X' - X = MSR(LN(X)) is
     unchanged by a positive rescaling of X (LN sits before MSR); with W_O = 0
     the same holds for the FFN branch; X' - Y is linear in W_2; and token t
@@ -520,7 +543,7 @@ def _stack_params(r, n_layers, dm, h, dk, dv, dff):
 
 
 def pin_stack_decode(m):
-    """A stack of layers (§四.4) decoded token by token in the recurrent form
+    """A stack of layers (§三.4) decoded token by token in the recurrent form
     (§2.2, each layer carrying its own (S, z)) equals the chunkwise forward
     of the stack at every position; a chunkwise prefill handing each layer's
     state to the decode continues the same sequence; the final states agree.

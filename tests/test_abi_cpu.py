@@ -137,8 +137,47 @@ def test_gemm_validation(B):
 
 
 def test_workspace_query(B):
-    assert B.LIB.retention_chunkwise_workspace_bytes(1, 2, 128, 32, 32, 64, 15) == 0
+    # the fused kernel's workspace: a key-sum snapshot, 256-byte rounded
+    assert B.LIB.retention_chunkwise_workspace_bytes(1, 2, 128, 32, 32, 64, 15) == 256
     assert B.LIB.retention_chunkwise_workspace_bytes(0, 2, 128, 32, 32, 64, 15) == 0
+    assert B.LIB.retention_chunkwise_workspace_bytes(1, 2, 1024, 256, 512, 512, 15) > 1 << 20
+
+
+def test_chunkwise_workspace_checks(B):
+    """The large-chunk kernels' workspace: missing, too small, misaligned, or
+    overlapping an input; the fused kernel's only when z_out overlaps z_in."""
+    b, h, L, dk, dv, chunk = 1, 2, 512, 256, 512, 512
+    sk_ = B.Strides(h * L * dk, L * dk, dk)
+    sv_ = B.Strides(h * L * dv, L * dv, dv)
+    q, k, v, o = (ctypes.c_void_p(a) for a in (0x10000000, 0x20000000, 0x30000000, 0x40000000))
+    need = B.LIB.retention_chunkwise_workspace_bytes(b, h, L, dk, dv, chunk, 15)
+    assert need > 0
+    kw = dict(q=q, sq=sk_, k=k, sk=sk_, v=v, sv=sv_, o=o, so=sv_, b=b, h=h, L=L, dk=dk, dv=dv, chunk=chunk)
+    st, err = _chunk(B, **kw, ws=None, wsb=0)
+    assert st == 4 and "workspace" in err
+    st, err = _chunk(B, **kw, ws=ctypes.c_void_p(0x50000000), wsb=need - 1)
+    assert st == 4
+    st, err = _chunk(B, **kw, ws=ctypes.c_void_p(0x50000010), wsb=need)
+    assert st == 3 and "256-byte" in err
+    st, err = _chunk(B, **kw, ws=ctypes.c_void_p(0x10000000 + 4096), wsb=need)
+    assert st == 1 and "overlap" in err
+    st, err = _chunk(B, **kw, ws=ctypes.c_void_p(0x40000000 - need + 256), wsb=need)
+    assert st == 1 and "overlap" in err
+    # fused kernel: z_out over z_in needs the snapshot room
+    z = ctypes.c_void_p(0x60000000)
+    st, err = _chunk(B, z_in=z, z_out=z, ws=None, wsb=0)
+    assert st == 4 and "workspace" in err
+    st, err = _chunk(B, z_in=z, z_out=z, ws=ctypes.c_void_p(0x60000000), wsb=256)
+    assert st == 1 and "overlap" in err
+
+
+def test_gemm_bf16_validation(B):
+    L = B.LIB
+    A, Bm, C = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    assert L.msr_gemm_bf16(A, Bm, C, 16, 16, 48, 1, None) == 2        # K % 32
+    assert L.msr_gemm_bf16(A, Bm, A, 16, 16, 64, 1, None) == 1        # alias
+    assert L.msr_gemm_bf16(A, Bm, C, 16, 16, 64, 7, None) == 1        # bad dtype
+    assert L.msr_gemm_bf16(FAKE_MIS, Bm, C, 16, 16, 64, 1, None) == 3
 
 
 def _bwd(B, **kw):

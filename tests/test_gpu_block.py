@@ -133,9 +133,34 @@ def test_block_small(R):
     _block_case(R, 2, 300, 256, 2, 128, 256, 64, seed=1)
 
 
-def test_block_full_shape_prefix(R):
+def test_block_full_shape(R):
     """The full block workload (batch 2, 8192 tokens, d_model 4096, 16 heads
-    of 256 / 512, chunk 512); the oracle recomputes batch 0's first 1024
-    tokens, which by causality depend on nothing later."""
+    of 256 / 512, chunk 512) in fp32 output; the oracle recomputes all 8192
+    tokens of batch 0 (every chunk, so every state hand-off between chunks)
+    and the plain bar max|err| <= 2e-2 RMS(oracle) applies."""
     c = W.BLOCK
-    _block_case(R, c["b"], c["L"], c["d_model"], c["h"], c["dk"], c["dv"], c["chunk"], seed=0, check_tokens=1024)
+    _block_case(R, c["b"], c["L"], c["d_model"], c["h"], c["dk"], c["dv"], c["chunk"], seed=0)
+
+
+def test_block_side_stream(R):
+    """The block on a side stream while the default stream allocates and
+    writes new tensors: the wrapper's intermediates belong to the side
+    stream, so the result equals the default-stream run bit for bit."""
+    cfg = dict(b=2, L=600, d_model=512, h=2, dk=128, dv=256, x_sigma=1.0, w_sigma=0.02)
+    X, WQ, WK, WV, WG, WO = W.block_inputs(**cfg, seed=11)
+    th = W.theta_vector(cfg["dk"])
+    flags = W.XPOS | W.NORM_ALL
+    dT = lambda w: dev(np.ascontiguousarray(w.T), "bf16")
+    args = (dev(X, "bf16"), dT(WQ), dT(WK), dT(WV), dT(WG), dT(WO), W.gamma_vector(cfg["h"]), th, 128, flags, 1e-5)
+    announce("msr block on a side stream")
+    ref = R.msr_block_fwd(*args, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        out = R.msr_block_fwd(*args, out_dtype=torch.float32, stream=side)
+        junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(64)]
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "side-stream result differs"
+        del junk

@@ -1,4 +1,4 @@
-"""Parity of the RetNet layer pieces (reading notes §四.4) with the fp64
+"""Parity of the RetNet layer pieces (reading notes §三.4) with the fp64
 oracle: the LayerNorm kernel, the GEMM's gelu / residual epilogue, and the
 whole layer Y = MSR(LN(X)) + X, X' = FFN(LN(Y)) + Y composed from library
 calls."""

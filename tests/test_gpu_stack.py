@@ -1,4 +1,4 @@
-"""Parity of a stack of RetNet layers (reading notes §四.4) with the fp64
+"""Parity of a stack of RetNet layers (reading notes §三.4) with the fp64
 oracle: the chunkwise forward of the stack with its per-layer states handed to
 the token-by-token decode (recurrent form, §2.2), and one decode step of a
 layer at the decode workload's shape (batch 128, d_model 4096, 16 heads of

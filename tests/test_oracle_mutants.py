@@ -38,6 +38,8 @@ MUTANTS = [
      "        num = np.einsum('bhd,bhde->bhe', qp, S - kp[:, :, :, None] * v[:, :, p, None, :])\n"),
     ("heads interleaved", "np.transpose(x.reshape(b, L, h, hd // h), (0, 2, 1, 3))",
      "np.transpose(x.reshape(b, L, hd // h, h), (0, 3, 1, 2))"),
+    ("block W_Q and W_K swapped", "    Q = split_heads(X @ _f64(WQ), h)\n    K = split_heads(X @ _f64(WK), h)\n",
+     "    Q = split_heads(X @ _f64(WK), h)\n    K = split_heads(X @ _f64(WQ), h)\n"),
     ("gate after W_O", "out = gate_norm(Y, G, eps) @ _f64(WO)",
      "out = (group_norm_heads(Y, eps) @ _f64(WO)) * swish(G[..., :WO.shape[1]])"),
     ("unbiased LN variance", "var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)",
