@@ -74,7 +74,12 @@ int hip_status(hipError_t e, const char* what) {
 
 void fill_params(ret::HeadParams& hp, const double* gamma, int h, const double* theta, int dk, unsigned flags) {
   memset(&hp, 0, sizeof(hp));
-  for (int i = 0; i < h; ++i) hp.gamma[i] = gamma[i];
+  for (int i = 0; i < h; ++i) {
+    hp.gamma[i] = gamma[i];
+    hp.lg2[i] = (float)log2(gamma[i]);
+    hp.omg[i] = (float)(1.0 - gamma[i]);
+    hp.lng[i] = (float)log1p(-(1.0 - gamma[i]));
+  }
   if ((flags & RET_XPOS) && theta)
     for (int j = 0; j < dk / 2; ++j) hp.theta[j] = theta[j];
 }

@@ -205,7 +205,7 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   const int c0 = c * p.B;
   const int Bc = min(p.B, p.L - c0);
   Decay dec;
-  dec.init(hp.gamma[head]);
+  dec.init(hp, head);
   const bool xpos = (p.flags & RET_XPOS) != 0;
 
   const T* Kg = reinterpret_cast<const T*>(p.k) + bb * p.sk.b + head * p.sk.h + (int64_t)c0 * p.sk.l;
@@ -407,7 +407,7 @@ __global__ void __launch_bounds__(256) scan_kernel(P3 p, HeadParams hp) {
   const int dbase = (tid & 7) * 32;
   const int half_ = col >> 8;
   Decay dec;
-  dec.init(hp.gamma[head]);
+  dec.init(hp, head);
   float R[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i)
@@ -505,7 +505,7 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
   const int cb = g % NCB64, bh = g / NCB64;
   const int bb = bh / p.h, head = bh % p.h;
   Decay dec;
-  dec.init(hp.gamma[head]);
+  dec.init(hp, head);
   const bool xpos = (p.flags & RET_XPOS) != 0;
   const T* Kg = reinterpret_cast<const T*>(p.k) + bb * p.sk.b + head * p.sk.h;
   const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + cb * SCB;
@@ -835,7 +835,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     const int r0 = rt * TR;
     const int qvalid = min(TR, Bc - r0);
     Decay dec;
-    dec.init(hp.gamma[head]);
+    dec.init(hp, head);
     const bool xpos = (p.flags & RET_XPOS) != 0;
     const float qk_scale = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
 

@@ -432,7 +432,7 @@ __global__ void __launch_bounds__(BT) bwd_state_kernel(BwdP p, HeadParams hp) {
   const int bh = blockIdx.x / (NEB * NDB);
   const int head = bh % p.h;
   Decay dec;
-  dec.init(hp.gamma[head]);
+  dec.init(hp, head);
   const float qk = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
   const uint16_t* X = (REV ? p.Qr : p.Kr) + (int64_t)bh * p.L * DK + 64 * db;
   const uint16_t* Y = (REV ? p.Gb : p.Vb) + (int64_t)bh * p.L * DV + DVB * eb;
@@ -626,7 +626,7 @@ __global__ void __launch_bounds__(BT) bwd_dq_kernel(BwdP p, HeadParams hp) {
   const int r0 = tile * TL, nq = min(TL, p.L - r0);
   const int c = r0 / p.B, c0 = c * p.B;
   Decay dec;
-  dec.init(hp.gamma[head]);
+  dec.init(hp, head);
   const float qk = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
   const uint16_t* Kr = p.Kr + (int64_t)bh * p.L * DK;
   const uint16_t* Vb = p.Vb + (int64_t)bh * p.L * DV;
@@ -847,7 +847,7 @@ __global__ void __launch_bounds__(BT) bwd_dk_kernel(BwdP p, HeadParams hp) {
   const int m0 = tile * TL, nk = min(TL, p.L - m0);
   const int c = m0 / p.B, c0 = c * p.B, c1 = min(c0 + p.B, p.L);
   Decay dec;
-  dec.init(hp.gamma[head]);
+  dec.init(hp, head);
   const float qk = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
   const uint16_t* Qr = p.Qr + (int64_t)bh * p.L * DK;
   const uint16_t* Vb = p.Vb + (int64_t)bh * p.L * DV;
@@ -997,7 +997,7 @@ __global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
   const int m0 = tile * TL, nk = min(TL, p.L - m0);
   const int c = m0 / p.B, c0 = c * p.B, c1 = min(c0 + p.B, p.L);
   Decay dec;
-  dec.init(hp.gamma[head]);
+  dec.init(hp, head);
   const float qk = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
   const uint16_t* Qr = p.Qr + (int64_t)bh * p.L * DK;
   const uint16_t* Kr = p.Kr + (int64_t)bh * p.L * DK;

@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(NT, 1) chunkwise_kernel(KParams p, HeadParams 
   const int s0 = slice * SV;
 
   Decay dec;
-  dec.init(hp.gamma[head]);
+  dec.init(hp, head);
   const bool xpos = (p.flags & RET_XPOS) != 0;
   const bool drow = (p.flags & RET_NORM_DROW) != 0;
   const float qk_scale = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;

@@ -30,6 +30,9 @@ constexpr int kMaxPairs = 256;    // d_k <= 512
 struct HeadParams {
   double gamma[kMaxHeads];
   double theta[kMaxPairs];
+  // per-head decay scalars, from gamma in float64 on the host, rounded once:
+  // lg2 = log2(gamma), omg = 1 - gamma, lng = ln(gamma) (see Decay)
+  float lg2[kMaxHeads], omg[kMaxHeads], lng[kMaxHeads];
 };
 
 __device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
@@ -69,18 +72,18 @@ template <> struct Elem<_Float16> {
 };
 
 // ---------------------------------------------------------------------------
-// Per-head scalars.  All of them come from gamma in float64 and are rounded to
-// float32 once.  lg2 = log2(gamma) feeds gamma^k = exp2(k * lg2); omg = 1 -
+// Per-head scalars.  All of them come from gamma in float64 (on the host,
+// in HeadParams) and are rounded to float32 once.  lg2 = log2(gamma) feeds gamma^k = exp2(k * lg2); omg = 1 -
 // gamma (exact for the 1 - 2^-k ladder); lng = ln(gamma) feeds
 // 1 - gamma^n = -expm1(n * lng), which keeps full relative accuracy when
 // gamma^n is close to 1 (gamma = 1 - 2^-20 at n = 1).
 // ---------------------------------------------------------------------------
 struct Decay {
   float lg2, omg, lng;
-  __device__ __forceinline__ void init(double g) {
-    lg2 = (float)log2(g);
-    omg = (float)(1.0 - g);
-    lng = (float)log1p(-(1.0 - g));
+  __device__ __forceinline__ void init(const HeadParams& hp, int head) {
+    lg2 = hp.lg2[head];
+    omg = hp.omg[head];
+    lng = hp.lng[head];
   }
   __device__ __forceinline__ float pow(float k) const { return exp2f(k * lg2); }
   // D-row factor sqrt((1-gamma)/(1-gamma^n)) for a row that has seen n tokens

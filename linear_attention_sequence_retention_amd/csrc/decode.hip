@@ -107,7 +107,7 @@ recurrent_step_kernel(const TI* __restrict__ q, const TI* __restrict__ k, const 
   }
   if (rg == 0) {
     Decay dec;
-    dec.init(g64);
+    dec.init(hp, head);
     float sc = 1.f;
     if (flags & RET_SCALE_QK) sc *= rsqrtf((float)dk);
     if (flags & RET_NORM_DROW) sc *= dec.drow((float)n_tokens);
