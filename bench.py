@@ -1,19 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the retention hot path on one MI355X.
 
-A step is one retention_chunkwise_fwd over the medium workload (batch 4, 8
-heads, L = 2048, d_k = 256, d_v = 512, bf16 inputs, chunk B = 512, xPos and all
-three normalisations, bf16 output): value = tokens/s = b*L / step time.  The
-inputs are resident in HBM before timing; three input/output buffer sets are
-rotated so the 256 MB MALL cannot serve a repeated set.  Secondary lines in
-the same JSON record: the same workload at B = 64, the long workload (L =
-32768, 16 heads), the parallel form on short sequences (32 x 8 heads x 512)
-against the chunkwise form, the chunkwise backward on the medium workload, the decode
-step (batch 128, 16 heads, 64 steps from
-position 8192), the GroupNorm + gate epilogue at the block shape, the gated
-MSR block (2 x 8192 tokens, d_model 4096), one RetNet layer around it
-(LayerNorms, residuals and a 4 x d_model gelu FFN), and that layer decoding
-one token for 128 sequences.
+A step is one retention_chunkwise_fwd over the long workload (batch 1, 16
+heads, L = 32768, d_k = 256, d_v = 512, bf16 inputs, chunk B = 512, xPos and
+all three normalisations, bf16 output), the largest chunkwise configuration:
+value = tokens/s = b*L / step time.  Its inputs (1.6 GB with the output) are
+resident in HBM before timing and exceed the 256 MB MALL.  The same JSON line
+carries, next to the headline, the medium workload (batch 4, 8 heads, L =
+2048) at B = 512 (three rotated buffer sets, so the MALL cannot serve a
+repeated set) and B = 64, each with its own roofline block; the decode step
+(batch 128, 16 heads, 64 steps from position 8192) with its roofline block;
+the measured ceilings (a streaming copy and an fp16 MFMA loop, both kernels of
+this library); the parallel form on short sequences; the chunkwise backward;
+the GroupNorm + gate epilogue; the gated MSR block (2 x 8192 tokens, d_model
+4096), one RetNet layer around it and that layer decoding one token for 128
+sequences; and the CPU legs of the fp64 oracle (chunkwise form, recurrent
+form, decode step) on bounded samples of the same workloads.
+
+Counter-derived figures (HBM bytes from FETCH_SIZE / WRITE_SIZE, MFMA busy
+cycles) are read from the committed profiles/ summaries, and reported only
+while the kernel sources hash to the value recorded there.
 
 Prints ONE JSON line.  Only N = 1 GPU is supported.
 """
@@ -32,34 +38,59 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+RIDGE = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
-# counter summary of the primary step and the sources its kernels are built from
-TRAFFIC_PROFILE = os.path.join("profiles", "chunkwise_medium_B512_traffic.md")
-TRAFFIC_SOURCES = [os.path.join("linear_attention_sequence_retention_amd", "csrc", f)
-                   for f in ("chunk3.hip", "common.h", "internal.h")]
+CSRC = os.path.join("linear_attention_sequence_retention_amd", "csrc")
+# the sources each profiled kernel group is built from
+CHUNK_SOURCES = [os.path.join(CSRC, f) for f in ("chunk3.hip", "common.h", "internal.h")]
+DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode.hip", "common.h", "internal.h")]
 
 
-def sources_sha256(root=ROOT):
+def sources_sha256(files, root=ROOT):
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in files:
         with open(os.path.join(root, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def profiled_traffic(root=ROOT):
-    """HBM bytes per call of the primary step from the committed FETCH_SIZE /
-    WRITE_SIZE summary (copy-calibrated), or None when the kernel sources have
-    changed since the counters were taken."""
+def profile_values(name, sources, root=ROOT):
+    """The 'key: value' lines of a committed profiles/ summary, or {} when the
+    file is missing or the kernel sources have changed since it was taken."""
     try:
-        with open(os.path.join(root, TRAFFIC_PROFILE)) as fh:
+        with open(os.path.join(root, "profiles", name)) as fh:
             text = fh.read()
     except OSError:
-        return None
-    vals = dict(re.findall(r"^(traffic_bytes_per_call|kernel_sources_sha256): (\S+)$", text, re.M))
-    if vals.get("kernel_sources_sha256") != sources_sha256(root) or "traffic_bytes_per_call" not in vals:
-        return None
-    return int(vals["traffic_bytes_per_call"])
+        return {}
+    vals = dict(re.findall(r"^([a-z0-9_]+): (\S+)$", text, re.M))
+    if vals.get("kernel_sources_sha256") != sources_sha256(sources, root):
+        return {}
+    return vals
+
+
+def profiled_traffic(name, sources, root=ROOT):
+    """HBM bytes per call from a FETCH_SIZE / WRITE_SIZE summary (copy-calibrated)."""
+    v = profile_values(name, sources, root).get("traffic_bytes_per_call")
+    return None if v is None else int(v)
+
+
+def profiled_mfma(name, sources, root=ROOT):
+    """MFMA busy fraction per kernel from a counter summary ({} if stale)."""
+    vals = profile_values(name, sources, root)
+    return {k[len("mfma_busy_"):]: float(v) for k, v in vals.items() if k.startswith("mfma_busy_")}
+
+
+def roofline(flops, nbytes, ms, traffic):
+    """The roofline block of a call: the binding roof by arithmetic intensity
+    (algorithmic flops over compulsory bytes), achieved = algorithmic work /
+    measured time."""
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    if flops / nbytes < RIDGE:
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+    return {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "traffic": traffic}
 
 
 def chunk_flops(b, h, L, dk, dv, B, with_state_out=False):
@@ -122,41 +153,92 @@ def make_chunk_sets(cfg, nsets, torch, W, dev):
     return sets, (q, k, v)
 
 
-def cpu_baseline(cfg, B, W):
-    """The fp64 oracle (chunkwise form, numpy + BLAS) on the medium workload
-    (all four sequences, all heads, full L), repeated until at least 10 s of
-    CPU time has run; tokens/s over the runs."""
-    import oracle
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg, B, W, budget_s=10.0):
+    """The fp64 oracle's chunkwise form (numpy + BLAS, all host threads) on a
+    bounded sample of the headline workload: whole heads (every token of the
+    sequence) one at a time until budget_s of CPU time has run; the rate is
+    scaled to the whole workload (b*L tokens over h heads)."""
+    import oracle
     q, k, v = W.chunkwise_inputs(**cfg)
-    qs, ks, vs = (W.as_f32(a, cfg["dtype"]).astype(np.float64) for a in (q, k, v))
     g, th = W.gamma_vector(cfg["h"]), W.theta_vector(cfg["dk"])
     t0 = time.perf_counter()
-    reps = 0
+    heads = 0
     while True:
-        oracle.retention_chunkwise(qs, ks, vs, g, th, cfg["flags"], B)
-        reps += 1
-        if time.perf_counter() - t0 > 10.0 or reps >= 200:
+        bb, hh = divmod(heads % (cfg["b"] * cfg["h"]), cfg["h"])
+        sl = (slice(bb, bb + 1), slice(hh, hh + 1))
+        qs, ks, vs = (W.as_f32(a[sl], cfg["dtype"]).astype(np.float64) for a in (q, k, v))
+        oracle.retention_chunkwise(qs, ks, vs, g[hh:hh + 1], th, cfg["flags"], B)
+        heads += 1
+        if time.perf_counter() - t0 > budget_s or heads >= 4 * cfg["b"] * cfg["h"]:
             break
-    dt = (time.perf_counter() - t0) / reps
-    toks = cfg["b"] * cfg["L"]
-    return {"value": toks / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle.retention_chunkwise (fp64 numpy/BLAS) over the whole medium workload "
-                      f"(b={cfg['b']}, {cfg['h']} heads, L={cfg['L']}, B={B}), {reps} run(s) of {dt:.2f} s"}
+    dt = (time.perf_counter() - t0) / heads                # per (batch, head) sequence
+    total = dt * cfg["b"] * cfg["h"]
+    return {"value": cfg["b"] * cfg["L"] / total, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"oracle.retention_chunkwise (fp64 numpy/BLAS, B={B}) over {heads} whole (batch, head) "
+                      f"sequences of the {W.workload_name(cfg)} workload, {dt:.2f} s each; "
+                      f"scaled to all {cfg['b'] * cfg['h']} heads"}
+
+
+def cpu_legs(cfg, dec, W, budget_s=10.0):
+    """The other CPU legs of the oracle: the recurrent form (the definition: a
+    Python loop over positions, numpy over (batch, head)) on the first tokens
+    of the headline workload, all heads, until budget_s; and the decode step on
+    a few of the decode workload's sequences for its 64 steps (GB/s of fp32
+    state read and written, the metric of the GPU leg)."""
+    import oracle
+    out = {"cores": _blas_threads()}
+    q, k, v = W.chunkwise_inputs(**cfg)
+    g, th = W.gamma_vector(cfg["h"]), W.theta_vector(cfg["dk"])
+    n = 64
+    while True:
+        qs, ks, vs = (W.as_f32(a[:, :, :n], cfg["dtype"]).astype(np.float64) for a in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.retention_recurrent(qs, ks, vs, g, th, cfg["flags"])
+        dt = time.perf_counter() - t0
+        if dt > budget_s / 4 or n >= cfg["L"]:
+            break
+        n = min(cfg["L"], n * 4)
+    out["recurrent"] = {"value": cfg["b"] * n / dt, "unit": "tokens/s",
+                        "sample": f"oracle.retention_recurrent over the first {n} tokens of every head of "
+                                  f"{W.workload_name(cfg)}, {dt:.2f} s"}
+    S0, qd, kd, vd = W.decode_inputs(**dec)
+    gd, thd = W.gamma_vector(dec["h"]), W.theta_vector(dec["dk"])
+    nb = 1
+    while True:
+        S = S0[:nb].astype(np.float64)
+        t0 = time.perf_counter()
+        for t in range(dec["steps"]):
+            step_in = [W.as_f32(a[t, :nb], "bf16").astype(np.float64) for a in (qd, kd, vd)]
+            _o, S, _z = oracle.recurrent_step(*step_in, S, gd, thd, dec["flags"], dec["pos0"] + t, dec["pos0"] + t + 1)
+        dt = time.perf_counter() - t0
+        if dt > budget_s / 4 or nb >= dec["b"]:
+            break
+        nb = min(dec["b"], nb * 4)
+    state = nb * dec["h"] * dec["dk"] * dec["dv"] * 4
+    out["decode"] = {"value": round(2 * state * dec["steps"] / dt / 1e9, 3), "unit": "GB/s",
+                     "tokens_per_s": nb * dec["steps"] / dt,
+                     "sample": f"oracle.recurrent_step, {nb} of {dec['b']} sequences x {dec['steps']} steps, "
+                               f"{dt:.2f} s (fp32-equivalent state bytes read and written)"}
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true", help="time the primary workload only")
-    ap.add_argument("--secondary", default="medium_B64,parallel_short,backward,long,decode,gate_norm,block,layer,decode_layer,copy",
+    ap.add_argument("--secondary",
+                    default="medium,medium_B64,decode,ceilings,parallel_short,backward,gate_norm,block,layer,decode_layer",
                     help="comma list of secondary measurements to run (empty for none)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -171,61 +253,75 @@ def main():
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
-    cfg = W.CHUNKWISE["medium"]
-    b, h, L, dk, dv = cfg["b"], cfg["h"], cfg["L"], cfg["dk"], cfg["dv"]
-    g, th = W.gamma_vector(h), W.theta_vector(dk)
-    flags = cfg["flags"]
+    # ---- primary: the long workload, K timed steps bracketed by synchronisation
+    lc = W.CHUNKWISE["long"]
     B = 512
-    sets, host = make_chunk_sets(cfg, 3, torch, W, dev)
-    it = [0]
+    lq, lk, lv = W.chunkwise_inputs(**lc)
+    lqd, lkd, lvd = dev(lq), dev(lk), dev(lv)
+    del lq, lk, lv
+    lo = torch.empty((lc["b"], lc["h"], lc["L"], lc["dv"]), dtype=torch.bfloat16, device="cuda")
+    lg, lth = W.gamma_vector(lc["h"]), W.theta_vector(lc["dk"])
+    lws = torch.empty(R.chunkwise_workspace_bytes(lc["b"], lc["h"], lc["L"], lc["dk"], lc["dv"], B, lc["flags"]),
+                      dtype=torch.uint8, device="cuda")
 
-    def step(Bc=B):
-        qd, kd, vd, od = sets[it[0] % 3]
-        it[0] += 1
-        R.chunkwise_fwd(qd, kd, vd, g, th, Bc, flags, out=od)
+    def step():
+        R.chunkwise_fwd(lqd, lkd, lvd, lg, lth, B, lc["flags"], out=lo, workspace=lws)
 
-    # ---- primary: K timed steps bracketed by synchronisation
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms_kernel = time_calls(step, args.steps, 0, torch)
+    ms = time_calls(step, args.steps, 0, torch)
     wall = time.perf_counter() - t0
-    ms = ms_kernel
-    tokens = b * L
+    tokens = lc["b"] * lc["L"]
     value = tokens / (ms * 1e-3)
-    flops = chunk_flops(b, h, L, dk, dv, B)
-    nbytes = chunk_bytes(b, h, L, dk, dv)
+    flops = chunk_flops(lc["b"], lc["h"], lc["L"], lc["dk"], lc["dv"], B)
+    nbytes = chunk_bytes(lc["b"], lc["h"], lc["L"], lc["dk"], lc["dv"])
     tflops = flops / (ms * 1e-3) / 1e12
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    intensity = flops / nbytes
-    ridge = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    bound = "hbm" if intensity < ridge else "mfma"
-    traffic = profiled_traffic()
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "traffic": traffic}
-
+    traffic = profiled_traffic("chunkwise_long_B512_traffic.md", CHUNK_SOURCES)
+    roof = roofline(flops, nbytes, ms, traffic)
     extra = {"primary": {"kernel": "retention_chunkwise_fwd (delta, scan, output kernels)",
                          "arithmetic": "bf16 in and out, fp16 MFMA operands, fp32 accumulate",
                          "traffic_x_compulsory": None if traffic is None else round(traffic / nbytes, 2),
+                         "mfma_busy": profiled_mfma("chunkwise_long_B512_mfma.md", CHUNK_SOURCES) or None,
                          "ms": round(ms, 4), "tflops": round(tflops, 1),
-                         "mfma_frac": round(tflops / PEAK_MFMA_TFLOPS, 4), "gbs": round(gbs, 1),
-                         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "alg_gflop": round(flops / 1e9, 2),
-                         "alg_mb": round(nbytes / 1e6, 1), "wall_s": round(wall, 3)}}
+                         "mfma_frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
+                         "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "alg_gflop": round(flops / 1e9, 2), "alg_mb": round(nbytes / 1e6, 1), "wall_s": round(wall, 3)}}
+    del lqd, lkd, lvd, lo, lws
+    torch.cuda.empty_cache()
 
+    cfg = W.CHUNKWISE["medium"]
+    b, h, L, dk, dv = cfg["b"], cfg["h"], cfg["L"], cfg["dk"], cfg["dv"]
+    g, th = W.gamma_vector(h), W.theta_vector(dk)
+    flags = cfg["flags"]
     todo = set() if args.only_primary else set(x for x in args.secondary.split(",") if x)
-    if "medium_B64" in todo:
-        # same workload at B = 64
-        ms64 = time_calls(lambda: step(64), max(5, args.steps // 2), 2, torch)
-        f64_ = chunk_flops(b, h, L, dk, dv, 64)
-        extra["medium_B64"] = {"ms": round(ms64, 4), "tokens_per_s": tokens / (ms64 * 1e-3),
-                               "tflops": round(f64_ / (ms64 * 1e-3) / 1e12, 1),
-                               "mfma_frac": round(f64_ / (ms64 * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
-                               "gbs": round(nbytes / (ms64 * 1e-3) / 1e9, 1)}
+    sets = []
+    if todo & {"medium", "medium_B64", "backward"}:
+        sets, _host = make_chunk_sets(cfg, 3, torch, W, dev)
+        del _host
+    it = [0]
+
+    def mstep(Bc):
+        qd, kd, vd, od = sets[it[0] % 3]
+        it[0] += 1
+        R.chunkwise_fwd(qd, kd, vd, g, th, Bc, flags, out=od)
+
+    mtokens = b * L
+    mbytes = chunk_bytes(b, h, L, dk, dv)
+    for key, Bc, prof in (("medium", 512, "medium_B512"), ("medium_B64", 64, "medium_B64")):
+        if key not in todo:
+            continue
+        # the medium workload, three rotated buffer sets (the MALL holds one)
+        msm = time_calls(lambda: mstep(Bc), args.steps, 3, torch)
+        fl = chunk_flops(b, h, L, dk, dv, Bc)
+        tr = profiled_traffic(f"chunkwise_{prof}_traffic.md", CHUNK_SOURCES)
+        extra[key] = {"workload": "chunkwise_fwd " + W.workload_name(cfg, Bc), "ms": round(msm, 4),
+                      "tokens_per_s": mtokens / (msm * 1e-3), "tflops": round(fl / (msm * 1e-3) / 1e12, 1),
+                      "mfma_frac": round(fl / (msm * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                      "roofline": roofline(fl, mbytes, msm, tr),
+                      "traffic_x_compulsory": None if tr is None else round(tr / mbytes, 2),
+                      "mfma_busy": profiled_mfma(f"chunkwise_{prof}_mfma.md", CHUNK_SOURCES) or None}
     if "parallel_short" in todo:
         # short sequences (32 x 8 heads x 512 tokens, the medium head shape): the
         # parallel form (one chunk) against the chunkwise form at B = 64 and 128
@@ -255,7 +351,7 @@ def main():
             msb = time_calls(lambda: R.chunkwise_bwd(qd, kd, vd, dod, g, th, Bb, flags, dq=grads[0], dk=grads[1],
                                                      dv=grads[2], workspace=wsb), max(5, args.steps // 2), 2, torch)
             fl = bwd_flops(b, h, L, dk, dv, Bb, True)
-            ent = {"ms": round(msb, 4), "chunk": Bb, "tokens_per_s": tokens / (msb * 1e-3),
+            ent = {"ms": round(msb, 4), "chunk": Bb, "tokens_per_s": mtokens / (msb * 1e-3),
                    "tflops": round(fl / (msb * 1e-3) / 1e12, 1),
                    "mfma_frac": round(fl / (msb * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4), "alg_gflop": round(fl / 1e9, 2)}
             if best is None or msb < best["ms"]:
@@ -265,23 +361,6 @@ def main():
         del dod, grads
     del sets[:]
     torch.cuda.empty_cache()
-    if "long" in todo:
-        # long workload
-        lc = W.CHUNKWISE["long"]
-        lq, lk, lv = W.chunkwise_inputs(**lc)
-        lqd, lkd, lvd = dev(lq), dev(lk), dev(lv)
-        del lq, lk, lv
-        lo = torch.empty((lc["b"], lc["h"], lc["L"], lc["dv"]), dtype=torch.bfloat16, device="cuda")
-        lg, lth = W.gamma_vector(lc["h"]), W.theta_vector(lc["dk"])
-        msl = time_calls(lambda: R.chunkwise_fwd(lqd, lkd, lvd, lg, lth, 512, lc["flags"], out=lo), 3, 1, torch)
-        fl = chunk_flops(lc["b"], lc["h"], lc["L"], lc["dk"], lc["dv"], 512)
-        bl = chunk_bytes(lc["b"], lc["h"], lc["L"], lc["dk"], lc["dv"])
-        extra["long_B512"] = {"ms": round(msl, 3), "tokens_per_s": lc["b"] * lc["L"] / (msl * 1e-3),
-                              "tflops": round(fl / (msl * 1e-3) / 1e12, 1),
-                              "mfma_frac": round(fl / (msl * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
-                              "gbs": round(bl / (msl * 1e-3) / 1e9, 1)}
-        del lqd, lkd, lvd, lo
-        torch.cuda.empty_cache()
     if "decode" in todo:
         # decode: 64 sequential steps at batch 128
         dc = W.DECODE
@@ -301,19 +380,33 @@ def main():
                 R.recurrent_step(qd[t], kd[t], vd[t], S, dg, dth, pos0 + t, pos0 + t + 1, dc["flags"], out=od)
         msd = time_calls(decode64, 3, 1, torch) / dc["steps"]
         dbytes = 2 * db * dh * ddk * ddv * 4 + db * dh * (2 * ddk * 2 + ddv * 2 + ddv * 4)
-        extra["decode"] = {"ms_per_step": round(msd, 4), "gbs": round(dbytes / (msd * 1e-3) / 1e9, 1),
+        dflops = 4 * db * dh * ddk * ddv
+        dtr = profiled_traffic("decode_b128_h16_traffic.md", DECODE_SOURCES)
+        extra["decode"] = {"workload": "recurrent step b128 h16 dk256 dv512 fp32 state, 64 steps from position 8192",
+                           "ms_per_step": round(msd, 4), "gbs": round(dbytes / (msd * 1e-3) / 1e9, 1),
                            "hbm_frac": round(dbytes / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                           "tokens_per_s": db / (msd * 1e-3), "alg_mb_per_step": round(dbytes / 1e6, 1)}
+                           "tokens_per_s": db / (msd * 1e-3), "alg_mb_per_step": round(dbytes / 1e6, 1),
+                           "roofline": roofline(dflops, dbytes, msd, dtr),
+                           "traffic_x_compulsory": None if dtr is None else round(dtr / dbytes, 3)}
         del S, qd, kd, vd
         torch.cuda.empty_cache()
-    if "copy" in todo:
-        # a plain 1 GiB device copy: measured HBM reference and the
-        # calibration kernel for the FETCH_SIZE / WRITE_SIZE counters
+    if "ceilings" in todo:
+        # measured ceilings from this library's own kernels: a 1 GiB streaming
+        # copy (also the calibration kernel of the FETCH_SIZE / WRITE_SIZE
+        # counters) and a loop of fp16 32x32x16 MFMAs on register operands
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        msc = time_calls(lambda: dst.copy_(src), 5, 1, torch)
-        extra["copy_1GiB"] = {"ms": round(msc, 4), "gbs": round(2 * (1 << 30) / (msc * 1e-3) / 1e9, 1)}
+        msc = time_calls(lambda: R.calib_copy(src, dst), 10, 2, torch)
         del src, dst
+        nblk, iters = 4096, 2000
+        mo = torch.empty(nblk * 256, dtype=torch.float32, device="cuda")
+        msm_ = time_calls(lambda: R.calib_mfma(mo, nblk, iters), 5, 1, torch)
+        mtf = nblk * 4 * iters * 4 * 32768 / (msm_ * 1e-3) / 1e12
+        extra["ceilings"] = {"copy_1GiB": {"ms": round(msc, 4), "gbs": round(2 * (1 << 30) / (msc * 1e-3) / 1e9, 1),
+                                           "frac_of_spec": round(2 * (1 << 30) / (msc * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                             "mfma_f16_loop": {"ms": round(msm_, 4), "tflops": round(mtf, 1),
+                                               "frac_of_spec": round(mtf / PEAK_MFMA_TFLOPS, 4)}}
+        del mo
         torch.cuda.empty_cache()
     if "block" in todo:
         # full gated MSR block forward: 2 x 8192 tokens, d_model 4096, 16 heads
@@ -335,19 +428,19 @@ def main():
         torch.cuda.empty_cache()
     if "layer" in todo:
         # one RetNet layer around the block: LN, MSR + residual, LN, FFN (4 x d_model, gelu) + residual
-        lc = W.LAYER
-        msr_w, W1, W2, ln1, ln2 = W.layer_inputs(**lc)
+        yc = W.LAYER
+        msr_w, W1, W2, ln1, ln2 = W.layer_inputs(**yc)
         dT = lambda w: dev(np.ascontiguousarray(w.T))
         vec = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
         Xd, ws, w1, w2 = dev(msr_w[0]), tuple(dT(w) for w in msr_w[1:]), dT(W1), dT(W2)
         l1, l2 = (vec(ln1[0]), vec(ln1[1])), (vec(ln2[0]), vec(ln2[1]))
         del msr_w, W1, W2
-        lg, lth = W.gamma_vector(lc["h"]), W.theta_vector(lc["dk"])
-        msl = time_calls(lambda: R.retnet_layer_fwd(Xd, ws, w1, w2, lg, lth, lc["chunk"], lc["flags"], lc["eps"],
-                                                     lc["ln_eps"], l1, l2), 3, 1, torch)
-        M, dm, hdk, hdv, dff = lc["b"] * lc["L"], lc["d_model"], lc["h"] * lc["dk"], lc["h"] * lc["dv"], lc["d_ff"]
+        lg, lth = W.gamma_vector(yc["h"]), W.theta_vector(yc["dk"])
+        msl = time_calls(lambda: R.retnet_layer_fwd(Xd, ws, w1, w2, lg, lth, yc["chunk"], yc["flags"], yc["eps"],
+                                                     yc["ln_eps"], l1, l2), 3, 1, torch)
+        M, dm, hdk, hdv, dff = yc["b"] * yc["L"], yc["d_model"], yc["h"] * yc["dk"], yc["h"] * yc["dv"], yc["d_ff"]
         gflop = 2 * M * dm * (2 * hdk + 2 * hdv) + 2 * M * hdv * dm + 4 * M * dm * dff
-        rflop = chunk_flops(lc["b"], lc["h"], lc["L"], lc["dk"], lc["dv"], lc["chunk"])
+        rflop = chunk_flops(yc["b"], yc["h"], yc["L"], yc["dk"], yc["dv"], yc["chunk"])
         extra["layer"] = {"ms": round(msl, 3), "tokens_per_s": M / (msl * 1e-3),
                           "tflops": round((gflop + rflop) / (msl * 1e-3) / 1e12, 1), "d_ff": dff,
                           "gemm_gflop": round(gflop / 1e9, 1), "retention_gflop": round(rflop / 1e9, 1)}
@@ -400,16 +493,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "chunkwise_fwd " + W.workload_name(cfg, B) + " xpos+all_norms",
-                   "global_batch": b, "seq_len": L, "heads": h, "d_k": dk, "d_v": dv, "chunk": B,
-                   "parallelism": "single_gpu"},
+        "config": {"workload": "chunkwise_fwd " + W.workload_name(lc, B) + " xpos+all_norms",
+                   "global_batch": lc["b"], "seq_len": lc["L"], "heads": lc["h"], "d_k": lc["dk"], "d_v": lc["dv"],
+                   "chunk": B, "parallelism": "single_gpu"},
         "roofline": roof,
         "mfma": {"achieved": round(tflops, 1), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(tflops / PEAK_MFMA_TFLOPS, 4)},
         "extra": extra,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, B, W)
+        line["cpu_baseline"] = cpu_baseline(lc, B, W)
+        extra["cpu_legs"] = cpu_legs(lc, W.DECODE, W)
     print(json.dumps(line), flush=True)
 
 

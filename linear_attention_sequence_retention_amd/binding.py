@@ -71,6 +71,10 @@ def load_library(path=LIB_PATH):
     lib.msr_gemm_workspace_bytes.restype = sz
     lib.ret_layer_norm.argtypes = [vp, vp, i32, i32, vp, vp, f32, i32, i32, vp]
     lib.ret_layer_norm.restype = i32
+    lib.ret_calib_copy.argtypes = [vp, vp, sz, vp]
+    lib.ret_calib_copy.restype = i32
+    lib.ret_calib_mfma.argtypes = [vp, i32, i32, vp]
+    lib.ret_calib_mfma.restype = i32
     lib.retention_last_error.argtypes = []
     lib.retention_last_error.restype = ctypes.c_char_p
     lib.retention_abi_version.argtypes = []
@@ -461,3 +465,20 @@ for _name in ("chunkwise_fwd", "parallel_fwd", "chunkwise_bwd", "recurrent_step"
               "layer_norm", "msr_block_fwd", "retnet_layer_fwd", "retnet_stack_fwd", "retnet_decode_step"):
     globals()[_name] = _on_stream(globals()[_name])
 del _name
+
+
+def calib_copy(src, dst, stream=None):
+    """dst <- src (equal-size contiguous device tensors, a multiple of 16 bytes):
+    the measured HBM ceiling of the benchmark."""
+    n = src.numel() * src.element_size()
+    if n % 16 or dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst must have the same size, a multiple of 16 bytes")
+    _check(LIB.ret_calib_copy(_ptr(src), _ptr(dst), n // 16, _stream(stream)), "ret_calib_copy")
+
+
+def calib_mfma(out, blocks, iters, stream=None):
+    """blocks x 4 waves x iters x 4 fp16 32x32x16 MFMAs (out: float32, blocks * 256):
+    the measured matrix-core ceiling of the benchmark."""
+    if out.dtype != torch.float32 or out.numel() < blocks * 256:
+        raise ValueError("out must be float32 with blocks * 256 elements")
+    _check(LIB.ret_calib_mfma(_ptr(out), blocks, iters, _stream(stream)), "ret_calib_mfma")

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include "internal.h"
+#include "retention_calib.h"
 
 namespace {
 
@@ -375,6 +376,19 @@ int ret_layer_norm(const void* x, void* y, int rows, int d, const float* weight,
   if (x == y) return fail(RET_E_INVAL, "y must not alias x");
   return hip_status(ret::launch_layer_norm(x, y, rows, d, weight, bias, eps, x_dt, y_dt, stream),
                     "ret_layer_norm launch");
+}
+
+int ret_calib_copy(const void* src, void* dst, size_t n16, hipStream_t stream) {
+  if (!src || !dst || n16 == 0) return fail(RET_E_INVAL, "src, dst must be non-NULL and n16 >= 1");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(RET_E_ALIGN, "src and dst must be 16-byte aligned");
+  if (overlaps(src, n16 * 16, dst, n16 * 16)) return fail(RET_E_INVAL, "src and dst must not overlap");
+  return hip_status(ret::launch_calib_copy(src, dst, n16, stream), "ret_calib_copy launch");
+}
+
+int ret_calib_mfma(float* out, int blocks, int iters, hipStream_t stream) {
+  if (!out || blocks < 1 || iters < 1) return fail(RET_E_INVAL, "out must be non-NULL, blocks and iters >= 1");
+  if (!aligned(out, 4)) return fail(RET_E_ALIGN, "out must be 4-byte aligned");
+  return hip_status(ret::launch_calib_mfma(out, blocks, iters, stream), "ret_calib_mfma launch");
 }
 
 }  // extern "C"

@@ -109,4 +109,8 @@ hipError_t launch_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C,
 hipError_t launch_layer_norm(const void* x, void* y, int rows, int d, const float* w, const float* bias, float eps,
                              ret_dtype x_dt, ret_dtype y_dt, hipStream_t st);
 
+// measured ceilings (calib.hip)
+hipError_t launch_calib_copy(const void* src, void* dst, size_t n16, hipStream_t st);
+hipError_t launch_calib_mfma(float* out, int blocks, int iters, hipStream_t st);
+
 }  // namespace ret

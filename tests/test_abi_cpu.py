@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "retention.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("retention.h", "retention_calib.h")]
 
 
 @pytest.fixture(scope="module")
@@ -19,14 +19,17 @@ def B():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(B):
     names = declared_functions()
-    assert {"retention_chunkwise_fwd", "retention_recurrent_step", "msr_gate_norm", "msr_gemm"} <= set(names)
+    assert {"retention_chunkwise_fwd", "retention_recurrent_step", "msr_gate_norm", "msr_gemm",
+            "msr_gemm_bf16", "ret_calib_copy", "ret_calib_mfma"} <= set(names)
     for n in names:
         assert hasattr(B.LIB, n), f"libretention.so does not export {n}"
     assert B.LIB.retention_abi_version() == 1
@@ -264,3 +267,15 @@ def test_layer_norm_and_gemm_ex_validation(B):
     assert ws(ctypes.c_void_p(0x300000 - 256), need) == 1          # overlaps C
     assert ws(W, need, ep=2) == 1                                  # unknown epilogue bit
     assert L.msr_gemm_ws(A, 1, Bm, C, 0, 64, 256, 500, None, 0, 0, W, need, None) == 2   # K % 32
+
+
+def test_calib_validation(B):
+    L = B.LIB
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    assert L.ret_calib_copy(None, b, 16, None) == 1
+    assert L.ret_calib_copy(a, b, 0, None) == 1
+    assert L.ret_calib_copy(FAKE_MIS, b, 16, None) == 3
+    assert L.ret_calib_copy(a, ctypes.c_void_p(0x100100), 64, None) == 1      # overlap
+    assert L.ret_calib_mfma(None, 1, 1, None) == 1
+    assert L.ret_calib_mfma(ctypes.c_void_p(0x100000), 0, 1, None) == 1
+    assert L.ret_calib_mfma(ctypes.c_void_p(0x100001), 1, 1, None) == 3
