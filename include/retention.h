@@ -286,6 +286,26 @@ int msr_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype
                 hipStream_t stream);
 
 /*
+ * msr_gemm_scratch -- msr_gemm_ws without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The split-K partial
+ * products go to a scratch array inside the library: MSR_GEMM_SCRATCH_BYTES
+ * per GPU, a static device array that each GPU the library runs on holds
+ * until the process ends.  Its address is looked up once per device (on the
+ * first call with that device current); the call itself allocates and frees
+ * nothing.  Every partial element is written before it is read, so the
+ * scratch needs no clearing, and it keeps the last call's contents.
+ * All calls on one GPU share its scratch array: calls that may overlap (on
+ * different streams without ordering) race; order them (one stream, or events).
+ * Arguments, results and errors as msr_gemm_ws; RET_E_WORKSPACE when
+ * msr_gemm_workspace_bytes(M, N, K) exceeds MSR_GEMM_SCRATCH_BYTES (which
+ * covers every M <= 128 with N <= 65536).
+ */
+#define MSR_GEMM_SCRATCH_BYTES ((size_t)32 << 20)
+int msr_gemm_scratch(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                     const void* residual, ret_dtype r_dt, unsigned epilogue, hipStream_t stream);
+
+/*
  * ret_layer_norm -- the LayerNorm of the RetNet layer ([notes] §三.4):
  *   y = (x - mean) / sqrt(biased variance + eps) over each row, then the
  *   optional per-channel affine

@@ -67,6 +67,8 @@ def load_library(path=LIB_PATH):
     lib.msr_gemm_ex.restype = i32
     lib.msr_gemm_ws.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, u32, vp, sz, vp]
     lib.msr_gemm_ws.restype = i32
+    lib.msr_gemm_scratch.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, i32, u32, vp]
+    lib.msr_gemm_scratch.restype = i32
     lib.msr_gemm_workspace_bytes.argtypes = [i32, i32, i32]
     lib.msr_gemm_workspace_bytes.restype = sz
     lib.ret_layer_norm.argtypes = [vp, vp, i32, i32, vp, vp, f32, i32, i32, vp]
@@ -83,6 +85,7 @@ def load_library(path=LIB_PATH):
 
 
 LIB = load_library()
+LIB_SCRATCH_BYTES = 32 << 20          # MSR_GEMM_SCRATCH_BYTES of include/retention.h
 
 
 def _check(status, what):

@@ -355,6 +355,24 @@ int msr_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype
                     "msr_gemm_ws launch");
 }
 
+int msr_gemm_scratch(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
+                     const void* residual, ret_dtype r_dt, unsigned epilogue, hipStream_t stream) {
+  const int st = gemm_checks(A, a_dt, B, C, c_dt, M, N, K, residual, r_dt, epilogue);
+  if (st != RET_OK) return st;
+  const size_t need = ret::gemm_workspace_bytes(M, N, K);
+  if (need > MSR_GEMM_SCRATCH_BYTES)
+    return fail(RET_E_WORKSPACE, "split-K partials of %zu bytes exceed the %zu-byte scratch", need,
+                (size_t)MSR_GEMM_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = ret::gemm_scratch_ptr(&ws);
+    if (e != hipSuccess) return hip_status(e, "msr_gemm_scratch scratch lookup");
+  }
+  return hip_status(ret::launch_gemm_ws(A, a_dt, B, C, c_dt, M, N, K, residual, r_dt,
+                                        (epilogue & MSR_GEMM_GELU) ? 1 : 0, ws, stream),
+                    "msr_gemm_scratch launch");
+}
+
 int msr_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
              hipStream_t stream) {
   return msr_gemm_ex(A, a_dt, B, C, c_dt, M, N, K, nullptr, c_dt, 0u, stream);

@@ -23,6 +23,8 @@
 // residual (the layer's two residual connections) stored as fp32, bf16 or
 // fp16 independently of the output, so that an fp32 residual stream can feed
 // a bf16 result and the reverse.
+#include <mutex>
+
 #include "internal.h"
 
 namespace ret {
@@ -524,6 +526,32 @@ hipError_t launch_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C,
   float* P = static_cast<float*>(ws);
   return a_dt == RET_F16 ? launch_splitk_a<half>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, P, st)
                          : launch_splitk_a<bf16>(A, B, C, c_dt, M, N, K, R, (int)r_dt, act, P, st);
+}
+
+// ---------------------------------------------------------------- scratch
+// The split-K partials of msr_gemm_scratch live in this static device array
+// (each device holds its own copy).  Host code uses the device address looked
+// up with hipGetSymbolAddress, never the array's name (a host-side stand-in).
+namespace {
+static __device__ __align__(256) float scratch[MSR_GEMM_SCRATCH_BYTES / sizeof(float)];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+}  // namespace
+
+hipError_t gemm_scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace ret

@@ -106,6 +106,9 @@ hipError_t launch_gemm(const void* A, ret_dtype a_dt, const void* B, void* C, re
 size_t gemm_workspace_bytes(int M, int N, int K);
 hipError_t launch_gemm_ws(const void* A, ret_dtype a_dt, const void* B, void* C, ret_dtype c_dt, int M, int N, int K,
                           const void* R, ret_dtype r_dt, int act, void* ws, hipStream_t st);
+// device address of the static split-K scratch of the current device
+// (MSR_GEMM_SCRATCH_BYTES, looked up once per device)
+hipError_t gemm_scratch_ptr(void** out);
 hipError_t launch_layer_norm(const void* x, void* y, int rows, int d, const float* w, const float* bias, float eps,
                              ret_dtype x_dt, ret_dtype y_dt, hipStream_t st);
 

@@ -279,3 +279,16 @@ def test_calib_validation(B):
     assert L.ret_calib_mfma(None, 1, 1, None) == 1
     assert L.ret_calib_mfma(ctypes.c_void_p(0x100000), 0, 1, None) == 1
     assert L.ret_calib_mfma(ctypes.c_void_p(0x100001), 1, 1, None) == 3
+
+
+def test_gemm_scratch_validation(B):
+    L = B.LIB
+    A, Bm, C = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    # partials of 128 x 131072 fp32 (one slice) exceed the 32 MiB scratch: rejected before any HIP call
+    assert L.msr_gemm_scratch(A, 1, Bm, C, 0, 128, 131072, 128, None, 0, 0, None) == 4
+    assert "scratch" in L.retention_last_error().decode()
+    assert L.msr_gemm_scratch(A, 1, Bm, C, 0, 16, 16, 48, None, 0, 0, None) == 2      # K % 32
+    assert L.msr_gemm_scratch(A, 1, Bm, A, 0, 16, 16, 64, None, 0, 0, None) == 1      # alias
+    assert L.msr_gemm_scratch(A, 1, Bm, C, 0, 16, 16, 64, None, 0, 8, None) == 1      # epilogue bit
+    assert B.gemm_workspace_bytes(128, 16384, 4096) <= B.LIB_SCRATCH_BYTES
+    assert B.gemm_workspace_bytes(128, 65536, 4096) <= B.LIB_SCRATCH_BYTES
