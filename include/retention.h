@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define RETENTION_ABI_VERSION 1
+#define RETENTION_ABI_VERSION 2
 
 typedef enum {
   RET_OK = 0,
@@ -46,7 +46,8 @@ typedef enum {
   RET_E_UNSUPPORTED = 2,  /* a shape or dtype combination without a compiled kernel */
   RET_E_ALIGN = 3,        /* a pointer or stride breaks the required alignment */
   RET_E_WORKSPACE = 4,    /* workspace missing or too small */
-  RET_E_HIP = 5           /* a HIP launch failed; the message names the HIP error */
+  RET_E_HIP = 5,          /* a HIP launch failed; the message names the HIP error */
+  RET_E_RANGE = 6         /* retention_range_status: a call wrote non-finite results */
 } ret_status;
 
 typedef enum { RET_F32 = 0, RET_BF16 = 1, RET_F16 = 2 } ret_dtype;
@@ -318,6 +319,31 @@ int msr_gemm_scratch(const void* A, ret_dtype a_dt, const void* B, void* C, ret_
  */
 int ret_layer_norm(const void* x, void* y, int rows, int d, const float* weight, const float* bias, float eps,
                    ret_dtype x_dt, ret_dtype y_dt, hipStream_t stream);
+
+/*
+ * retention_range_status -- reports whether retention_chunkwise_fwd,
+ * retention_parallel_fwd or retention_chunkwise_bwd wrote any non-finite
+ * value (NaN, inf, or a value beyond the output type's range) since the
+ * previous query on this device, and clears that record.
+ *
+ * The fp16 operands of the bf16 / f16 paths ([notes] §2.3, §2.4: every
+ * product of the rotated q', k' with each other and with v) hold at most
+ * 65504; an operand beyond that (for instance |v| >= 65520) becomes inf, and
+ * inf reaches every output it feeds, as inf or NaN.  The kernels test every
+ * value they store and set a per-device record when one is not finite, so an
+ * out-of-range input surfaces here instead of passing silently.  Non-finite
+ * inputs are reported the same way.
+ *
+ * Returns RET_OK when nothing non-finite was written, RET_E_RANGE when
+ * something was (retention_last_error() says whether by a forward or a
+ * backward call), RET_E_HIP on a HIP failure.  The query enqueues a one-thread
+ * kernel and a 4-byte copy on `stream` and waits for `stream`: calls enqueued
+ * on `stream` before it are covered; calls on other streams are covered once
+ * they have completed (order them before the query with events).  The record
+ * is one word per device, shared by all callers: concurrent queries on one
+ * device split the record between them.  It allocates nothing.
+ */
+int retention_range_status(hipStream_t stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* retention_last_error(void);

@@ -21,7 +21,7 @@ XPOS, SCALE_QK, NORM_DROW, NORM_SCORE = 1, 2, 4, 8
 NORM_ALL = SCALE_QK | NORM_DROW | NORM_SCORE
 RET_F32, RET_BF16, RET_F16 = 0, 1, 2
 STATUS = {0: "RET_OK", 1: "RET_E_INVAL", 2: "RET_E_UNSUPPORTED", 3: "RET_E_ALIGN",
-          4: "RET_E_WORKSPACE", 5: "RET_E_HIP"}
+          4: "RET_E_WORKSPACE", 5: "RET_E_HIP", 6: "RET_E_RANGE"}
 
 
 class Strides(ctypes.Structure):
@@ -77,6 +77,8 @@ def load_library(path=LIB_PATH):
     lib.ret_calib_copy.restype = i32
     lib.ret_calib_mfma.argtypes = [vp, i32, i32, vp]
     lib.ret_calib_mfma.restype = i32
+    lib.retention_range_status.argtypes = [vp]
+    lib.retention_range_status.restype = i32
     lib.retention_last_error.argtypes = []
     lib.retention_last_error.restype = ctypes.c_char_p
     lib.retention_abi_version.argtypes = []
@@ -92,6 +94,17 @@ def _check(status, what):
     if status != 0:
         msg = LIB.retention_last_error().decode()
         raise RuntimeError(f"{what} failed with {STATUS.get(status, status)}: {msg}")
+
+
+def range_status(stream=None):
+    """None when no retention call on the current device wrote a non-finite
+    value since the last query, else the library's message naming the forward
+    and / or backward call (the record is cleared; the stream is waited for)."""
+    st = LIB.retention_range_status(_stream(stream))
+    if st == 6:
+        return LIB.retention_last_error().decode()
+    _check(st, "retention_range_status")
+    return None
 
 
 def _dt(t):

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "retention_calib.h"
 
@@ -87,6 +89,35 @@ void fill_params(ret::HeadParams& hp, const double* gamma, int h, const double* 
 
 }  // namespace
 
+// ---------------------------------------------------------------- non-finite flag
+// word 0: bits OR-ed in by kernels that wrote a non-finite output; word 1: the
+// value taken by the last retention_range_status() (read back by the host)
+namespace {
+__device__ __align__(16) unsigned g_nf[4];
+std::mutex g_nf_mu;
+unsigned* g_nf_ptr[64];
+
+__global__ void take_nonfinite_kernel(unsigned* w) { w[1] = atomicExch(&w[0], 0u); }
+}  // namespace
+
+namespace ret {
+hipError_t nonfinite_flag_ptr(unsigned** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_nf_mu);
+  if (!g_nf_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_nf));
+    if (e != hipSuccess) return e;
+    g_nf_ptr[dev] = static_cast<unsigned*>(p);
+  }
+  *out = g_nf_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace ret
+
 extern "C" {
 
 int retention_abi_version(void) { return RETENTION_ABI_VERSION; }
@@ -159,6 +190,8 @@ int retention_chunkwise_fwd(const void* q, ret_strides sq, const void* k, ret_st
   a.pos0 = pos0; a.n_prev = n_prev; a.flags = flags; a.in_dt = in_dt; a.out_dt = out_dt;
   a.state_in = state_in; a.z_in = z_in; a.state_out = state_out; a.z_out = z_out;
   a.ws = workspace; a.ws_bytes = workspace_bytes; a.hp = &hp;
+  hipError_t fe = ret::nonfinite_flag_ptr(&a.nf);
+  if (fe != hipSuccess) return hip_status(fe, "retention_chunkwise_fwd flag lookup");
   bool sup = true;
   hipError_t e = ret::launch_chunkwise(a, stream, &sup);
   if (!sup) return fail(RET_E_UNSUPPORTED, "no chunkwise kernel for this shape");
@@ -250,6 +283,8 @@ int retention_chunkwise_bwd(const void* q, ret_strides sq, const void* k, ret_st
   a.b = b; a.h = h; a.L = L; a.d_k = d_k; a.d_v = d_v; a.B = chunk_B;
   a.pos0 = pos0; a.flags = flags; a.in_dt = in_dt; a.grad_dt = grad_dt;
   a.ws = workspace; a.hp = &hp;
+  const hipError_t fe = ret::nonfinite_flag_ptr(&a.nf);
+  if (fe != hipSuccess) return hip_status(fe, "retention_chunkwise_bwd flag lookup");
   return hip_status(ret::launch_chunkwise_bwd(a, stream), "retention_chunkwise_bwd launch");
 }
 
@@ -394,6 +429,22 @@ int ret_layer_norm(const void* x, void* y, int rows, int d, const float* weight,
   if (x == y) return fail(RET_E_INVAL, "y must not alias x");
   return hip_status(ret::launch_layer_norm(x, y, rows, d, weight, bias, eps, x_dt, y_dt, stream),
                     "ret_layer_norm launch");
+}
+
+int retention_range_status(hipStream_t stream) {
+  unsigned* w = nullptr;
+  hipError_t e = ret::nonfinite_flag_ptr(&w);
+  if (e != hipSuccess) return hip_status(e, "retention_range_status flag lookup");
+  hipLaunchKernelGGL(take_nonfinite_kernel, dim3(1), dim3(1), 0, stream, w);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_status(e, "retention_range_status launch");
+  unsigned taken = 0;
+  if ((e = hipMemcpyAsync(&taken, w + 1, sizeof(taken), hipMemcpyDeviceToHost, stream)) != hipSuccess)
+    return hip_status(e, "retention_range_status copy");
+  if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_status(e, "retention_range_status sync");
+  if (taken == 0) return ok();
+  return fail(RET_E_RANGE, "non-finite values were written by %s%s%s", (taken & ret::kNonFiniteFwd) ? "a forward call" : "",
+              (taken & ret::kNonFiniteFwd) && (taken & ret::kNonFiniteBwd) ? " and " : "",
+              (taken & ret::kNonFiniteBwd) ? "a backward call" : "");
 }
 
 int ret_calib_copy(const void* src, void* dst, size_t n16, hipStream_t stream) {

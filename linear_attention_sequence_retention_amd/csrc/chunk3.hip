@@ -145,6 +145,7 @@ struct P3 {
   unsigned flags;
   const float *state_in, *z_in;
   float *state_out, *z_out;
+  unsigned* nf;
   Work w;
 };
 
@@ -1140,6 +1141,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     constexpr int OV = 16 / (int)sizeof(TO);        // elements per 16 bytes
     constexpr int OP = DV + OV;                     // staging row pitch
     static_assert(TR * OP * sizeof(TO) <= offsetof(OutSmem, Ps), "staging overlaps live LDS");
+    bool bad = false;
   #pragma unroll
     for (int qh = 0; qh < 2; ++qh)
   #pragma unroll
@@ -1148,9 +1150,12 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = qh * 32 + acc_row(r, lane);
-          Os[row * OP + col] = Store<TO>::cvt(O[qh][jj][r] * sm.rs[row]);
+          const float x = O[qh][jj][r] * sm.rs[row];
+          bad |= row < qvalid && nonfinite_as<TO>(x);
+          Os[row * OP + col] = Store<TO>::cvt(x);
         }
       }
+    flag_nonfinite(p.nf, bad, kNonFiniteFwd);
     __syncthreads();
     for (int e = tid; e < TR * (DV / OV); e += NT3) {
       const int row = e / (DV / OV), cv = e % (DV / OV);
@@ -1193,6 +1198,7 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
   p.nbh = a.b * a.h;
   p.pos0 = a.pos0; p.n_prev = a.n_prev; p.flags = a.flags;
   p.state_in = a.state_in; p.z_in = a.z_in; p.state_out = a.state_out; p.z_out = a.z_out;
+  p.nf = a.nf;
   const int bh = a.b * a.h;
   carve(a.ws, bh, a.L, a.B, &p.w);
   hipError_t e;

@@ -61,6 +61,7 @@ struct BwdP {
   float *rmax, *umax;            // [bh][nc][partial maxima] of |R_c| and |U_c|
   float *Rin, *zin, *Ust, *ust;  // [bh][nc][DK][DV] and [bh][nc][DK]
   float *ra, *rc;                // [bh][L]: a_p and c_p (with the score normalisation)
+  unsigned* nf;                  // non-finite output flag word
 };
 
 // ------------------------------------------------------------ fp16 packing
@@ -581,14 +582,17 @@ __device__ __forceinline__ void store_rotated(const float* t, TG* out, const ret
     phase(RPP, hp.theta[j], c1, s1);
   }
   TG* o = out + bb * so.b + hh * so.h;
+  bool bad = false;
   for (int i = i0; i < nrows; i += RPP) {
     float x0 = gs * t[i * TP + 2 * j], x1 = gs * t[i * TP + 2 * j + 1];
     if (xpos) {
       rot(x0, x1, c, -s);
       advance(c, s, c1, s1);
     }
+    bad |= nonfinite_as<TG>(x0) | nonfinite_as<TG>(x1);
     Out2<TG>::st(o + (int64_t)(r0 + i) * so.l + 2 * j, x0, x1);
   }
+  flag_nonfinite(p.nf, bad, kNonFiniteBwd);
 }
 
 // ------------------------------------------------------------ dq
@@ -1097,13 +1101,19 @@ __global__ void __launch_bounds__(BT) bwd_dv_kernel(BwdP p, HeadParams hp) {
   }
   TG* o = reinterpret_cast<TG*>(p.dv) + bb * p.sdv.b + head * p.sdv.h;
   const float gs = p.gsc[bh];
+  bool bad = false;
 #pragma unroll
   for (int es = 0; es < NEH; ++es)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ml = 32 * bi + acc_row(r, lane);
-      if (ml < nk) o[(int64_t)(m0 + ml) * p.sdv.l + e0 + 64 * es + 32 * bj + l32] = Store<TG>::cvt(gs * acc[es][r]);
+      if (ml < nk) {
+        const float x = gs * acc[es][r];
+        bad |= nonfinite_as<TG>(x);
+        o[(int64_t)(m0 + ml) * p.sdv.l + e0 + 64 * es + 32 * bj + l32] = Store<TG>::cvt(x);
+      }
     }
+  flag_nonfinite(p.nf, bad, kNonFiniteBwd);
 }
 
 // ------------------------------------------------------------ host side
@@ -1150,7 +1160,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t st) {
   p.h = a.h; p.L = a.L; p.B = a.B;
   p.nc = (a.L + a.B - 1) / a.B;
   p.nt = (a.L + TL - 1) / TL;
-  p.pos0 = a.pos0; p.flags = a.flags;
+  p.pos0 = a.pos0; p.flags = a.flags; p.nf = a.nf;
   const Carve cv = carve_bwd(a.b, a.h, a.L, DK, DV, a.B);
   unsigned char* w = static_cast<unsigned char*>(a.ws);
   p.Qr = reinterpret_cast<uint16_t*>(w + cv.qr);

@@ -67,6 +67,7 @@ struct KParams {
   unsigned flags;
   const float *state_in, *z_in;
   float *state_out, *z_out;
+  unsigned* nf;
 };
 
 // Raw pair loads (two consecutive input elements) kept in one register
@@ -494,13 +495,17 @@ __global__ void __launch_bounds__(NT, 1) chunkwise_kernel(KParams p, HeadParams 
       __syncthreads();
       // coalesced store: each thread writes 4 consecutive columns of a row
       constexpr int C4 = SV / 4;
+      bool bad = false;
       for (int e = tid; e < TR * C4; e += NT) {
         const int row = e / C4, c4 = e % C4;
         if (row < qvalid) {
           const float* src = sm.Oc + row * CPITCH + 4 * c4;
+          bad |= nonfinite_as<TO>(src[0]) | nonfinite_as<TO>(src[1]) | nonfinite_as<TO>(src[2]) |
+                 nonfinite_as<TO>(src[3]);
           store4(Og + (int64_t)(c0 + r0 + row) * p.so.l + 4 * c4, src);
         }
       }
+      flag_nonfinite(p.nf, bad, kNonFiniteFwd);
     }
     job = nj;
   }
@@ -539,6 +544,7 @@ static hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
   p.h = a.h; p.L = a.L; p.B = a.B; p.nslice = DV / SV;
   p.pos0 = a.pos0; p.n_prev = a.n_prev; p.flags = a.flags;
   p.state_in = a.state_in; p.z_in = a.z_in; p.state_out = a.state_out; p.z_out = a.z_out;
+  p.nf = a.nf;
   if (fused_z_snapshot(a)) {
     // every d_v slice of a head reads z_in, and slice 0 writes z_out when it
     // ends: with z_out over z_in, a slice that starts after its head's slice 0

@@ -4,16 +4,34 @@
 
 namespace ret {
 
+// kLim: the smallest magnitude that is no longer finite once converted to TO
+// with round-to-nearest-even (half: 65504 + half an ulp; bf16 likewise)
 template <typename TO> struct Store;
 template <> struct Store<float> {
+  static constexpr float kLim = __builtin_huge_valf();
   __device__ __forceinline__ static float cvt(float x) { return x; }
 };
 template <> struct Store<bf16> {
+  static constexpr float kLim = 0x1.ffp127f;
   __device__ __forceinline__ static bf16 cvt(float x) { return bf16{f2bf(x)}; }
 };
 template <> struct Store<half> {
+  static constexpr float kLim = 65520.f;
   __device__ __forceinline__ static half cvt(float x) { return (half)x; }
 };
+// true when x, written as TO, is not a finite number (NaN, inf or beyond TO's range)
+template <typename TO> __device__ __forceinline__ bool nonfinite_as(float x) { return !(fabsf(x) < Store<TO>::kLim); }
+
+// Non-finite output flag: kernels that write a non-finite result OR their bit
+// into a per-device word (nf), which retention_range_status() reads and clears.
+// An fp16 operand that overflowed its range becomes inf and reaches every
+// output it feeds, so this is how such an overflow surfaces.
+enum : unsigned { kNonFiniteFwd = 1u, kNonFiniteBwd = 2u };
+__device__ __forceinline__ void flag_nonfinite(unsigned* nf, bool bad, unsigned bit) {
+  if (bad && nf) atomicOr(nf, bit);
+}
+// the per-device flag word (device address, looked up once per device)
+hipError_t nonfinite_flag_ptr(unsigned** out);
 
 // four consecutive outputs (8-byte aligned for 16-bit types, 16 for float)
 __device__ __forceinline__ void store4(float* p, const float* x) {
@@ -69,6 +87,7 @@ struct ChunkArgs {
   void* ws;
   size_t ws_bytes;
   const HeadParams* hp;
+  unsigned* nf;     // non-finite output flag word
 };
 // returns false in *supported when no kernel is compiled for the shape
 hipError_t launch_chunkwise(const ChunkArgs& a, hipStream_t st, bool* supported);
@@ -93,6 +112,7 @@ struct BwdArgs {
   ret_dtype in_dt, grad_dt;
   void* ws;
   const HeadParams* hp;
+  unsigned* nf;     // non-finite output flag word
 };
 bool chunkwise_bwd_supported(int dk, int dv);
 size_t chunkwise_bwd_workspace(int b, int h, int L, int dk, int dv, int B);

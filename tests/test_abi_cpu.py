@@ -29,10 +29,22 @@ def declared_functions():
 def test_exports_every_declared_symbol(B):
     names = declared_functions()
     assert {"retention_chunkwise_fwd", "retention_recurrent_step", "msr_gate_norm", "msr_gemm",
-            "msr_gemm_bf16", "ret_calib_copy", "ret_calib_mfma"} <= set(names)
+            "msr_gemm_bf16", "ret_calib_copy", "ret_calib_mfma", "retention_range_status"} <= set(names)
     for n in names:
         assert hasattr(B.LIB, n), f"libretention.so does not export {n}"
-    assert B.LIB.retention_abi_version() == 1
+    assert B.LIB.retention_abi_version() == 2
+
+
+def test_range_status_without_device(B):
+    """The non-finite-record query on a host without a GPU: the device lookup
+    fails and the call returns RET_E_HIP with the lookup named, no crash; the
+    binding maps RET_E_RANGE (6) to its name."""
+    st = B.LIB.retention_range_status(None)
+    assert st == 5
+    assert "flag lookup" in B.LIB.retention_last_error().decode()
+    assert B.STATUS[6] == "RET_E_RANGE"
+    hdr = open(HEADERS[0]).read()
+    assert "RET_E_RANGE = 6" in hdr and "#define RETENTION_ABI_VERSION 2" in hdr
 
 
 def _dptr(a):
