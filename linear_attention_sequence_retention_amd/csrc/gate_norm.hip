@@ -1,7 +1,7 @@
 // MSR epilogue before W_O (RetNet reading notes, §三.2):
 //   Z = swish(G) (.) GroupNorm_h(Concat(head_1 .. head_h))
-// One wave per (batch, token, head) group of d_v channels: the group is held
-// in registers (8 channels per lane per 512-wide slab), its mean and biased
+// One wave per GP (batch, token, head) groups of d_v channels: each group is
+// held in registers (8 channels per lane per 512-wide slab), its mean and biased
 // variance come from two wave reductions (centred second pass), and the
 // normalised, gated result is written once.  HBM-bound: Y and G are read
 // once and Z written once.
@@ -10,9 +10,11 @@
 namespace ret {
 
 template <typename T> struct Vec8;
+// Every byte is touched once, so the 16-bit types load and store non-temporally
+// (no reuse to keep in the caches).
 template <> struct Vec8<bf16> {
   __device__ __forceinline__ static void ld(const bf16* p, float* x) {
-    u32x4 u = *reinterpret_cast<const u32x4*>(p);
+    u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     x[0] = lo_bf(u.x); x[1] = hi_bf(u.x); x[2] = lo_bf(u.y); x[3] = hi_bf(u.y);
     x[4] = lo_bf(u.z); x[5] = hi_bf(u.z); x[6] = lo_bf(u.w); x[7] = hi_bf(u.w);
   }
@@ -20,12 +22,12 @@ template <> struct Vec8<bf16> {
     u32x4 u;
     u.x = pack_bf2(x[0], x[1]); u.y = pack_bf2(x[2], x[3]);
     u.z = pack_bf2(x[4], x[5]); u.w = pack_bf2(x[6], x[7]);
-    *reinterpret_cast<u32x4*>(p) = u;
+    __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
   }
 };
 template <> struct Vec8<half> {
   __device__ __forceinline__ static void ld(const half* p, float* x) {
-    f16x8 v = *reinterpret_cast<const f16x8*>(p);
+    f16x8 v = __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(p));
 #pragma unroll
     for (int j = 0; j < 8; ++j) x[j] = (float)v[j];
   }
@@ -33,7 +35,7 @@ template <> struct Vec8<half> {
     f16x8 v;
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = (half)x[j];
-    *reinterpret_cast<f16x8*>(p) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<f16x8*>(p));
   }
 };
 template <> struct Vec8<float> {
@@ -48,63 +50,84 @@ template <> struct Vec8<float> {
   }
 };
 
-template <typename TY, typename TG, typename TO, int NI>
+template <typename TY, typename TG, typename TO, int NI, int GP>
 __global__ void __launch_bounds__(256)
 gate_norm_kernel(const TY* __restrict__ y, ret_strides sy, const TG* __restrict__ g, TO* __restrict__ out,
                  int L, int h, int dv, int64_t ngroups, const float* __restrict__ w,
                  const float* __restrict__ bias, float eps) {
   const int lane = threadIdx.x & 63;
-  const int64_t gi = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (gi >= ngroups) return;
-  const int hh = (int)(gi % h);
-  const int64_t bt = gi / h;
-  const int t = (int)(bt % L);
-  const int bb = (int)(bt / L);
-  const TY* yp = y + bb * sy.b + hh * sy.h + (int64_t)t * sy.l;
-  const int64_t row = gi * dv;   // offset of this group in G and Z
-  // the gate is requested with y, so its latency overlaps the two reductions
-  float x[NI][8], gg[NI][8];
-  float sum = 0.f;
+  const int64_t g0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * GP;
+  if (g0 >= ngroups) return;
+  // every load of the wave's GP groups is issued before the first reduction,
+  // so GP * NI * 2 16-byte requests per lane are in flight together (two
+  // groups of 512 measured best: more cost occupancy, 8 waves per SIMD)
+  float x[GP][NI][8], gg[GP][NI][8];
+  float sum[GP];
 #pragma unroll
-  for (int it = 0; it < NI; ++it) {
-    const int e = 8 * lane + 512 * it;
-    if (e < dv) {
-      Vec8<TY>::ld(yp + e, x[it]);
-      Vec8<TG>::ld(g + row + e, gg[it]);
+  for (int k = 0; k < GP; ++k) {
+    const int64_t gi = g0 + k;
+    sum[k] = 0.f;
+    if (gi < ngroups) {
+      const int hh = (int)(gi % h);
+      const int64_t bt = gi / h;
+      const TY* yp = y + (bt / L) * sy.b + hh * sy.h + (bt % L) * sy.l;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sum += x[it][j];
+      for (int it = 0; it < NI; ++it) {
+        const int e = 8 * lane + 512 * it;
+        if (e < dv) {
+          Vec8<TY>::ld(yp + e, x[k][it]);
+          Vec8<TG>::ld(g + gi * dv + e, gg[k][it]);
+        }
+      }
     }
   }
   const float inv_n = 1.f / (float)dv;
-  const float mean = wave_sum(sum) * inv_n;
-  float sq = 0.f;
+  float mean[GP], rstd[GP];
 #pragma unroll
-  for (int it = 0; it < NI; ++it) {
-    const int e = 8 * lane + 512 * it;
-    if (e < dv) {
+  for (int k = 0; k < GP; ++k) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float d = x[it][j] - mean;
-        sq += d * d;
+    for (int it = 0; it < NI; ++it)
+      if (8 * lane + 512 * it < dv) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum[k] += x[k][it][j];
       }
-    }
+    mean[k] = wave_sum(sum[k]) * inv_n;
   }
-  const float rstd = rsqrtf(wave_sum(sq) * inv_n + eps);
 #pragma unroll
-  for (int it = 0; it < NI; ++it) {
-    const int e = 8 * lane + 512 * it;
-    if (e < dv) {
-      float r[8];
+  for (int k = 0; k < GP; ++k) {
+    float sq = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float yn = (x[it][j] - mean) * rstd;
-        const int c = hh * dv + e + j;
-        if (w) yn *= w[c];
-        if (bias) yn += bias[c];
-        const float sw = gg[it][j] / (1.f + __expf(-gg[it][j]));
-        r[j] = sw * yn;
+    for (int it = 0; it < NI; ++it)
+      if (8 * lane + 512 * it < dv) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float d = x[k][it][j] - mean[k];
+          sq += d * d;
+        }
       }
-      Vec8<TO>::st(out + row + e, r);
+    rstd[k] = rsqrtf(wave_sum(sq) * inv_n + eps);
+  }
+#pragma unroll
+  for (int k = 0; k < GP; ++k) {
+    const int64_t gi = g0 + k;
+    if (gi >= ngroups) break;
+    const int hh = (int)(gi % h);
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int e = 8 * lane + 512 * it;
+      if (e < dv) {
+        float r[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float yn = (x[k][it][j] - mean[k]) * rstd[k];
+          const int c = hh * dv + e + j;
+          if (w) yn *= w[c];
+          if (bias) yn += bias[c];
+          const float sw = gg[k][it][j] / (1.f + __expf(-gg[k][it][j]));
+          r[j] = sw * yn;
+        }
+        Vec8<TO>::st(out + gi * dv + e, r);
+      }
     }
   }
 }
@@ -112,15 +135,15 @@ gate_norm_kernel(const TY* __restrict__ y, ret_strides sy, const TG* __restrict_
 template <typename TY, typename TG, typename TO>
 static hipError_t launch_gn_t(const GateArgs& a, hipStream_t st) {
   const int64_t ng = (int64_t)a.b * a.L * a.h;
-  dim3 grid((unsigned)((ng + 3) / 4));
   const int ni = (a.dv + 511) / 512;
-#define RET_GN(NI)                                                                               \
-  hipLaunchKernelGGL((gate_norm_kernel<TY, TG, TO, NI>), grid, dim3(256), 0, st, (const TY*)a.y, \
-                     a.sy, (const TG*)a.g, (TO*)a.out, a.L, a.h, a.dv, ng, a.w, a.bias, a.eps)
-  if (ni <= 1) RET_GN(1);
-  else if (ni <= 2) RET_GN(2);
-  else if (ni <= 4) RET_GN(4);
-  else RET_GN(8);
+#define RET_GN(NI, GP)                                                                               \
+  hipLaunchKernelGGL((gate_norm_kernel<TY, TG, TO, NI, GP>), dim3((unsigned)((ng + 4 * GP - 1) / (4 * GP))), \
+                     dim3(256), 0, st, (const TY*)a.y, a.sy, (const TG*)a.g, (TO*)a.out, a.L, a.h, a.dv, ng, \
+                     a.w, a.bias, a.eps)
+  if (ni <= 1) RET_GN(1, 2);
+  else if (ni <= 2) RET_GN(2, 1);
+  else if (ni <= 4) RET_GN(4, 1);
+  else RET_GN(8, 1);
 #undef RET_GN
   return hipGetLastError();
 }
