@@ -378,20 +378,34 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   amax = maxabs_block(amax, reinterpret_cast<float*>(&sm.Vh[0][0]));
   const int e = scale_exp(amax);
   const float down = ldexpf(1.f, -e);
-  half* dR = p.w.dR + ((int64_t)bh * p.nc + c) * DV * DK;
+  // the workgroup's 256 columns of dR are one contiguous 128 KB block ([col][d]):
+  // staged in LDS (over the dead tiles; pitch 2 mod 64 dwords, so the 32 columns
+  // of a write fall in distinct bank pairs), then written with 16-byte stores
+  constexpr int RP = DK + 4;
+  static_assert(256 * RP * sizeof(half) <= sizeof(sm.Kz) + sizeof(sm.Vh), "dR staging exceeds the tiles");
+  half* Rst = &sm.Kz[0][0];
+  __syncthreads();                                  // the reductions' LDS reads are done
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int col = half_ * 256 + n0 + 32 * jj + (lane & 31);
+      const int col = n0 + 32 * jj + (lane & 31);
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int d = d0 + 32 * i + 8 * rg + 4 * (lane >> 5);   // acc rows 4*rg .. 4*rg+3 are d .. d+3
         float x[4] = {acc[i][jj][4 * rg] * down, acc[i][jj][4 * rg + 1] * down, acc[i][jj][4 * rg + 2] * down,
                       acc[i][jj][4 * rg + 3] * down};
-        st4(dR + (int64_t)col * DK + d, x);
+        st4(Rst + col * RP + d, x);
       }
     }
+  __syncthreads();
+  half* dR = p.w.dR + (((int64_t)bh * p.nc + c) * DV + half_ * 256) * DK;
+#pragma unroll
+  for (int i = 0; i < 256 * DK / 8 / NT3; ++i) {
+    const int e = tid + i * NT3;
+    const int col = e >> 5, piece = e & 31;
+    *reinterpret_cast<u32x4*>(dR + (int64_t)e * 8) = *reinterpret_cast<const u32x4*>(Rst + col * RP + piece * 8);
+  }
   if (tid == 0) p.w.dRs[((int64_t)bh * p.nc + c) * 2 + half_] = ldexpf(1.f, e);
   if (half_ == 0 && tid < DK) p.w.dz[((int64_t)bh * p.nc + c) * DK + tid] = sm.dzs[tid];
 }
@@ -953,7 +967,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     issue_v(rt);
     __syncthreads();                                // the query tile and the row tables
     {
-      constexpr int NSX = DK / 16, XR = 4;
+      constexpr int NSX = DK / 16, XR = 6;
       const half* rp = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK + (int64_t)(2 * wave * NSX * 64 + lane) * 8;
       f16x8 rb[XR][2], qa[2][2];
   #pragma unroll
