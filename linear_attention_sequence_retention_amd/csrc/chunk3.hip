@@ -816,9 +816,17 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   // the query tile of an item, as raw element pairs: thread -> pair column
   // tid % 128 of rows 16 (tid / 128) + 0..15.  The next item's tile is loaded
   // while the current item is normalised and stored.
+  // (with it, the item's key-sum z_{c-1} (thread -> d) and the power-of-two
+  // scales of this wave's two state column blocks, used in the rotation and
+  // after the cross term)
   uint32_t qraw[16];
+  float zpre_n, up0_n, up1_n;
   auto issue_q = [&](int rt, int c, int bh) {
     const int j = threadIdx.x & 127, grp = threadIdx.x >> 7;
+    const int64_t ci = (int64_t)bh * p.nc + c;
+    zpre_n = p.w.zc[ci * DK + (threadIdx.x & (DK - 1))];
+    up0_n = p.w.Rs[ci * NCB + 2 * (threadIdx.x >> 6)];
+    up1_n = p.w.Rs[ci * NCB + 2 * (threadIdx.x >> 6) + 1];
     const int bb = bh / p.h, head = bh % p.h;
     const int r0 = rt * TR;
     const int qvalid = min(TR, min(p.B, p.L - c * p.B) - r0);
@@ -855,12 +863,8 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     const float qk_scale = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
 
     const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + (int64_t)c0 * p.sv.l;
-    // z_{c-1} (thread -> d) and the power-of-two scales of this wave's two
-    // state column blocks, requested first: they are used after the query
-    // rotation and after the cross term
-    const int64_t ci = (int64_t)bh * p.nc + c;
-    const float zpre = p.w.zc[ci * DK + (tid & (DK - 1))];
-    const float up0 = p.w.Rs[ci * NCB + 2 * wave], up1 = p.w.Rs[ci * NCB + 2 * wave + 1];
+    // z_{c-1} and the state scales, requested with the query tile
+    const float zpre = zpre_n, up0 = up0_n, up1 = up1_n;
     const half* Kt = p.w.kt + ((int64_t)bh * p.L + c0) * DK;
     TO* Og = reinterpret_cast<TO*>(p.o) + bb * p.so.b + head * p.so.h + (int64_t)(c0 + r0) * p.so.l;
 
