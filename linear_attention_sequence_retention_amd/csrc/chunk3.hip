@@ -265,6 +265,8 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   auto stage = [&](int kt, int buf) {
     const int k0 = kt * TK;
     const int kvalid = min(TK, Bc - k0);
+    // a key past the end of a ragged chunk is zeroed; its value row (a copy
+    // of the last key's, from issue) then adds nothing to dR
     float x[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -294,14 +296,13 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
       if (half_ == 0 && key < kvalid) st8(ktg + (int64_t)(k0 + key) * DK + 8 * cq, x[i]);
       const float z = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key) * dec.lg2);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[i][e] *= z;
-        dzp[e] += x[i][e];
+      for (int e = 0; e < 8; ++e) x[i][e] *= z;
+      if (half_ == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dzp[e] += x[i][e];
       }
       st8(sm.Kz[buf] + key * DP + 8 * cq, x[i]);
-      u32x4 v = Raw16<T>::f16(vr[i]);
-      if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(sm.Vh[buf] + key * DP + 8 * cq) = v;
+      *reinterpret_cast<u32x4*>(sm.Vh[buf] + key * DP + 8 * cq) = Raw16<T>::f16(vr[i]);
     }
   };
   auto mma = [&](int buf) {
@@ -769,6 +770,11 @@ struct OutSmem {
   float dpart[2][TR];       // within-chunk row sums of key halves 0 / 1
   float zs[DK];
   float ginv[32];           // gamma^-m, m = 0 .. 31
+  // per pair, set once per workgroup: theta and e^{i theta} (an fp64 load
+  // from global memory inside an item would wait for the previous item's
+  // output stores as well: the vector memory counter completes in order)
+  double theta[DK / 2];
+  float2 step1[DK / 2];
 };
 
 template <typename T, typename TO>
@@ -830,13 +836,26 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     const int bb = bh / p.h, head = bh % p.h;
     const int r0 = rt * TR;
     const int qvalid = min(TR, min(p.B, p.L - c * p.B) - r0);
-    const T* Qg = reinterpret_cast<const T*>(p.q) + bb * p.sq.b + head * p.sq.h + (int64_t)(c * p.B + r0) * p.sq.l;
+    const char* Qg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(p.q) + bb * p.sq.b + head * p.sq.h +
+                                                   (int64_t)(c * p.B + r0) * p.sq.l);
+    // a 32-bit byte offset from the tile origin (strides < 2^25 elements),
+    // stepped one row per load and held at the tile's last valid row
+    const uint32_t rowb = (uint32_t)p.sq.l * 2u;
+    uint32_t off = (uint32_t)min(grp * 16, qvalid - 1) * rowb + 4u * (uint32_t)j;
   #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int rc = min(grp * 16 + i, qvalid - 1);
-      qraw[i] = *reinterpret_cast<const uint32_t*>(Qg + (uint32_t)(rc * (int)p.sq.l + 2 * j));
+      qraw[i] = *reinterpret_cast<const uint32_t*>(Qg + off);
+      if (grp * 16 + i + 1 < qvalid) off += rowb;
     }
   };
+  if ((p.flags & RET_XPOS) && threadIdx.x < DK / 2) {
+    OutSmem& sm = *reinterpret_cast<OutSmem*>(smem_raw);
+    const double th = hp.theta[threadIdx.x];
+    float2 t;
+    phase(1, th, t.x, t.y);
+    sm.theta[threadIdx.x] = th;
+    sm.step1[threadIdx.x] = t;
+  }
   int k = 0, rt = 0, c = 0, bh = 0;
   while (k < nk && !decode(k, rt, c, bh)) ++k;
   if (k < nk) issue_q(rt, c, bh);
@@ -881,8 +900,10 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       }
       float cs = 1.f, sn = 0.f, c1 = 1.f, s1 = 0.f;
       if (xpos) {
-        phase(p.pos0 + c0 + r0 + grp * 16, hp.theta[j], cs, sn);
-        phase(1, hp.theta[j], c1, s1);
+        phase(p.pos0 + c0 + r0 + grp * 16, sm.theta[j], cs, sn);
+        const float2 t = sm.step1[j];
+        c1 = t.x;
+        s1 = t.y;
       }
   #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -1175,11 +1196,16 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       }
     flag_nonfinite(p.nf, bad, kNonFiniteFwd);
     __syncthreads();
-    for (int e = tid; e < TR * (DV / OV); e += NT3) {
-      const int row = e / (DV / OV), cv = e % (DV / OV);
-      if (row < qvalid)
-        *reinterpret_cast<u32x4*>(Og + (int64_t)row * p.so.l + cv * OV) =
-            *reinterpret_cast<const u32x4*>(Os + row * OP + cv * OV);
+    // a fixed number of unconditional stores per thread, with no branch
+    // around them (rows past a ragged tile rewrite its last row with the
+    // same bytes)
+    static_assert(TR * (DV / OV) % NT3 == 0, "store pieces per thread");
+  #pragma unroll
+    for (int i = 0; i < TR * (DV / OV) / NT3; ++i) {
+      const int e = tid + i * NT3;
+      const int row = min(e / (DV / OV), qvalid - 1), cv = e % (DV / OV);
+      *reinterpret_cast<u32x4*>(Og + (int64_t)row * p.so.l + cv * OV) =
+          *reinterpret_cast<const u32x4*>(Os + row * OP + cv * OV);
     }
     }
     k = kn;
