@@ -224,24 +224,6 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   // thread -> 16-byte piece cq (d or columns 8 cq .. 8 cq + 7) of keys
   // 4 (tid / 32) + 0..3 of every tile
   const int cq = tid & 31, kq = 4 * (tid >> 5);
-  float dzp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // key-sum of d 8 cq .. +7
-  // xPos phase of this thread's first key in the current tile for its four
-  // pairs, the one-key and the one-tile steps
-  float pc[4], ps[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    pc[u] = 1.f;
-    ps[u] = 0.f;
-    if (xpos) phase(p.pos0 + c0 + kq, hp.theta[4 * cq + u], pc[u], ps[u]);
-  }
-  if (xpos && tid < DK / 2) {
-    float4 t;
-    phase(1, hp.theta[tid], t.x, t.y);
-    phase(TK, hp.theta[tid], t.z, t.w);
-    sm.step[tid] = t;
-  }
-  __syncthreads();
-
   const int nkt = (Bc + TK - 1) / TK;
   u32x4 kr[4], vr[4];
   auto issue = [&](int kt) {
@@ -257,6 +239,35 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
       vr[i] = *reinterpret_cast<const u32x4*>(Vt + (uint32_t)(kc * (int)p.sv.l + 8 * cq));
     }
   };
+  // the first tile is requested before the phase set-up, which then runs
+  // under its latency; the angles are read first (the vector memory counter
+  // completes in order, so a later read would wait for the tile as well)
+  double th[4], th1 = 0.0;
+  if (xpos) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) th[u] = hp.theta[4 * cq + u];
+    if (tid < DK / 2) th1 = hp.theta[tid];
+  }
+  issue(0);
+  float dzp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // key-sum of d 8 cq .. +7
+  // xPos phase of this thread's first key in the current tile for its four
+  // pairs, the one-key and the one-tile steps
+  float pc[4], ps[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    pc[u] = 1.f;
+    ps[u] = 0.f;
+    if (xpos) phase(p.pos0 + c0 + kq, th[u], pc[u], ps[u]);
+  }
+  if (xpos && tid < DK / 2) {
+    float4 t;
+    phase(1, th1, t.x, t.y);
+    phase(TK, th1, t.z, t.w);
+    sm.step[tid] = t;
+  }
+
+  __syncthreads();
+
   // transposed-read origin of this lane (see lds_read_tr16): key 8 (lane / 32)
   // + (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
   const int tro = (8 * (lane >> 5) + ((lane & 15) >> 2)) * DP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -276,6 +287,11 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
         for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
       }
     }
+    // every load of the tile is taken here, before the first store of rotated
+    // keys: a later wait for a value load would also wait for those stores
+    // (the vector memory counter completes in order)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(vr[i]));
     if (xpos) {
       // pair-outer: each pair's phase advances once per key
 #pragma unroll
@@ -331,7 +347,6 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   };
   // two LDS buffers: tile kt + 1 is staged while tile kt is multiplied (one
   // barrier per tile); tile kt + 2 is then loaded into registers
-  issue(0);
   stage(0, 0);
   if (nkt > 1) issue(1);
   __syncthreads();
