@@ -46,7 +46,7 @@ struct Work {
   half* Rt;      // state operands     [bh][nc][DV*DK]    (R_{i-1}, fragment order, rt_frag)
   float* Rs;     // operand scales     [bh][nc][NCB]
   float* zc;     // z_{i-1}            [bh][nc][DK]
-  half* dump;    // 8 KB that masked lanes of the state scan store to (never read)
+  half* dump;    // 8 KB that masked lanes of the state scan and output kernels store to (never read)
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -71,7 +71,7 @@ size_t carve(void* base, int bh, int L, int B, Work* w) {
   const size_t o_Rt = take((size_t)bh * nc * DV * DK * 2);
   const size_t o_Rs = take((size_t)bh * nc * NCB * 4);
   const size_t o_zc = take((size_t)bh * nc * DK * 4);
-  const size_t o_dump = take(deltas ? 0 : NT3 * 16);
+  const size_t o_dump = take(NT3 * 16);
   if (w) {
     char* b = static_cast<char*>(base);
     w->kt = reinterpret_cast<half*>(b + o_kt);
@@ -991,7 +991,11 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     const int vtr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * DV + 4 * (lane & 1);
     const int vtr_sw = ((lane >> 2) & 3) << 2, vtr_lo = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 
-    // output tiles of this wave: query halves {0,1} x column tiles {2w, 2w+1}
+    // output tiles of this wave: query halves {0,1} x column tiles {2w, 2w+1},
+    // held transposed (the MFMAs take the column operand first): lane l,
+    // register r of O[qh][jj] is query qh 32 + l % 32, column (2w + jj) 32 +
+    // acc_row(r, l), so each lane holds runs of four consecutive columns of one
+    // query row, stored straight from registers
     f32x16 O[2][2];
   #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1028,7 +1032,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
         for (int qh = 0; qh < 2; ++qh)
   #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
-            O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[t & 1][qh], rb[t % XR][jj], O[qh][jj], 0, 0, 0);
+            O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rb[t % XR][jj], qa[t & 1][qh], O[qh][jj], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (t + XR < NSX) {
   #pragma unroll
@@ -1038,15 +1042,18 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       }
     }
     {
-      // row scale s xi and the operand's per-block power of two
+      // row scale s xi and the operand's per-block power of two (the lane's
+      // query row is l32 of each half)
   #pragma unroll
-      for (int qh = 0; qh < 2; ++qh)
+      for (int qh = 0; qh < 2; ++qh) {
+        const float x = sm.xs[qh * 32 + l32];
+        const float x0 = x * up0, x1 = x * up1;
   #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float x = sm.xs[qh * 32 + acc_row(r, lane)];
-          O[qh][0][r] *= x * up0;
-          O[qh][1][r] *= x * up1;
+          O[qh][0][r] *= x0;
+          O[qh][1][r] *= x1;
         }
+      }
       // cross part of the score denominator, s xi (Q' . z_{c-1}): 8 threads per row
       const int row = tid >> 3, part = tid & 7;     // d 32 part .. 32 part + 31
       float acc = 0.f;
@@ -1163,7 +1170,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
           for (int qh = 0; qh < 2; ++qh)
   #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
-              O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[t & 1][qh], bv[t & 1][jj], O[qh][jj], 0, 0, 0);
+              O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[t & 1][jj], pa[t & 1][qh], O[qh][jj], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1187,40 +1194,38 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       sm.rs[tid] = (p.flags & RET_NORM_SCORE) ? 1.f / fmaxf(fabsf(d), 1.f) : 1.f;
     }
 
-    // ---- normalise and store: the whole tile is staged in LDS in the output
-    // type (over the query / key / value buffers, dead by now), then written
-    // with 16-byte stores
+    // ---- normalise and store straight from the accumulators: per query row
+    // and column tile, four 4-column runs of the row (lanes l and l + 32 hold
+    // adjacent runs).  Every lane issues the same stores with no branch around
+    // them (a lane of a query row past a ragged tile writes to its own slot
+    // of the workspace's discard area), so a later wait for the next item's
+    // loads is not made to drain these stores.
     __syncthreads();
-    TO* Os = reinterpret_cast<TO*>(smem_raw);
-    constexpr int OV = 16 / (int)sizeof(TO);        // elements per 16 bytes
-    constexpr int OP = DV + OV;                     // staging row pitch
-    static_assert(TR * OP * sizeof(TO) <= offsetof(OutSmem, Ps), "staging overlaps live LDS");
-    bool bad = false;
+    {
+      bool bad = false;
+      TO* dumpo = reinterpret_cast<TO*>(p.w.dump) + tid * (16 / (int)sizeof(TO));
   #pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
+      for (int qh = 0; qh < 2; ++qh) {
+        const int row = qh * 32 + l32;
+        const float f = sm.rs[row];
+        const bool live = row < qvalid;
+        TO* orow = Og + (int64_t)row * p.so.l;
   #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int col = (2 * wave + jj) * 32 + l32;
+        for (int jj = 0; jj < 2; ++jj) {
   #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = qh * 32 + acc_row(r, lane);
-          const float x = O[qh][jj][r] * sm.rs[row];
-          bad |= row < qvalid && nonfinite_as<TO>(x);
-          Os[row * OP + col] = Store<TO>::cvt(x);
+          for (int g = 0; g < 4; ++g) {
+            const int col = (2 * wave + jj) * 32 + 8 * g + 4 * lh;
+            float x[4];
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[e] = O[qh][jj][4 * g + e] * f;
+              bad |= live && nonfinite_as<TO>(x[e]);
+            }
+            store4(live ? orow + col : dumpo, x);
+          }
         }
       }
-    flag_nonfinite(p.nf, bad, kNonFiniteFwd);
-    __syncthreads();
-    // a fixed number of unconditional stores per thread, with no branch
-    // around them (rows past a ragged tile rewrite its last row with the
-    // same bytes)
-    static_assert(TR * (DV / OV) % NT3 == 0, "store pieces per thread");
-  #pragma unroll
-    for (int i = 0; i < TR * (DV / OV) / NT3; ++i) {
-      const int e = tid + i * NT3;
-      const int row = min(e / (DV / OV), qvalid - 1), cv = e % (DV / OV);
-      *reinterpret_cast<u32x4*>(Og + (int64_t)row * p.so.l + cv * OV) =
-          *reinterpret_cast<const u32x4*>(Os + row * OP + cv * OV);
+      flag_nonfinite(p.nf, bad, kNonFiniteFwd);
     }
     }
     k = kn;
