@@ -38,8 +38,21 @@ constexpr int NCB = DV / 32;   // column blocks of the state operand
 // and a half-wave touches all 64 banks once
 __host__ __device__ constexpr int vswz(int key, int piece) { return piece ^ ((key & 3) << 2); }
 
+// sequence length rounded up to whole 64-key tiles (the rotated-key region
+// holds whole tiles, so a tile read never leaves it)
+__host__ __device__ constexpr int lpad(int L) { return (L + TK - 1) / TK * TK; }
+// Rotated keys are stored per 64-key tile in the A-fragment order of a
+// 32x32x16 MFMA with k = d: the block of 32 keys and 16 d is 1 KB, in which
+// lane 32 ((d / 8) % 2) + key % 32 holds its 8 consecutive d as 16 contiguous
+// bytes, so one wave load of 1 KB is one fragment.  Offset of (key, d) from
+// the head's origin (key counted over the whole sequence):
+__host__ __device__ constexpr int64_t kt_off(int key, int d) {
+  return (int64_t)(key >> 6) * (TK * DK) +
+         (((((key >> 5) & 1) * (DK / 16) + (d >> 4)) * 64 + 32 * ((d >> 3) & 1) + (key & 31)) << 3) + (d & 7);
+}
+
 struct Work {
-  half* kt;      // rotated keys       [bh][L][DK]
+  half* kt;      // rotated keys       [bh][Lp/64][64*DK] (per 64-key tile, MFMA fragment order, kt_off)
   half* dR;      // chunk deltas       [bh][nc][DV][DK]   (column-major: [col][d])
   float* dRs;    // delta scales       [bh][nc][2]        (2^e per d_v half)
   float* dz;     // key-sum deltas     [bh][nc][DK]
@@ -64,7 +77,7 @@ size_t carve(void* base, int bh, int L, int B, Work* w) {
     off += align256(bytes);
     return o;
   };
-  const size_t o_kt = take((size_t)bh * L * DK * 2);
+  const size_t o_kt = take((size_t)bh * lpad(L) * DK * 2);
   const size_t o_dR = take(deltas ? (size_t)bh * nc * DV * DK * 2 : 0);
   const size_t o_dRs = take(deltas ? (size_t)bh * nc * 2 * 4 : 0);
   const size_t o_dz = take(deltas ? (size_t)bh * nc * DK * 4 : 0);
@@ -187,8 +200,8 @@ __device__ __forceinline__ int scale_exp(float amax) {
 // four key rows of one transposed read start 64 bytes apart in the bank space.
 constexpr int DP = 256 + 32;
 struct DeltaSmem {
-  half Kz[2][TK * DP];  // zeta-scaled rotated keys [key][d], two tiles
-  half Vh[2][TK * DP];  // this half of the value tile [key][col], two tiles
+  half Kz[2][TK * DP];  // rotated keys [key][d], two tiles
+  half Vh[2][TK * DP];  // this half of the value tile scaled by zeta [key][col], two tiles
   float dzs[DK];
   float4 step[DK / 2];  // per pair: e^{i theta} and e^{i TK theta} as (c1, s1, cT, sT)
 };
@@ -211,7 +224,7 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
 
   const T* Kg = reinterpret_cast<const T*>(p.k) + bb * p.sk.b + head * p.sk.h + (int64_t)c0 * p.sk.l;
   const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + (int64_t)c0 * p.sv.l + half_ * 256;
-  half* ktg = p.w.kt + ((int64_t)bh * p.L + c0) * DK;
+  half* kth = p.w.kt + (int64_t)bh * lpad(p.L) * DK;
 
   // wave tile: d rows [(wave >> 1) * 64, +64), columns [(wave & 1) * 128, +128)
   const int d0 = (wave >> 1) * 64, n0 = (wave & 1) * 128;
@@ -271,8 +284,11 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   // transposed-read origin of this lane (see lds_read_tr16): key 8 (lane / 32)
   // + (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
   const int tro = (8 * (lane >> 5) + ((lane & 15) >> 2)) * DP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  // ---- rotate the keys (-> workspace), scale by zeta (-> LDS, key-sum);
-  // convert the values (-> LDS), tile kt into LDS buffer buf
+  // ---- rotate the keys (-> LDS; key-sum of the zeta-scaled keys); scale the
+  // values by zeta (-> LDS), tile kt into LDS buffer buf.  zeta is applied to
+  // the value rows rather than the keys (the same product K'^T (V (.) zeta)),
+  // so the LDS key tile is the unscaled rotated keys that the output kernel
+  // reads: they are written out from there in fragment order
   auto stage = [&](int kt, int buf) {
     const int k0 = kt * TK;
     const int kvalid = min(TK, Bc - k0);
@@ -309,16 +325,37 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = kq + i;
-      if (half_ == 0 && key < kvalid) st8(ktg + (int64_t)(k0 + key) * DK + 8 * cq, x[i]);
       const float z = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key) * dec.lg2);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] *= z;
       if (half_ == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dzp[e] += x[i][e];
+        for (int e = 0; e < 8; ++e) dzp[e] += x[i][e] * z;
       }
       st8(sm.Kz[buf] + key * DP + 8 * cq, x[i]);
-      *reinterpret_cast<u32x4*>(sm.Vh[buf] + key * DP + 8 * cq) = Raw16<T>::f16(vr[i]);
+      float y[8];
+      Raw16<T>::f32(vr[i], y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= z;
+      st8(sm.Vh[buf] + key * DP + 8 * cq, y);
+    }
+  };
+  // the rotated keys of tile kt (LDS buffer buf) to the workspace: thread ->
+  // 16-byte pieces tid + 512 i of the tile in fragment order, so every wave
+  // store is one contiguous 1 KB fragment block
+  auto write_kt = [&](int kt, int buf) {
+    const int k0 = kt * TK;
+    const int kvalid = min(TK, Bc - k0);
+    half* dst = kth + kt_off(c0 + k0, 0);
+    // the lane's addressing is recomputed here rather than kept live across
+    // the tile loop (the registers are needed by the accumulators)
+    int t = tid;
+    asm volatile("" : "+v"(t));
+#pragma unroll
+    for (int i = 0; i < TK * DK / 8 / NT3; ++i) {
+      const int e = t + i * NT3;
+      const int blk = e >> 6, slot = e & 63;           // block (32 keys x 16 d) and its lane slot
+      const int key = 32 * (blk / (DK / 16)) + (slot & 31), d = 16 * (blk % (DK / 16)) + 8 * (slot >> 5);
+      if (key < kvalid)
+        *reinterpret_cast<u32x4*>(dst + (int64_t)e * 8) = *reinterpret_cast<const u32x4*>(sm.Kz[buf] + key * DP + d);
     }
   };
   auto mma = [&](int buf) {
@@ -355,6 +392,7 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   const bool stage_first = wave >= 4;
   for (int kt = 0; kt < nkt; ++kt) {
     const bool more = kt + 1 < nkt;
+    if (half_ == 0) write_kt(kt, kt & 1);
     if (!stage_first) mma(kt & 1);
     if (more) {
       stage(kt + 1, (kt + 1) & 1);
@@ -491,8 +529,15 @@ __global__ void __launch_bounds__(256) scan_kernel(P3 p, HeadParams hp) {
     if (cb == 0) z = gB * z + dzc;
   }
   if (p.state_out) {
+    // a state that an fp16 operand overflow made non-finite is recorded as
+    // such (no later chunk of this call reads it, so no output shows it)
+    bool bad = false;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) p.state_out[((int64_t)bh * DK + dbase + i) * DV + col] = R[i];
+    for (int i = 0; i < 32; ++i) {
+      p.state_out[((int64_t)bh * DK + dbase + i) * DV + col] = R[i];
+      bad |= nonfinite_as<float>(R[i]);
+    }
+    flag_nonfinite(p.nf, bad, kNonFiniteFwd);
   }
   if (cb == 0 && p.z_out) p.z_out[(int64_t)bh * DK + tid] = z;
 }
@@ -540,7 +585,7 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
   const bool xpos = (p.flags & RET_XPOS) != 0;
   const T* Kg = reinterpret_cast<const T*>(p.k) + bb * p.sk.b + head * p.sk.h;
   const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + cb * SCB;
-  half* ktg = p.w.kt + (int64_t)bh * p.L * DK;
+  half* kth = p.w.kt + (int64_t)bh * lpad(p.L) * DK;
   half* dump = p.w.dump + tid * 8;                   // 16-byte scratch slot of this thread
 
   if (xpos && tid < DK / 2) {
@@ -640,7 +685,7 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kq + i;
-          if (LEAD) st8(key < kvalid ? ktg + (int64_t)(c0 + k0 + key) * DK + 8 * cq : dump, x[i]);
+          if (LEAD) st8(key < kvalid ? kth + kt_off(c0 + k0 + key, 8 * cq) : dump, x[i]);
           const float zt = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key) * dec.lg2);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -763,24 +808,43 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
   if (cb == 0) body(std::true_type{});
   else body(std::false_type{});
   if (p.state_out) {
+    // a state that an fp16 operand overflow made non-finite is recorded as such
+    bool bad = false;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < 16; ++r) {
         p.state_out[((int64_t)bh * DK + d0 + acc_row(r, lane)) * DV + cb * SCB + 32 * jj + l32] = acc[jj][r];
+        bad |= nonfinite_as<float>(acc[jj][r]);
+      }
+    flag_nonfinite(p.nf, bad, kNonFiniteFwd);
   }
 }
 
 // ---------------------------------------------------------------- output
+// Warp-specialised, one 64-row query item at a time:
+//   producers (waves 0..3): wave w forms the 32 x 32 block S^T = K' Q'^T of
+//     keys 32 ((w / 2) % 2) .. and queries 32 (w % 2) .. of every key tile
+//     (its query fragments stay in registers for the whole item; the key
+//     fragments are wave loads of the fragment-ordered rotated keys), scales
+//     it by s gamma^(q - k) and writes P (fp16) to LDS, keeping fp32 row sums
+//   consumers (waves 4..7): wave w owns output columns 128 (w % 4) .. + 127 of
+//     all 64 rows: the cross term Q' R_{c-1} first (the state operand streamed
+//     from global memory in fragment order), then P V for every key tile (a
+//     bf16 value fragment is converted to fp16 in registers as it is read, so
+//     P V runs on fp16 MFMA with fp16 P), then the normalised tile into LDS,
+//     from where all eight waves write it with coalesced 16-byte stores; they
+//     also copy the value tiles from global memory straight into LDS (16 key
+//     rows per wave, no registers), the next tile's during this tile's P V
+// P and the value tile are double-buffered, so the producers form the scores
+// of tile j + 1 while the consumers copy its values and multiply tile j: one
+// barrier per key tile.  The copies are issued from inline assembly, so the
+// compiler does not drain them before every later LDS access (it cannot tell
+// their destination from the buffers being read); the consumers wait for
+// them explicitly before the barrier that publishes the tile.
 struct OutSmem {
-  half Qs[TR * QP];
-  union {
-    struct {
-      half Ks[TK * QP];
-      half Vn[TK * DV];     // value tile [key][col] (fp16), pieces swizzled (vswz)
-    } kv;
-  } u;
-  half Ps[TR * KP];
+  half V[2][TK * DV];       // value tiles [key][col] (input type, pieces swizzled by vswz); the query tile overlays V[1]
+  half Ps[2][TR * KP];      // P tiles [query][key]
   float rs[TR], xs[TR], dens[TR];
   float dpart[2][TR];       // within-chunk row sums of key halves 0 / 1
   float zs[DK];
@@ -791,7 +855,12 @@ struct OutSmem {
   double theta[DK / 2];
   float2 step1[DK / 2];
 };
+static_assert(TR * QP <= TK * DV, "the query tile fits in one value buffer");
 
+// m0 is declared clobbered by the value-tile copies (the compiler keeps no
+// value in it across them)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <typename T, typename TO>
 __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -834,20 +903,24 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     bh = grp / p.nc;
     return rt * TR < min(p.B, p.L - c * p.B);              // ragged last chunk
   };
+  // the role and the wave's place in it are uniform over the wave
+  const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const bool producer = wave_u < 4;
+  const int sk = (wave_u >> 1) & 1, sqh = wave_u & 1;     // producer: key half, query half
+  const int cw = wave_u & 3;                               // consumer: block of 128 columns
   // the query tile of an item, as raw element pairs: thread -> pair column
   // tid % 128 of rows 16 (tid / 128) + 0..15.  The next item's tile is loaded
-  // while the current item is normalised and stored.
-  // (with it, the item's key-sum z_{c-1} (thread -> d) and the power-of-two
-  // scales of this wave's two state column blocks, used in the rotation and
-  // after the cross term)
+  // while the current item is normalised and stored, with the item's key-sum
+  // z_{c-1} (thread -> d) and the power-of-two scales of the consumer's four
+  // state column blocks
   uint32_t qraw[16];
-  float zpre_n, up0_n, up1_n;
+  float zpre_n, up_n[4];
   auto issue_q = [&](int rt, int c, int bh) {
     const int j = threadIdx.x & 127, grp = threadIdx.x >> 7;
     const int64_t ci = (int64_t)bh * p.nc + c;
     zpre_n = p.w.zc[ci * DK + (threadIdx.x & (DK - 1))];
-    up0_n = p.w.Rs[ci * NCB + 2 * (threadIdx.x >> 6)];
-    up1_n = p.w.Rs[ci * NCB + 2 * (threadIdx.x >> 6) + 1];
+  #pragma unroll
+    for (int jj = 0; jj < 4; ++jj) up_n[jj] = p.w.Rs[ci * NCB + 4 * cw + jj];
     const int bb = bh / p.h, head = bh % p.h;
     const int r0 = rt * TR;
     const int qvalid = min(TR, min(p.B, p.L - c * p.B) - r0);
@@ -876,6 +949,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   if (k < nk) issue_q(rt, c, bh);
   while (k < nk) {
     int kn = k + 1, rtn = 0, cn = 0, bhn = 0;
+    while (kn < nk && !decode(kn, rtn, cn, bhn)) ++kn;
     __syncthreads();                                       // the previous item's LDS reads are done
     {
     OutSmem& sm = *reinterpret_cast<OutSmem*>(smem_raw);
@@ -884,26 +958,52 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     // persistent loop (where it would stay live across the whole item)
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
     const int lh = lane >> 5, l32 = lane & 31;
     const int bb = bh / p.h, head = bh % p.h;
     const int c0 = c * p.B;
     const int Bc = min(p.B, p.L - c0);
     const int r0 = rt * TR;
     const int qvalid = min(TR, Bc - r0);
+    const int n = rt + 1;                           // key tiles, taken in the order rt, 0, 1, .., rt - 1
+    auto ktile = [&](int j) { return j == 0 ? rt : j - 1; };
     Decay dec;
     dec.init(hp, head);
     const bool xpos = (p.flags & RET_XPOS) != 0;
     const float qk_scale = (p.flags & RET_SCALE_QK) ? rsqrtf((float)DK) : 1.f;
-
     const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + (int64_t)c0 * p.sv.l;
-    // z_{c-1} and the state scales, requested with the query tile
-    const float zpre = zpre_n, up0 = up0_n, up1 = up1_n;
-    const half* Kt = p.w.kt + ((int64_t)bh * p.L + c0) * DK;
+    const float zpre = zpre_n;
+    const float up[4] = {up_n[0], up_n[1], up_n[2], up_n[3]};
+    // the chunk's first tile of rotated keys (c0 is a whole number of tiles)
+    const half* Kc = p.w.kt + ((int64_t)bh * lpad(p.L) + c0) * DK;
     TO* Og = reinterpret_cast<TO*>(p.o) + bb * p.so.b + head * p.so.h + (int64_t)(c0 + r0) * p.so.l;
+    half* Qs = sm.V[1];
+    // staging row pitch of the output tile: 16 bytes of padding per row
+    constexpr int SPB = DV * (int)sizeof(TO) + 16;
+    static_assert(TR * SPB <= sizeof(OutSmem::V) + sizeof(OutSmem::Ps), "the staged output tile fits");
 
+    // a value tile into LDS buffer buf: consumer wave cw copies key rows
+    // 16 cw .. 16 cw + 15, one 1 KB row per wave instruction (lane i lands at
+    // byte 16 i of the row, so it fetches the piece that belongs there under
+    // the swizzle); rows past a ragged chunk's end repeat its last key, whose
+    // P entries are zero.  The copy writes no register.
+    auto dma_v = [&](int kt, int buf) {
+      const int k0 = kt * TK;
+      const int kvalid = min(TK, Bc - k0);
+      const T* Vt = Vg + (int64_t)k0 * p.sv.l;       // offsets inside the tile fit 32 bits
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = cw * 16 + i;
+        const int key = min(r, kvalid - 1);
+        const T* src = Vt + (uint32_t)(key * (int)p.sv.l + vswz(r, lane) * 8);
+        const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(sm.V[buf] + r * DV);
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
+      }
+    };
+    // wait for this wave's copies (before the barrier that publishes them)
+    auto dma_wait = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };        // vmcnt(0)
     // ---- rotated query tile, row tables
-    {
+    auto rotate_q = [&] {
       const int j = tid & 127, grp = tid >> 7;      // 16 rows per group
       float a[16], b[16];
   #pragma unroll
@@ -926,209 +1026,81 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
           rot(a[i], b[i], cs, sn);
           advance(cs, sn, c1, s1);
         }
-        st2(sm.Qs + (grp * 16 + i) * QP + 2 * j, a[i], b[i]);
+        st2(Qs + (grp * 16 + i) * QP + 2 * j, a[i], b[i]);
       }
       if (tid < TR) {
         float s = qk_scale;
         if (p.flags & RET_NORM_DROW) s *= dec.drow((float)(p.n_prev + c0 + r0 + tid + 1));
         sm.rs[tid] = s;
         sm.xs[tid] = s * dec.pow((float)(r0 + tid + 1));
-        sm.dens[tid] = 0.f;
       }
       if (tid < DK) sm.zs[tid] = zpre;
       if (tid < 32) sm.ginv[tid] = __builtin_amdgcn_exp2f(-(float)tid * dec.lg2);
-    }
+    };
 
-    // ---- staged key / value tile registers
-    u32x4 kreg[4];          // 64 keys x 256 d fp16: 2048 16-byte pieces, 4 per thread
-    u32x4 vreg[8];          // 64 keys x 512 columns: 4096 16-byte pieces, 8 per thread
-    auto issue_k = [&](int kt) {
-      const int k0 = kt * TK;
-      const int kvalid = min(TK, Bc - k0);
+    constexpr int NSX = DK / 16, XR = 3;
+    if (producer) {
+      // the key fragments of the next score tile (16 steps of d)
+      f16x8 kf[NSX];
+      auto issue_kf = [&](int kt) {
+        const half* kp = Kc + (int64_t)kt * (TK * DK) + (sk * NSX * 64 + lane) * 8;
   #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = tid + i * NT3;
-        const int key = min(e >> 5, kvalid - 1), piece = e & 31;
-        kreg[i] = *reinterpret_cast<const u32x4*>(Kt + (int64_t)(k0 + key) * DK + piece * 8);
-      }
-    };
-    auto issue_v = [&](int kt) {
-      const int k0 = kt * TK;
-      const int kvalid = min(TK, Bc - k0);
-      const T* Vt = Vg + (int64_t)k0 * p.sv.l;       // offsets inside the tile fit 32 bits
-  #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = tid + i * NT3;
-        const int key = min(e >> 6, kvalid - 1), piece = e & 63;
-        vreg[i] = *reinterpret_cast<const u32x4*>(Vt + (uint32_t)(key * (int)p.sv.l + piece * 8));
-      }
-    };
-    auto commit_k = [&](int kt) {
-      const int kvalid = min(TK, Bc - kt * TK);
-  #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = tid + i * NT3;
-        const int key = e >> 5, piece = e & 31;
-        u32x4 v = kreg[i];
-        if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(sm.u.kv.Ks + key * QP + piece * 8) = v;
-      }
-    };
-    auto commit_v = [&](int kt) {
-      const int kvalid = min(TK, Bc - kt * TK);
-  #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = tid + i * NT3;
-        const int key = e >> 6, piece = e & 63;
-        u32x4 v = Raw16<T>::f16(vreg[i]);
-        if (key >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(sm.u.kv.Vn + key * DV + vswz(key, piece) * 8) = v;
-      }
-    };
-    // this lane's transposed-read origin in a value tile: key 8 (lane / 32) +
-    // (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
-    // (swizzled: the lane's key row has r % 4 = (lane / 4) % 4)
-    const int vtr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * DV + 4 * (lane & 1);
-    const int vtr_sw = ((lane >> 2) & 3) << 2, vtr_lo = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-
-    // output tiles of this wave: query halves {0,1} x column tiles {2w, 2w+1},
-    // held transposed (the MFMAs take the column operand first): lane l,
-    // register r of O[qh][jj] is query qh 32 + l % 32, column (2w + jj) 32 +
-    // acc_row(r, l), so each lane holds runs of four consecutive columns of one
-    // query row, stored straight from registers
-    f32x16 O[2][2];
-  #pragma unroll
-    for (int i = 0; i < 2; ++i)
-  #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) O[i][jj] = f32x16{};
-
-    // ---- cross-chunk term Q' R_{c-1}.  Wave w owns state columns 64 w ..
-    // 64 w + 63.  The state operand is stored in MFMA fragment order (a
-    // 32-column x 16-d block is one 1 KB wave load), so each wave streams its
-    // B fragments straight from global memory, XR steps ahead, with no LDS
-    // staging and no barriers.  The first key / value tile is loaded meanwhile.
-    issue_k(rt);
-    issue_v(rt);
-    __syncthreads();                                // the query tile and the row tables
-    {
-      constexpr int NSX = DK / 16, XR = 6;
-      const half* rp = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK + (int64_t)(2 * wave * NSX * 64 + lane) * 8;
-      f16x8 rb[XR][2], qa[2][2];
-  #pragma unroll
-      for (int t = 0; t < XR; ++t)
-  #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) rb[t][jj] = *reinterpret_cast<const f16x8*>(rp + (int64_t)(jj * NSX + t) * 512);
-      auto load_q = [&](int t, int buf) {
-  #pragma unroll
-        for (int qh = 0; qh < 2; ++qh)
-          qa[buf][qh] = *reinterpret_cast<const f16x8*>(sm.Qs + (qh * 32 + l32) * QP + 16 * t + 8 * lh);
+        for (int t = 0; t < NSX; ++t) kf[t] = *reinterpret_cast<const f16x8*>(kp + t * 512);
       };
-      load_q(0, 0);
+      // the first tile's key fragments are requested before the query
+      // rotation, which runs under them
+      issue_kf(rt);
+      rotate_q();
+      __syncthreads();                              // the query tile and the row tables
+      // this wave's 32 queries as B fragments, for the whole item
+      f16x8 qf[NSX];
   #pragma unroll
-      for (int t = 0; t < NSX; ++t) {
-        if (t + 1 < NSX) load_q(t + 1, (t + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < NSX; ++t) qf[t] = *reinterpret_cast<const f16x8*>(Qs + (sqh * 32 + l32) * QP + 16 * t + 8 * lh);
+      // cross part of the score denominator, s xi (Q' . z_{c-1}): 4 threads per row
+      {
+        const int row = tid >> 2, part = tid & 3;   // d 64 part .. 64 part + 63
+        float acc = 0.f;
   #pragma unroll
-        for (int qh = 0; qh < 2; ++qh)
+        for (int u = 0; u < 8; ++u) {
+          const f16x8 qv = *reinterpret_cast<const f16x8*>(Qs + row * QP + 64 * part + 8 * u);
+          const f32x4 z0 = *reinterpret_cast<const f32x4*>(sm.zs + 64 * part + 8 * u);
+          const f32x4 z1 = *reinterpret_cast<const f32x4*>(sm.zs + 64 * part + 8 * u + 4);
   #pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rb[t % XR][jj], qa[t & 1][qh], O[qh][jj], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (t + XR < NSX) {
+          for (int e = 0; e < 4; ++e) acc += (float)qv[e] * z0[e];
   #pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            rb[t % XR][jj] = *reinterpret_cast<const f16x8*>(rp + (int64_t)(jj * NSX + t + XR) * 512);
+          for (int e = 0; e < 4; ++e) acc += (float)qv[4 + e] * z1[e];
         }
+        acc += __shfl_xor(acc, 1, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        if (part == 0) sm.dens[row] = sm.xs[row] * acc;
       }
-    }
-    {
-      // row scale s xi and the operand's per-block power of two (the lane's
-      // query row is l32 of each half)
-  #pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {
-        const float x = sm.xs[qh * 32 + l32];
-        const float x0 = x * up0, x1 = x * up1;
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          O[qh][0][r] *= x0;
-          O[qh][1][r] *= x1;
-        }
-      }
-      // cross part of the score denominator, s xi (Q' . z_{c-1}): 8 threads per row
-      const int row = tid >> 3, part = tid & 7;     // d 32 part .. 32 part + 31
-      float acc = 0.f;
-  #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f16x8 qv = *reinterpret_cast<const f16x8*>(sm.Qs + row * QP + 32 * part + 8 * u);
-        const f32x4 z0 = *reinterpret_cast<const f32x4*>(sm.zs + 32 * part + 8 * u);
-        const f32x4 z1 = *reinterpret_cast<const f32x4*>(sm.zs + 32 * part + 8 * u + 4);
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) acc += (float)qv[e] * z0[e];
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) acc += (float)qv[4 + e] * z1[e];
-      }
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      acc += __shfl_xor(acc, 4, 64);
-      if (part == 0) sm.dens[row] = sm.xs[row] * acc;
-    }
-
-    // ---- within-chunk term, diagonal key tile first (tile order rt, 0, 1, ..)
-    // Two phases per key tile, one barrier after each:
-    //   1. waves 0..3 form S^T = K' Q'^T as 32 x 32 tiles (keys 32 (w / 2) ..,
-    //      queries 32 (w % 2) ..) and write P; then every wave commits its
-    //      share of the value tile and loads the next one
-    //   2. all eight waves accumulate P V, then commit the next key tile and
-    //      load the one after
-    float den = 0.f;
-    const int sk = wave >> 1, sqh = wave & 1;
-    commit_k(rt);                                   // the key / value region is free since the item began
-    if (rt > 0) issue_k(0);
-    __syncthreads();
-    for (int idx = 0; idx <= rt; ++idx) {
-      const int kt = (idx == 0) ? rt : idx - 1;
-      const bool diag = (idx == 0);
-      const int k0 = kt * TK;
-      if (wave < 4) {
-        const bool skip = diag && sk > sqh;         // keys 32..63 vs queries 0..31 of the diagonal
+      float den = 0.f;
+      // scores of key tile ktile(j) into P buffer buf; kf holds its key fragments
+      auto score = [&](int j, int buf) {
+        const int k0 = ktile(j) * TK;
+        const bool diag = (j == 0);
         float pv[16];
-        if (!skip) {
-          // fragments of step s + 3 are read while step s multiplies
-          const half* kp = sm.u.kv.Ks + (sk * 32 + l32) * QP + 8 * lh;
-          const half* qp = sm.Qs + (sqh * 32 + l32) * QP + 8 * lh;
-          constexpr int NS = DK / 16, PD = 4;
-          f16x8 ka[PD], qb[PD];
-  #pragma unroll
-          for (int t = 0; t < PD - 1; ++t) {
-            ka[t] = *reinterpret_cast<const f16x8*>(kp + 16 * t);
-            qb[t] = *reinterpret_cast<const f16x8*>(qp + 16 * t);
-          }
+        if (!(diag && sk > sqh)) {                  // keys 32..63 vs queries 0..31 of the diagonal: zero
           f32x16 S = {};
   #pragma unroll
-          for (int t = 0; t < NS; ++t) {
-            if (t + PD - 1 < NS) {
-              ka[(t + PD - 1) % PD] = *reinterpret_cast<const f16x8*>(kp + 16 * (t + PD - 1));
-              qb[(t + PD - 1) % PD] = *reinterpret_cast<const f16x8*>(qp + 16 * (t + PD - 1));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            S = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t % PD], qb[t % PD], S, 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);      // keep the reads ahead of the multiplies
-          }
+          for (int t = 0; t < NSX; ++t) S = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[t], qf[t], S, 0, 0, 0);
           // D = gamma^(q - k) split as gamma^base gamma^-(8i + j), base = q - (first key of the lane)
           const int base = r0 + sqh * 32 + l32 - k0 - sk * 32 - 4 * lh;
           const float gq = sm.rs[sqh * 32 + l32] * __builtin_amdgcn_exp2f((float)base * dec.lg2);
-          // the causal mask q >= k only bites on the diagonal tile
+          // the causal mask q >= k only bites on the diagonal tile (it also
+          // drops the keys past a ragged chunk's end, whose fragments hold
+          // whatever the workspace held)
           auto scale = [&](auto masked) {
   #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float4 gi = *reinterpret_cast<const float4*>(sm.ginv + 8 * i);
               const float gv[4] = {gi.x, gi.y, gi.z, gi.w};
   #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                float val = S[4 * i + j] * gq * gv[j];
-                if (decltype(masked)::value) val = (base >= 8 * i + j) ? val : 0.f;
+              for (int jj = 0; jj < 4; ++jj) {
+                float val = S[4 * i + jj] * gq * gv[jj];
+                if (decltype(masked)::value) val = (base >= 8 * i + jj) ? val : 0.f;
                 den += val;
-                pv[4 * i + j] = val;
+                pv[4 * i + jj] = val;
               }
             }
           };
@@ -1139,93 +1111,181 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
           for (int i = 0; i < 16; ++i) pv[i] = 0.f;
         }
   #pragma unroll
-        for (int i = 0; i < 4; ++i) st4(sm.Ps + (sqh * 32 + l32) * KP + sk * 32 + 8 * i + 4 * lh, pv + 4 * i);
-      }
-      commit_v(kt);
-      if (idx < rt) issue_v(idx);                   // next tile: kt = idx
+        for (int i = 0; i < 4; ++i) st4(sm.Ps[buf] + (sqh * 32 + l32) * KP + sk * 32 + 8 * i + 4 * lh, pv + 4 * i);
+      };
+      // the diagonal tile, while the consumers form the cross term
+      score(0, 0);
+      if (n > 1) issue_kf(ktile(1));
       __syncthreads();
-      // O += P V: the value fragment of a column tile serves both query halves
-      // (rows 0..31 of P are zero against keys 32..63 of the diagonal tile);
-      // the fragments of step s + 1 are read while step s multiplies
-      {
-        f16x8 pa[2][2], bv[2][2];
-        auto load_pv = [&](int kb, int buf) {
+      for (int j = 0; j < n; ++j) {
+        if (j + 1 < n) {
+          score(j + 1, (j + 1) & 1);
+          if (j + 2 < n) issue_kf(ktile(j + 2));
+        } else {
+          den += __shfl_xor(den, 32, 64);           // lanes l and l + 32 hold the same query
+          if (lh == 0) sm.dpart[sk][sqh * 32 + l32] = den;
+        }
+        __syncthreads();
+      }
+      if (kn < nk) issue_q(rtn, cn, bhn);
+    } else {
+      // output tiles of this wave: query halves {0,1} x column tiles 4 cw +
+      // {0..3}, held transposed (the MFMAs take the column operand first):
+      // lane l, register r of O[qh][jj] is query qh 32 + l % 32, column
+      // (4 cw + jj) 32 + acc_row(r, l), so each lane holds runs of four
+      // consecutive columns of one query row, stored straight from registers
+      f32x16 O[2][4];
   #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            // keys kb + 8 (lane / 32) + 0..7 of column (2w + jj) 32 + lane % 32
-            const half* vp = sm.u.kv.Vn + kb * DV + vtr_row + ((((2 * wave + jj) * 4) ^ vtr_sw) + vtr_lo) * 8;
+      for (int i = 0; i < 2; ++i)
+  #pragma unroll
+        for (int jj = 0; jj < 4; ++jj) O[i][jj] = f32x16{};
+      // the ring of state-operand fragments (fragment (jj, t) of this wave's
+      // four column blocks at rp + (jj NSX + t) 512)
+      const half* rp = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK + (int64_t)(4 * cw * NSX * 64 + lane) * 8;
+      f16x8 rb[XR * 4];
+      // the head of the ring and the first value tile are requested before
+      // the query rotation, which runs under them
+  #pragma unroll
+      for (int t = 0; t < XR; ++t)
+  #pragma unroll
+        for (int jj = 0; jj < 4; ++jj) rb[t * 4 + jj] = *reinterpret_cast<const f16x8*>(rp + (jj * NSX + t) * 512);
+      dma_v(rt, 0);
+      rotate_q();
+      __syncthreads();                              // the query tile and the row tables
+      // ---- cross-chunk term Q' R_{c-1}, the state operand's fragments
+      // streamed XR steps ahead with no LDS staging
+      {
+        f16x8 qa[2][2];
+        auto load_q = [&](int t, int buf) {
+  #pragma unroll
+          for (int qh = 0; qh < 2; ++qh)
+            qa[buf][qh] = *reinterpret_cast<const f16x8*>(Qs + (qh * 32 + l32) * QP + 16 * t + 8 * lh);
+        };
+        load_q(0, 0);
+  #pragma unroll
+        for (int t = 0; t < NSX; ++t) {
+          if (t + 1 < NSX) load_q(t + 1, (t + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int qh = 0; qh < 2; ++qh)
+  #pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rb[(t % XR) * 4 + jj], qa[t & 1][qh], O[qh][jj], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (t + XR < NSX) {
+  #pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              rb[(t % XR) * 4 + jj] = *reinterpret_cast<const f16x8*>(rp + (jj * NSX + t + XR) * 512);
+          }
+        }
+      }
+      // row scale s xi and the operand's per-block power of two (the lane's
+      // query row is l32 of each half)
+  #pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        const float x = sm.xs[qh * 32 + l32];
+  #pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float xu = x * up[jj];
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) O[qh][jj][r] *= xu;
+        }
+      }
+      dma_wait();
+      __syncthreads();
+      // this lane's transposed-read origin in a value tile: key 8 (lane / 32) +
+      // (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
+      // (swizzled: the lane's key row has r % 4 = (lane / 4) % 4)
+      const int vtr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * DV + 4 * (lane & 1);
+      const int vtr_sw = ((lane >> 2) & 3) << 2, vtr_lo = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+      for (int j = 0; j < n; ++j) {
+        if (j + 1 < n) dma_v(ktile(j + 1), (j + 1) & 1);
+        // O += P V (rows 0..31 of P are zero against keys 32..63 of the
+        // diagonal tile); the fragments of step s + 1 are read while step s
+        // multiplies
+        const int buf = j & 1;
+        f16x8 pa[2][2];
+        u32x4 bv[2][4];                             // raw value fragments (input type)
+        auto load_pv = [&](int kb, int b2) {
+  #pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            // keys kb + 8 (lane / 32) + 0..7 of column (4 cw + jj) 32 + lane % 32
+            const half* vp = sm.V[buf] + kb * DV + vtr_row + ((((4 * cw + jj) * 4) ^ vtr_sw) + vtr_lo) * 8;
             const f16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * DV);
-            bv[buf][jj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            bv[b2][jj] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           }
   #pragma unroll
           for (int qh = 0; qh < 2; ++qh)
-            pa[buf][qh] = *reinterpret_cast<const f16x8*>(sm.Ps + (qh * 32 + l32) * KP + kb + 8 * lh);
+            pa[b2][qh] = *reinterpret_cast<const f16x8*>(sm.Ps[buf] + (qh * 32 + l32) * KP + kb + 8 * lh);
         };
         load_pv(0, 0);
   #pragma unroll
         for (int t = 0; t < TK / 16; ++t) {
           if (t + 1 < TK / 16) load_pv(16 * (t + 1), (t + 1) & 1);
           __builtin_amdgcn_sched_barrier(0);
+          f16x8 vf[4];
+  #pragma unroll
+          for (int jj = 0; jj < 4; ++jj) vf[jj] = __builtin_bit_cast(f16x8, Raw16<T>::f16(bv[t & 1][jj]));
   #pragma unroll
           for (int qh = 0; qh < 2; ++qh)
   #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-              O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[t & 1][jj], pa[t & 1][qh], O[qh][jj], 0, 0, 0);
+            for (int jj = 0; jj < 4; ++jj)
+              O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[jj], pa[t & 1][qh], O[qh][jj], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
+        dma_wait();
+        __syncthreads();
       }
-      if (idx < rt) {
-        commit_k(idx);                              // next tile: kt = idx
-        if (idx + 1 < rt) issue_k(idx + 1);
-      }
-      __syncthreads();
-    }
-    // the next item's query tile
-    while (kn < nk && !decode(kn, rtn, cn, bhn)) ++kn;
-    if (kn < nk) issue_q(rtn, cn, bhn);
-    if (wave < 4) {
-      den += __shfl_xor(den, 32, 64);               // lanes l and l + 32 hold the same query
-      if (lh == 0) sm.dpart[sk][sqh * 32 + l32] = den;
-    }
-    __syncthreads();
-    // cross part plus the two key halves, summed in a fixed order
-    if (tid < TR) {
-      const float d = sm.dens[tid] + sm.dpart[0][tid] + sm.dpart[1][tid];
-      sm.rs[tid] = (p.flags & RET_NORM_SCORE) ? 1.f / fmaxf(fabsf(d), 1.f) : 1.f;
-    }
+      // the next item's query tile
+      if (kn < nk) issue_q(rtn, cn, bhn);
 
-    // ---- normalise and store straight from the accumulators: per query row
-    // and column tile, four 4-column runs of the row (lanes l and l + 32 hold
-    // adjacent runs).  Every lane issues the same stores with no branch around
-    // them (a lane of a query row past a ragged tile writes to its own slot
-    // of the workspace's discard area), so a later wait for the next item's
-    // loads is not made to drain these stores.
-    __syncthreads();
-    {
+      // ---- normalise into the staging tile (row pitch SPB bytes, over the
+      // dead value and P buffers); lane l writes query row l % 32 of each half
       bool bad = false;
-      TO* dumpo = reinterpret_cast<TO*>(p.w.dump) + tid * (16 / (int)sizeof(TO));
+      char* stage = reinterpret_cast<char*>(&sm.V[0][0]);
   #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
         const int row = qh * 32 + l32;
-        const float f = sm.rs[row];
+        // cross part plus the two key halves, summed in a fixed order
+        const float d = sm.dens[row] + sm.dpart[0][row] + sm.dpart[1][row];
+        const float f = (p.flags & RET_NORM_SCORE) ? 1.f / fmaxf(fabsf(d), 1.f) : 1.f;
         const bool live = row < qvalid;
-        TO* orow = Og + (int64_t)row * p.so.l;
+        TO* srow = reinterpret_cast<TO*>(stage + row * SPB);
   #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
+        for (int jj = 0; jj < 4; ++jj) {
   #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int col = (2 * wave + jj) * 32 + 8 * g + 4 * lh;
+            const int col = (4 * cw + jj) * 32 + 8 * g + 4 * lh;
             float x[4];
   #pragma unroll
             for (int e = 0; e < 4; ++e) {
               x[e] = O[qh][jj][4 * g + e] * f;
               bad |= live && nonfinite_as<TO>(x[e]);
             }
-            store4(live ? orow + col : dumpo, x);
+            store4(srow + col, x);
           }
         }
       }
       flag_nonfinite(p.nf, bad, kNonFiniteFwd);
+    }
+    __syncthreads();                                // the staged output tile
+    // ---- every wave writes the tile: 16-byte pieces, consecutive lanes along
+    // a row.  Every lane issues the same stores with no branch around them (a
+    // piece of a row past a ragged tile goes to the thread's own slot of the
+    // workspace's discard area), so a later wait for the next item's loads is
+    // not made to drain these stores.
+    {
+      constexpr int RPC = DV * (int)sizeof(TO) / 16;          // 16-byte pieces per row
+      const char* stage = reinterpret_cast<const char*>(&sm.V[0][0]);
+      char* dumpo = reinterpret_cast<char*>(p.w.dump) + tid * 16;
+  #pragma unroll
+      for (int i = 0; i < TR * RPC / NT3; ++i) {
+        const int e = tid + i * NT3;
+        const int row = e / RPC, piece = e % RPC;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * SPB + piece * 16);
+        char* dst = row < qvalid ? reinterpret_cast<char*>(Og + (int64_t)row * p.so.l) + piece * 16 : dumpo;
+        *reinterpret_cast<u32x4*>(dst) = v;
+      }
     }
     }
     k = kn;
@@ -1234,6 +1294,8 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     bh = bhn;
   }
 }
+
+#pragma clang diagnostic pop
 
 static_assert(sizeof(OutSmem) <= 160 * 1024 && sizeof(DeltaSmem) <= 160 * 1024 && sizeof(SScanSmem) <= 160 * 1024,
               "LDS of one workgroup");
