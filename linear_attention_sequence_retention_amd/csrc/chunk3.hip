@@ -556,8 +556,8 @@ constexpr int SCB = 64;             // state columns per workgroup
 constexpr int VBP = SCB + 32;       // fp16 pitch of the value block [key][col] (192 bytes)
 constexpr int RSP = DK + 8;         // fp16 pitch of the published block [col][d]
 struct SScanSmem {
-  half Kz[TK * DP];                 // zeta-scaled rotated keys of one 64-key tile [key][d]
-  half Vb[TK * VBP];                // the block's value columns of the tile [key][col]
+  half Kz[TK * DP];                 // rotated keys of one 64-key tile [key][d]
+  half Vb[TK * VBP];                // the block's value columns of the tile scaled by zeta [key][col]
   half Rst[SCB * RSP];              // R_{c-1} operand [col][d] before it is stored
   float amaxw[NT3 / 64][2];         // per wave and 32-column block: max |R|
   float dzw[NT3 / 64][DK];          // per wave: key-sum partials of the chunk
@@ -657,8 +657,11 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) dzp[e] = 0.f;
       }
-      // ---- stage the tile: rotate the keys (-> workspace), scale by zeta (->
-      // LDS, key-sum); convert the value block (-> LDS)
+      // ---- stage the tile: rotate the keys (-> LDS; key-sum of the
+      // zeta-scaled keys); scale the value block by zeta (-> LDS).  zeta goes
+      // on the value rows (the same product K'^T (V (.) zeta)), so the LDS key
+      // tile holds the unscaled rotated keys, which column block 0 writes out
+      // in fragment order
       {
         float x[4][8];
 #pragma unroll
@@ -685,18 +688,17 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kq + i;
-          if (LEAD) st8(key < kvalid ? kth + kt_off(c0 + k0 + key, 8 * cq) : dump, x[i]);
           const float zt = __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - key) * dec.lg2);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            x[i][e] *= zt;
-            dzp[e] += x[i][e];
-          }
+          for (int e = 0; e < 8; ++e) dzp[e] += x[i][e] * zt;
           st8(sm.Kz + key * DP + 8 * cq, x[i]);
         }
-        u32x4 v = Raw16<T>::f16(cur.v);
-        if (vk >= kvalid) v = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(sm.Vb + vk * VBP + 8 * vp) = v;
+        float y[8];
+        Raw16<T>::f32(cur.v, y);
+        const float zv = vk < kvalid ? __builtin_amdgcn_exp2f((float)(Bc - 1 - k0 - vk) * dec.lg2) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] *= zv;
+        st8(sm.Vb + vk * VBP + 8 * vp, y);
       }
       if (s == 0) {
         // ---- publish R_{c-1}: per 32-column block, a power of two puts max |R| in [2^14, 2^15)
@@ -711,6 +713,21 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
         }
       }
       __syncthreads();
+      if (LEAD) {
+        // the tile's rotated keys to the workspace in fragment order: thread
+        // -> 16-byte pieces tid + 512 i, so every wave store is one contiguous
+        // 1 KB block (keys past the sequence's end go to the thread's
+        // discard slot)
+        half* kdst = kth + kt_off(c0 + k0, 0);
+#pragma unroll
+        for (int i = 0; i < TK * DK / 8 / NT3; ++i) {
+          const int e = tid + i * NT3;
+          const int blk = e >> 6, slot = e & 63;
+          const int key = 32 * (blk / (DK / 16)) + (slot & 31), d = 16 * (blk % (DK / 16)) + 8 * (slot >> 5);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sm.Kz + key * DP + d);
+          *reinterpret_cast<u32x4*>(key < kvalid ? kdst + (int64_t)e * 8 : dump) = v;
+        }
+      }
       if (s == 0) {
         float down[2];
 #pragma unroll
@@ -757,7 +774,7 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
         for (int jj = 0; jj < 2; ++jj) acc[jj] *= gB;
         gprev = gB;
       }
-      // ---- R += (K' zeta)^T V over the tile's keys
+      // ---- R += K'^T (V (.) zeta) over the tile's keys
 #pragma unroll
       for (int kb = 0; kb < TK; kb += 16) {
         const half* ap = sm.Kz + kb * DP + d0 + tro;
