@@ -107,7 +107,11 @@ typedef struct { int64_t b, h, l; } ret_strides;   /* element strides of a [b,h,
  * contracted with fp16 MFMA operands and fp32 accumulation; the operands
  * require |q|, |k| < 2^15, |v| < 2^16 and normalised scores
  * s_t |q'_t . k'_m| < 2^16 (the state copy used as an operand is rescaled by
- * a power of two per chunk, so the state itself has no such limit).
+ * a power of two per chunk, so the state itself has no such limit).  An
+ * operand that overflows anyway makes the outputs it feeds non-finite (with
+ * d_k = 256, d_v = 512 and B a multiple of 64, also a returned state_out);
+ * that is recorded and reported by retention_range_status() (the call itself
+ * returns RET_OK).
  */
 int retention_chunkwise_fwd(const void* q, ret_strides sq, const void* k, ret_strides sk,
                             const void* v, ret_strides sv, void* o, ret_strides so,
