@@ -860,7 +860,7 @@ __global__ void __launch_bounds__(NT3, 1) sscan_kernel(P3 p, HeadParams hp) {
 // their destination from the buffers being read); the consumers wait for
 // them explicitly before the barrier that publishes the tile.
 struct OutSmem {
-  half V[2][TK * DV];       // value tiles [key][col] (input type, pieces swizzled by vswz); the query tile overlays V[1]
+  half V[2][TK * DV];       // value tiles, per consumer a [key][128 col] slice (input type, pieces swizzled); the query tile overlays V[1]
   half Ps[2][TR * KP];      // P tiles [query][key]
   float rs[TR], xs[TR], dens[TR];
   float dpart[2][TR];       // within-chunk row sums of key halves 0 / 1
@@ -999,26 +999,37 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
     constexpr int SPB = DV * (int)sizeof(TO) + 16;
     static_assert(TR * SPB <= sizeof(OutSmem::V) + sizeof(OutSmem::Ps), "the staged output tile fits");
 
-    // a value tile into LDS buffer buf: consumer wave cw copies key rows
-    // 16 cw .. 16 cw + 15, one 1 KB row per wave instruction (lane i lands at
-    // byte 16 i of the row, so it fetches the piece that belongs there under
-    // the swizzle); rows past a ragged chunk's end repeat its last key, whose
-    // P entries are zero.  The copy writes no register.
+    // a value tile's columns 128 cw .. 128 cw + 127 into consumer cw's slice
+    // of LDS buffer buf ([key][16 pieces of 16 bytes], 256-byte rows, pieces
+    // XOR-swizzled by 4 (key % 4) like vswz): one instruction per 4 key rows
+    // (lane i lands at byte 16 i, so it fetches the piece that belongs there);
+    // rows past a ragged chunk's end repeat its last key, whose P entries are
+    // zero.  The copy writes no register.  Each consumer reads only its own
+    // slice, so it refills a slice as soon as its own P V has read it and
+    // waits for the copy only before its own next read.
     auto dma_v = [&](int kt, int buf) {
       const int k0 = kt * TK;
       const int kvalid = min(TK, Bc - k0);
-      const T* Vt = Vg + (int64_t)k0 * p.sv.l;       // offsets inside the tile fit 32 bits
+      const T* Vt = Vg + (int64_t)k0 * p.sv.l + cw * 128;   // offsets inside the tile fit 32 bits
+      // the lane's piece is recomputed here rather than kept live across the
+      // stage loop
+      int ln = threadIdx.x;
+      asm volatile("" : "+v"(ln));
+      const int pp = ln & 15, rq = (ln >> 4) & 3;
   #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = cw * 16 + i;
+        const int r = 4 * i + rq;
         const int key = min(r, kvalid - 1);
-        const T* src = Vt + (uint32_t)(key * (int)p.sv.l + vswz(r, lane) * 8);
-        const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(sm.V[buf] + r * DV);
+        const T* src = Vt + (uint32_t)(key * (int)p.sv.l + vswz(r, pp) * 8);
+        const uint32_t dst =
+            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(sm.V[buf] + cw * (TK * 128) + 4 * i * 128);
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory", "m0");
       }
     };
-    // wait for this wave's copies (before the barrier that publishes them)
+    // wait for this wave's copies: all, or all but the 16 instructions of
+    // the most recent one
     auto dma_wait = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };        // vmcnt(0)
+    auto dma_wait1 = [] { __builtin_amdgcn_s_waitcnt(0x4F70); };       // vmcnt(16)
     // ---- rotated query tile, row tables
     auto rotate_q = [&] {
       const int j = tid & 127, grp = tid >> 7;      // 16 rows per group
@@ -1213,10 +1224,19 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       // this lane's transposed-read origin in a value tile: key 8 (lane / 32) +
       // (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
       // (swizzled: the lane's key row has r % 4 = (lane / 4) % 4)
-      const int vtr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * DV + 4 * (lane & 1);
+      const int vtr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * 128 + 4 * (lane & 1);
       const int vtr_sw = ((lane >> 2) & 3) << 2, vtr_lo = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
       for (int j = 0; j < n; ++j) {
-        if (j + 1 < n) dma_v(ktile(j + 1), (j + 1) & 1);
+        // tile 1 goes to buffer 1, free of the query tile since the last
+        // barrier; tile j (j >= 1) was requested a tile ago or earlier, and
+        // only the copy of tile j + 1 may still be in flight
+        if (j == 0) {
+          if (n > 1) dma_v(ktile(1), 1);
+        } else if (j + 1 < n) {
+          dma_wait1();
+        } else {
+          dma_wait();
+        }
         // O += P V (rows 0..31 of P are zero against keys 32..63 of the
         // diagonal tile); the fragments of step s + 1 are read while step s
         // multiplies
@@ -1227,8 +1247,8 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
   #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             // keys kb + 8 (lane / 32) + 0..7 of column (4 cw + jj) 32 + lane % 32
-            const half* vp = sm.V[buf] + kb * DV + vtr_row + ((((4 * cw + jj) * 4) ^ vtr_sw) + vtr_lo) * 8;
-            const f16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * DV);
+            const half* vp = sm.V[buf] + cw * (TK * 128) + kb * 128 + vtr_row + (((jj * 4) ^ vtr_sw) + vtr_lo) * 8;
+            const f16x4 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * 128);
             bv[b2][jj] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           }
   #pragma unroll
@@ -1250,7 +1270,11 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
               O[qh][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[jj], pa[t & 1][qh], O[qh][jj], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
-        dma_wait();
+        // this slice of buffer j % 2 is read: refill it with tile j + 2
+        if (j + 2 < n) {
+          __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the slice's reads have returned
+          dma_v(ktile(j + 2), j & 1);
+        }
         __syncthreads();
       }
       // the next item's query tile
