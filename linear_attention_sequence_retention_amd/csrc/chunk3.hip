@@ -2,14 +2,14 @@
 // notes, §2.4, with §2.3's xPos rotation and §三.3's normalisations), split
 // into three kernels whose boundaries are the only synchronisation:
 //
-//   delta  (one workgroup per head, chunk and half of d_v)
+//   delta  (persistent; one unit of work per head, chunk and half of d_v)
 //          dR_i = K'_[i]^T (V_[i] (.) zeta),  dz_i = K'_[i]^T zeta
 //          and, once per head and chunk, the rotated keys K' in fp16
 //   scan   (one workgroup per head and block of 32 state columns)
 //          R_i = gamma^(B_i) R_{i-1} + dR_i,  z_i likewise; it stores the
 //          state every chunk starts from, R_{i-1}, as an fp16 operand copy
 //          scaled by a power of two per block of 32 columns
-//   output (one workgroup per head, chunk and 64-row query tile)
+//   output (persistent; one item per head, chunk and 64-row query tile)
 //          O = (Q'K'^T (.) D) V + (Q' R_{i-1}) (.) xi, with the row scales and
 //          score normalisation, written once
 //
@@ -17,8 +17,9 @@
 // (one workgroup per head and block of 64 state columns, walking the chunks
 // in order with the state in MFMA accumulators), which also rotates the keys.
 //
-// Every key element is rotated once (the output kernel reads the rotated fp16
-// keys), and no work is repeated across d_v slices.  Operands are fp16 with fp32 accumulation.
+// The keys are rotated only in the delta kernel (by both d_v halves of a
+// chunk; the output kernel reads the rotated fp16 keys that half 0 writes),
+// and no score is recomputed across d_v slices.  Operands are fp16 with fp32 accumulation.
 // Shapes: d_k = 256, d_v = 512, chunk B a multiple of 64.
 #include "internal.h"
 
@@ -204,26 +205,92 @@ struct DeltaSmem {
   half Vh[2][TK * DP];  // this half of the value tile scaled by zeta [key][col], two tiles
   float dzs[DK];
   float4 step[DK / 2];  // per pair: e^{i theta} and e^{i TK theta} as (c1, s1, cT, sT)
+  double theta[DK / 2];
 };
 
 template <typename T>
 __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   DeltaSmem& sm = *reinterpret_cast<DeltaSmem*>(smem_raw);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = xcd_local(blockIdx.x, gridDim.x);
+  const int tid0 = threadIdx.x;
+  // Persistent: unit g = (head, chunk, half of d_v) with g = 2 (bh nc + c) +
+  // half.  Workgroup i runs on XCD i mod 8; each XCD walks a contiguous range
+  // of units, its workgroups taking consecutive units side by side, so both
+  // halves of a chunk run together on one XCD and share its keys in that L2.
+  // The next unit's first tile is requested during the current unit's last
+  // tile, so its latency and the workgroup turnover run under the current
+  // unit's dR stores.
+  const int U = p.nbh * p.nc * 2;
+  const int NX = min(8, (int)gridDim.x);
+  const int xw = blockIdx.x % NX, jw = blockIdx.x / NX;
+  const int wx = ((int)gridDim.x - xw + NX - 1) / NX;      // workgroups of this XCD
+  const int uhi = (int)((int64_t)(xw + 1) * U / NX);
+  int g = (int)((int64_t)xw * U / NX) + jw;
+  if (g >= uhi) return;                                    // uniform over the workgroup
+  const bool xpos = (p.flags & RET_XPOS) != 0;
+
+  // the key rows and this half's value rows of unit g, and the chunk's length
+  auto unit_src = [&](int gu, const T*& Kg_, const T*& Vg_, int& Bc_) {
+    const int bhu = (gu >> 1) / p.nc, c0u = ((gu >> 1) % p.nc) * p.B;
+    const int bbu = bhu / p.h, hu = bhu % p.h;
+    Bc_ = min(p.B, p.L - c0u);
+    Kg_ = reinterpret_cast<const T*>(p.k) + bbu * p.sk.b + hu * p.sk.h + (int64_t)c0u * p.sk.l;
+    Vg_ = reinterpret_cast<const T*>(p.v) + bbu * p.sv.b + hu * p.sv.h + (int64_t)c0u * p.sv.l + (gu & 1) * 256;
+  };
+  u32x4 kr[4], vr[4];
+  auto issue_at = [&](const T* Kg_, const T* Vg_, int Bc_, int kt) {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    const int cq = t & 31, kq = 4 * (t >> 5);
+    const int k0 = kt * TK;
+    const int kvalid = min(TK, Bc_ - k0);
+    // 64-bit tile origin; offsets inside a 64-key tile fit 32 bits (strides < 2^25)
+    const T* Kt = Kg_ + (int64_t)k0 * p.sk.l;
+    const T* Vt = Vg_ + (int64_t)k0 * p.sv.l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kc = min(kq + i, kvalid - 1);
+      kr[i] = *reinterpret_cast<const u32x4*>(Kt + (uint32_t)(kc * (int)p.sk.l + 8 * cq));
+      vr[i] = *reinterpret_cast<const u32x4*>(Vt + (uint32_t)(kc * (int)p.sv.l + 8 * cq));
+    }
+  };
+  // per pair, once per workgroup: theta (an fp64 load from global memory
+  // inside a unit would wait for the tile loads as well: the vector memory
+  // counter completes in order), e^{i theta} and e^{i TK theta}
+  if (xpos && tid0 < DK / 2) {
+    const double th1 = hp.theta[tid0];
+    float4 t;
+    phase(1, th1, t.x, t.y);
+    phase(TK, th1, t.z, t.w);
+    sm.theta[tid0] = th1;
+    sm.step[tid0] = t;
+  }
+  {
+    const T *Kg0, *Vg0;
+    int Bc0;
+    unit_src(g, Kg0, Vg0, Bc0);
+    issue_at(Kg0, Vg0, Bc0, 0);
+  }
+  for (; g < uhi; g += wx) {
+  // the thread index passes through an empty asm each unit, so per-lane
+  // addressing is recomputed inside the unit rather than hoisted out of the
+  // persistent loop (where it would stay live across the whole unit)
+  int tl = threadIdx.x;
+  asm volatile("" : "+v"(tl));
+  const int tid = tl, lane = tl & 63, wave = tl >> 6;
+  // thread -> 16-byte piece cq (d or columns 8 cq .. 8 cq + 7) of keys
+  // 4 (tid / 32) + 0..3 of every tile
+  const int cq = tid & 31, kq = 4 * (tid >> 5);
   const int half_ = g & 1;
   const int c = (g >> 1) % p.nc;
   const int bh = (g >> 1) / p.nc;
-  const int bb = bh / p.h, head = bh % p.h;
+  const int head = bh % p.h;
   const int c0 = c * p.B;
-  const int Bc = min(p.B, p.L - c0);
+  const T *Kg, *Vg;
+  int Bc;
+  unit_src(g, Kg, Vg, Bc);
   Decay dec;
   dec.init(hp, head);
-  const bool xpos = (p.flags & RET_XPOS) != 0;
-
-  const T* Kg = reinterpret_cast<const T*>(p.k) + bb * p.sk.b + head * p.sk.h + (int64_t)c0 * p.sk.l;
-  const T* Vg = reinterpret_cast<const T*>(p.v) + bb * p.sv.b + head * p.sv.h + (int64_t)c0 * p.sv.l + half_ * 256;
   half* kth = p.w.kt + (int64_t)bh * lpad(p.L) * DK;
 
   // wave tile: d rows [(wave >> 1) * 64, +64), columns [(wave & 1) * 128, +128)
@@ -234,52 +301,21 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  // thread -> 16-byte piece cq (d or columns 8 cq .. 8 cq + 7) of keys
-  // 4 (tid / 32) + 0..3 of every tile
-  const int cq = tid & 31, kq = 4 * (tid >> 5);
   const int nkt = (Bc + TK - 1) / TK;
-  u32x4 kr[4], vr[4];
-  auto issue = [&](int kt) {
-    const int k0 = kt * TK;
-    const int kvalid = min(TK, Bc - k0);
-    // 64-bit tile origin; offsets inside a 64-key tile fit 32 bits (strides < 2^25)
-    const T* Kt = Kg + (int64_t)k0 * p.sk.l;
-    const T* Vt = Vg + (int64_t)k0 * p.sv.l;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kc = min(kq + i, kvalid - 1);
-      kr[i] = *reinterpret_cast<const u32x4*>(Kt + (uint32_t)(kc * (int)p.sk.l + 8 * cq));
-      vr[i] = *reinterpret_cast<const u32x4*>(Vt + (uint32_t)(kc * (int)p.sv.l + 8 * cq));
-    }
-  };
-  // the first tile is requested before the phase set-up, which then runs
-  // under its latency; the angles are read first (the vector memory counter
-  // completes in order, so a later read would wait for the tile as well)
-  double th[4], th1 = 0.0;
-  if (xpos) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) th[u] = hp.theta[4 * cq + u];
-    if (tid < DK / 2) th1 = hp.theta[tid];
-  }
-  issue(0);
+  auto issue = [&](int kt) { issue_at(Kg, Vg, Bc, kt); };
+  // the unit's first tile was requested before this point (during the
+  // previous unit's last tile, or above); the phase set-up runs under it
+  __syncthreads();                                  // the previous unit's LDS reads; theta and the steps
   float dzp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // key-sum of d 8 cq .. +7
   // xPos phase of this thread's first key in the current tile for its four
-  // pairs, the one-key and the one-tile steps
+  // pairs
   float pc[4], ps[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     pc[u] = 1.f;
     ps[u] = 0.f;
-    if (xpos) phase(p.pos0 + c0 + kq, th[u], pc[u], ps[u]);
+    if (xpos) phase(p.pos0 + c0 + kq, sm.theta[4 * cq + u], pc[u], ps[u]);
   }
-  if (xpos && tid < DK / 2) {
-    float4 t;
-    phase(1, th1, t.x, t.y);
-    phase(TK, th1, t.z, t.w);
-    sm.step[tid] = t;
-  }
-
-  __syncthreads();
 
   // transposed-read origin of this lane (see lds_read_tr16): key 8 (lane / 32)
   // + (lane % 16) / 4, column 16 ((lane / 16) % 2) + 4 (lane % 4)
@@ -397,6 +433,12 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
     if (more) {
       stage(kt + 1, (kt + 1) & 1);
       if (kt + 2 < nkt) issue(kt + 2);
+    } else if (g + wx < uhi) {
+      // the next unit's first tile (the registers are free from here on)
+      const T *Kgn, *Vgn;
+      int Bcn;
+      unit_src(g + wx, Kgn, Vgn, Bcn);
+      issue_at(Kgn, Vgn, Bcn, 0);
     }
     if (stage_first) mma(kt & 1);
     __syncthreads();
@@ -429,7 +471,19 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
     for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[i][jj][r]));
-  amax = maxabs_block(amax, reinterpret_cast<float*>(&sm.Vh[0][0]));
+  {
+    // block max, the wave's slot addressed from the unit's own thread index
+    // (a hoisted address would stay live across the unit)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    float* red = reinterpret_cast<float*>(&sm.Vh[0][0]);
+    __syncthreads();
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    amax = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT3 / 64; ++w) amax = fmaxf(amax, red[w]);
+  }
   const int e = scale_exp(amax);
   const float down = ldexpf(1.f, -e);
   // the workgroup's 256 columns of dR are one contiguous 128 KB block ([col][d]):
@@ -462,6 +516,7 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   }
   if (tid == 0) p.w.dRs[((int64_t)bh * p.nc + c) * 2 + half_] = ldexpf(1.f, e);
   if (half_ == 0 && tid < DK) p.w.dz[((int64_t)bh * p.nc + c) * DK + tid] = sm.dzs[tid];
+  }
 }
 
 // ---------------------------------------------------------------- scan
@@ -1379,7 +1434,10 @@ hipError_t run(const ChunkArgs& a, hipStream_t st) {
     auto k = delta_kernel<T>;
     e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(DeltaSmem));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(bh * p.nc * 2), dim3(NT3), sizeof(DeltaSmem), st, p, *a.hp);
+    const int units = bh * p.nc * 2;
+    int W = min(units, persistent_workgroups());
+    if (W >= 8) W -= W % 8;
+    hipLaunchKernelGGL(k, dim3(W), dim3(NT3), sizeof(DeltaSmem), st, p, *a.hp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(scan_kernel, dim3(bh * NCB), dim3(256), 0, st, p, *a.hp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
