@@ -215,8 +215,10 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   const int tid0 = threadIdx.x;
   // Persistent: unit g = (head, chunk, half of d_v) with g = 2 (bh nc + c) +
   // half.  Workgroup i runs on XCD i mod 8; each XCD walks a contiguous range
-  // of units, its workgroups taking consecutive units side by side, so both
-  // halves of a chunk run together on one XCD and share its keys in that L2.
+  // of units.  Workgroups 2m and 2m + 1 of an XCD take the two halves of one
+  // chunk at every step, swapping halves from step to step (half 0 also
+  // writes the rotated keys, so neither falls behind the other): the two read
+  // the chunk's keys at the same time, the second read from the XCD's L2.
   // The next unit's first tile is requested during the current unit's last
   // tile, so its latency and the workgroup turnover run under the current
   // unit's dR stores.
@@ -224,8 +226,12 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
   const int NX = min(8, (int)gridDim.x);
   const int xw = blockIdx.x % NX, jw = blockIdx.x / NX;
   const int wx = ((int)gridDim.x - xw + NX - 1) / NX;      // workgroups of this XCD
-  const int uhi = (int)((int64_t)(xw + 1) * U / NX);
-  int g = (int)((int64_t)xw * U / NX) + jw;
+  const int ulo = (int)((int64_t)xw * U / NX), uhi = (int)((int64_t)(xw + 1) * U / NX);
+  const bool paired = (wx % 2 == 0) && (ulo % 2 == 0) && (uhi % 2 == 0);
+  auto unit_at = [&](int i) {
+    return paired ? ulo + 2 * ((jw >> 1) + (wx >> 1) * i) + ((jw ^ i) & 1) : ulo + jw + wx * i;
+  };
+  int step = 0, g = unit_at(0);
   if (g >= uhi) return;                                    // uniform over the workgroup
   const bool xpos = (p.flags & RET_XPOS) != 0;
 
@@ -271,7 +277,8 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
     unit_src(g, Kg0, Vg0, Bc0);
     issue_at(Kg0, Vg0, Bc0, 0);
   }
-  for (; g < uhi; g += wx) {
+  for (; g < uhi; g = unit_at(++step)) {
+  const int gnext = unit_at(step + 1);
   // the thread index passes through an empty asm each unit, so per-lane
   // addressing is recomputed inside the unit rather than hoisted out of the
   // persistent loop (where it would stay live across the whole unit)
@@ -433,11 +440,11 @@ __global__ void __launch_bounds__(NT3, 1) delta_kernel(P3 p, HeadParams hp) {
     if (more) {
       stage(kt + 1, (kt + 1) & 1);
       if (kt + 2 < nkt) issue(kt + 2);
-    } else if (g + wx < uhi) {
+    } else if (gnext < uhi) {
       // the next unit's first tile (the registers are free from here on)
       const T *Kgn, *Vgn;
       int Bcn;
-      unit_src(g + wx, Kgn, Vgn, Bcn);
+      unit_src(gnext, Kgn, Vgn, Bcn);
       issue_at(Kgn, Vgn, Bcn, 0);
     }
     if (stage_first) mma(kt & 1);
