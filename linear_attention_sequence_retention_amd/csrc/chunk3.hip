@@ -1141,6 +1141,13 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       // rotation, which runs under them
       issue_kf(rt);
       rotate_q();
+      // the first value tile, producer w copying consumer w's slice, issued
+      // after the rotation's waits for the query tile: the copies are not in
+      // the compiler's count of outstanding loads, so a copy issued before a
+      // wait that the compiler places makes that wait cover the copy too (the
+      // consumers, issuing it before their state-operand loads, waited for
+      // it in the query rotation and the first cross-term step)
+      dma_v(rt, 0);
       __syncthreads();                              // the query tile and the row tables
       // this wave's 32 queries as B fragments, for the whole item
       f16x8 qf[NSX];
@@ -1205,6 +1212,7 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       };
       // the diagonal tile, while the consumers form the cross term
       score(0, 0);
+      dma_wait();                                   // the first value tile has landed
       if (n > 1) issue_kf(ktile(1));
       __syncthreads();
       for (int j = 0; j < n; ++j) {
@@ -1217,7 +1225,11 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
         }
         __syncthreads();
       }
-      if (kn < nk) issue_q(rtn, cn, bhn);
+      // the next item's query tile (requested even after the last item, then
+      // the current one's again: a conditional request left the old and new
+      // registers live together, and the copy between them at the join
+      // waited for the loads)
+      issue_q(kn < nk ? rtn : rt, kn < nk ? cn : c, kn < nk ? bhn : bh);
     } else {
       // output tiles of this wave: query halves {0,1} x column tiles 4 cw +
       // {0..3}, held transposed (the MFMAs take the column operand first):
@@ -1233,13 +1245,12 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
       // four column blocks at rp + (jj NSX + t) 512)
       const half* rp = p.w.Rt + ((int64_t)bh * p.nc + c) * DV * DK + (int64_t)(4 * cw * NSX * 64 + lane) * 8;
       f16x8 rb[XR * 4];
-      // the head of the ring and the first value tile are requested before
-      // the query rotation, which runs under them
+      // the head of the ring is requested before the query rotation, which
+      // runs under it (the producers copy the first value tile)
   #pragma unroll
       for (int t = 0; t < XR; ++t)
   #pragma unroll
         for (int jj = 0; jj < 4; ++jj) rb[t * 4 + jj] = *reinterpret_cast<const f16x8*>(rp + (jj * NSX + t) * 512);
-      dma_v(rt, 0);
       rotate_q();
       __syncthreads();                              // the query tile and the row tables
       // ---- cross-chunk term Q' R_{c-1}, the state operand's fragments
@@ -1339,8 +1350,8 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
         }
         __syncthreads();
       }
-      // the next item's query tile
-      if (kn < nk) issue_q(rtn, cn, bhn);
+      // the next item's query tile (unconditional, as in the producers)
+      issue_q(kn < nk ? rtn : rt, kn < nk ? cn : c, kn < nk ? bhn : bh);
 
       // ---- normalise into the staging tile (row pitch SPB bytes, over the
       // dead value and P buffers); lane l writes query row l % 32 of each half
@@ -1354,18 +1365,50 @@ __global__ void __launch_bounds__(NT3, 1) output_kernel(P3 p, HeadParams hp) {
         const float f = (p.flags & RET_NORM_SCORE) ? 1.f / fmaxf(fabsf(d), 1.f) : 1.f;
         const bool live = row < qvalid;
         TO* srow = reinterpret_cast<TO*>(stage + row * SPB);
+        if constexpr (sizeof(TO) == 2) {
+          // a 16-bit output is not finite iff its exponent field is all ones
+          // (what a value at or past the type's limit rounds to): a running
+          // packed 16-bit max of the stored words' magnitudes, one test per
+          // row at the end (one compare and one scalar OR per value before)
+          typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+          u16x2 mx = {0, 0};
   #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+          for (int jj = 0; jj < 4; ++jj) {
   #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = (4 * cw + jj) * 32 + 8 * g + 4 * lh;
-            float x[4];
+            for (int g = 0; g < 4; ++g) {
+              const int col = (4 * cw + jj) * 32 + 8 * g + 4 * lh;
+              float x[4];
   #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              x[e] = O[qh][jj][4 * g + e] * f;
-              bad |= live && nonfinite_as<TO>(x[e]);
+              for (int e = 0; e < 4; ++e) x[e] = O[qh][jj][4 * g + e] * f;
+              uint2 u;
+              if constexpr (std::is_same<TO, bf16>::value) {
+                u.x = pack_bf2(x[0], x[1]);
+                u.y = pack_bf2(x[2], x[3]);
+              } else {
+                u.x = __builtin_bit_cast(uint32_t, f16x2{(_Float16)x[0], (_Float16)x[1]});
+                u.y = __builtin_bit_cast(uint32_t, f16x2{(_Float16)x[2], (_Float16)x[3]});
+              }
+              *reinterpret_cast<uint2*>(srow + col) = u;
+              mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, u.x & 0x7fff7fffu));
+              mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, u.y & 0x7fff7fffu));
             }
-            store4(srow + col, x);
+          }
+          constexpr unsigned short kExp = std::is_same<TO, bf16>::value ? 0x7f80 : 0x7c00;
+          bad |= live && (mx.x >= kExp || mx.y >= kExp);
+        } else {
+  #pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+  #pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int col = (4 * cw + jj) * 32 + 8 * g + 4 * lh;
+              float x[4];
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                x[e] = O[qh][jj][4 * g + e] * f;
+                bad |= live && nonfinite_as<TO>(x[e]);
+              }
+              store4(srow + col, x);
+            }
           }
         }
       }
